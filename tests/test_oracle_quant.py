@@ -1,0 +1,306 @@
+"""Pins of the oracle's quantizers, bit packing, slot layout and dequantization.
+
+Sources: vLLM rocm_octave docs (module text on slot layout and code packing;
+OctaveFormat; _pack; _quantize_lut; reference_quantize;
+reference_dequantize) and Strata PR #21 (Q4_0 block; max-abs tie-break in
+the maintainer's note; quant/dequant error bounds in "Verification").
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+
+
+# ----------------------------------------------------------------- fp16 ---
+def test_f16_conversion_matches_numpy():
+    rng = np.random.default_rng(0)
+    xs = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-9, 6, 20000),
+        np.array([0.0, -0.0, 65504.0, 65519.0, 65520.0, 1e6, -1e6, np.inf, -np.inf,
+                  2.0 ** -24, 2.0 ** -25, 2.0 ** -25 * 1.5, 2.0 ** -26, 6.1e-5, 1.0 + 2.0 ** -11,
+                  1.0 + 3 * 2.0 ** -11], np.float32)]).astype(np.float32)
+    # ties to even at every exponent
+    ties = (np.float32(1.0) + np.arange(1, 50, 2).astype(np.float32) * np.float32(2.0 ** -11))
+    xs = np.concatenate([xs, ties, -ties]).astype(np.float32)
+    want = xs.astype(np.float16).view(np.uint16)
+    got = np.array([O.f32_to_f16_bits(float(x)) for x in xs], np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_f16_widening_matches_numpy_all_patterns():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = h.view(np.float16).astype(np.float32)
+    got = np.array([O.f16_bits_to_f32(int(v)) for v in h], np.float32)
+    finite = np.isfinite(want)
+    np.testing.assert_array_equal(got[finite].view(np.uint32), want[finite].view(np.uint32))
+    assert np.all(np.isnan(got[np.isnan(want)]))
+    assert np.array_equal(got[np.isinf(want)], want[np.isinf(want)])
+
+
+# --------------------------------------------------------------- layout ---
+def test_slot_layouts():
+    f = O.format_init("octave_k3v4", 128, 64)
+    assert (f.off_k_nope, f.off_v, f.off_scales, f.slot_bytes, f.kernel_code) == (32, 56, 120, 128, 4)
+    assert (f.k_block, f.v_block, f.num_k_scales, f.num_scales) == (64, 128, 2, 3)
+    f = O.format_init("octave_k3v3", 128, 64)
+    assert (f.off_k_nope, f.off_v, f.off_scales, f.slot_bytes, f.kernel_code) == (32, 56, 104, 112, 3)
+    f = O.format_init("octave_k3v3_compact", 256, 64)
+    assert (f.off_k_nope, f.off_v, f.off_scales, f.slot_bytes, f.kernel_code) == (0, 96, 192, 196, 19)
+    assert (f.k_block, f.v_block, f.num_k_scales) == (256, 256, 1)
+    f = O.format_init("octave_k3v4", 192, 64)      # non power of two: V in 64-blocks
+    assert (f.k_block, f.v_block) == (64, 64)
+    f = O.format_init("q4_0", 256)
+    assert (f.off_v, f.off_scales, f.slot_bytes, f.num_k_scales) == (128, 256, 288, 8)
+    # 4.5 bits per element
+    assert f.slot_bytes * 8 / (2 * 256) == 4.5
+
+
+@pytest.mark.parametrize("args", [
+    ("octave_k3v3_compact", 192, 64),   # compact needs a power-of-two head
+    ("octave_k3v4", 128, 32),           # rope_dim not a multiple of 64
+    ("octave_k3v4", 96, 0),             # head_size not a multiple of 64
+    ("octave_k3v4", 128, 192),          # rope part larger than the head
+    ("octave_k5v5", 128, 64),           # unknown cache dtype
+    ("q4_0", 96, 0),                    # FWHT over the head needs a power of two
+])
+def test_format_validation(args):
+    with pytest.raises(ValueError):
+        O.format_init(*args)
+
+
+# -------------------------------------------------------------- packing ---
+def test_pack4_identities():
+    rng = np.random.default_rng(1)
+    c = rng.integers(0, 16, 64).astype(np.uint8)
+    p = O.pack(c, 4)
+    assert p.shape == (32,)
+    w = p.view("<u4")
+    for m, word in enumerate(w):
+        lo = int(word) & 0x0F0F0F0F
+        hi = (int(word) >> 4) & 0x0F0F0F0F
+        assert list(lo.to_bytes(4, "little")) == c[8 * m:8 * m + 4].tolist()
+        assert list(hi.to_bytes(4, "little")) == c[8 * m + 4:8 * m + 8].tolist()
+    assert np.array_equal(O.unpack(p, 64, 4), c)
+
+
+def test_pack3_identities():
+    rng = np.random.default_rng(2)
+    n = 128
+    c = rng.integers(0, 8, n).astype(np.uint8)
+    p = O.pack(c, 3)
+    assert p.shape == (3 * n // 8,)
+    lo_w = p[:n // 4].view("<u4")
+    hi_w = p[n // 4:].view("<u4")
+    for d0 in range(0, n, 4):
+        i2 = (d0 % 16) // 4
+        lo = (int(lo_w[d0 // 16]) >> (2 * i2)) & 0x03030303
+        i1 = (d0 % 32) // 4
+        hi = (int(hi_w[d0 // 32]) >> i1) & 0x01010101
+        got = [a + 4 * b for a, b in zip(lo.to_bytes(4, "little"), hi.to_bytes(4, "little"))]
+        assert got == c[d0:d0 + 4].tolist()
+    assert np.array_equal(O.unpack(p, n, 3), c)
+
+
+# ---------------------------------------------------------------- Q4_0 ---
+def _q4_dequant(codes, d16):
+    return (codes.astype(np.float64) - 8.0) * float(np.uint16(d16).view(np.float16))
+
+
+def test_q4_0_error_bound_and_nearest_code():
+    rng = np.random.default_rng(3)
+    for trial in range(3000):
+        x = rng.standard_normal(32).astype(np.float32) * np.float32(10.0 ** rng.uniform(-3, 3))
+        if trial % 3 == 0:
+            x[rng.integers(0, 32)] *= np.float32(20.0)
+        c, d16 = O.q4_0_block(x)
+        assert c.max() <= 15
+        d = float(np.uint16(d16).view(np.float16))
+        err = np.abs(x.astype(np.float64) - _q4_dequant(c, d16))
+        # fp32 scale before fp16 rounding: d = m / -8
+        amax = np.abs(x).max()
+        dd = amax / 8.0
+        bound_unclamped = dd * (0.5 + 2.0 ** -8) + 1e-6 * dd
+        bound_clamped = dd * (1.0 + 2.0 ** -8) + 1e-6 * dd
+        clamped = (c == 15) & (np.sign(x) == np.sign(d))
+        assert np.all(err[~clamped] <= bound_unclamped)
+        assert np.all(err[clamped] <= bound_clamped)
+        # code - 8 is the nearest integer to x / d (halves up), clamped to [-8, 7]
+        t = x.astype(np.float64) / (x[np.argmax(np.abs(x))].astype(np.float64) / -8.0)
+        r = np.clip(np.floor(t + 0.5), -8, 7)
+        near_half = np.abs(t - np.floor(t) - 0.5) < 1e-5
+        assert np.all((c.astype(int) - 8)[~near_half] == r[~near_half])
+
+
+def test_q4_0_max_element_maps_to_code_zero():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(32).astype(np.float32)
+    j = int(np.argmax(np.abs(x)))
+    c, d16 = O.q4_0_block(x)
+    assert c[j] == 0
+    assert np.float16(np.uint16(d16).view(np.float16)) == np.float16(x[j] / np.float32(-8.0))
+
+
+@pytest.mark.parametrize("first_negative", [True, False])
+def test_q4_0_tie_break_prefers_larger_signed_value(first_negative):
+    x = np.zeros(32, np.float32)
+    x[1:30] = np.linspace(-1, 1, 29, dtype=np.float32)
+    a = np.float32(3.0)
+    x[5], x[20] = (-a, a) if first_negative else (a, -a)
+    c, d16 = O.q4_0_block(x)
+    d = float(np.uint16(d16).view(np.float16))
+    assert d == -3.0 / 8.0           # the scale carries the sign of +a
+    pos, neg = (20, 5) if first_negative else (5, 20)
+    assert c[pos] == 0 and c[neg] == 15
+
+
+def test_q4_0_on_grid_round_trip_is_exact():
+    rng = np.random.default_rng(5)
+    for e in (-6, -1, 0, 3, 8):
+        k = rng.integers(-8, 8, 32)
+        k[rng.integers(0, 32)] = -8
+        x = (k * 2.0 ** e).astype(np.float32)
+        c, d16 = O.q4_0_block(x)
+        assert np.array_equal(_q4_dequant(c, d16), x.astype(np.float64))
+
+
+def test_q4_0_all_zero_block():
+    c, d16 = O.q4_0_block(np.zeros(32, np.float32))
+    assert d16 == 0x8000 and np.all(c == 8)
+
+
+# -------------------------------------------------------------- Octave ---
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("n", [64, 128, 256])
+def test_octave_norm_preserving_scale(bits, n):
+    # The scale makes x . x_hat = |x|^2 (module text; _quantize_lut).
+    rng = np.random.default_rng(bits * 1000 + n)
+    lut, _ = O.codebook(bits)
+    for _ in range(200):
+        x = rng.standard_normal(n).astype(np.float32) * np.float32(rng.uniform(0.01, 50))
+        codes, scale = O.quantize_lut(x, bits)
+        assert codes.max() < (1 << bits)
+        s16 = float(np.float16(scale))
+        xh = lut[codes].astype(np.float64) * s16 / 64.0
+        xx = float(np.dot(x.astype(np.float64), x.astype(np.float64)))
+        assert abs(float(np.dot(x.astype(np.float64), xh)) - xx) <= 2.0 ** -10 * xx
+        assert scale > 0
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_octave_codes_are_nearest_codebook_entries(bits):
+    rng = np.random.default_rng(11 + bits)
+    lut, mult = O.codebook(bits)
+    for _ in range(100):
+        x = rng.standard_normal(64).astype(np.float32)
+        codes, _ = O.quantize_lut(x, bits)
+        y = x.astype(np.float64) / np.sqrt(np.mean(x.astype(np.float64) ** 2)) * mult
+        dist = np.abs(y[:, None] - lut[None, :])
+        best = dist.min(axis=1)
+        ok = np.abs(dist[np.arange(64), codes] - best) < 1e-4
+        assert ok.all()
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_octave_power_of_two_equivariance(bits):
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal(64).astype(np.float32)
+    c1, s1 = O.quantize_lut(x, bits)
+    c2, s2 = O.quantize_lut(x * np.float32(8.0), bits)
+    assert np.array_equal(c1, c2) and s2 == 8.0 * s1
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_octave_zero_block(bits):
+    codes, scale = O.quantize_lut(np.zeros(64, np.float32), bits)
+    assert np.all(codes == (1 << (bits - 1)) - 1) and scale == 0.0
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_octave_distortion_near_lloyd_max(bits):
+    # Relative MSE on Gaussian blocks stays close to the Lloyd-Max distortion
+    # (0.03454 at 3 bits, 0.009497 at 4; Max 1960): the int8 codebook and the
+    # norm-preserving (not least-squares) scale cost a little.
+    rng = np.random.default_rng(31)
+    lut, _ = O.codebook(bits)
+    num = den = 0.0
+    for _ in range(300):
+        x = rng.standard_normal(256).astype(np.float32)
+        codes, scale = O.quantize_lut(x, bits)
+        xh = lut[codes] * float(np.float16(scale)) / 64.0
+        num += float(np.sum((x - xh) ** 2))
+        den += float(np.sum(x.astype(np.float64) ** 2))
+    ref = {3: 0.03454, 4: 0.009497}[bits]
+    assert ref * 0.95 < num / den < ref * 1.25
+
+
+# ---------------------------------------------------- whole slots -------
+def _rand(shape, seed, dtype=np.float32):
+    return np.random.default_rng(seed).standard_normal(shape).astype(dtype)
+
+
+@pytest.mark.parametrize("dtype,D,R", [("octave_k3v4", 128, 64), ("octave_k3v3", 128, 64),
+                                       ("octave_k3v3_compact", 256, 64), ("octave_k3v4", 192, 64),
+                                       ("octave_k3v4", 128, 0), ("octave_k3v4", 128, 128),
+                                       ("q4_0", 256, 0), ("q4_0", 128, 0)])
+def test_quantize_dequantize_round_trip(dtype, D, R):
+    f = O.format_init(dtype, D, R)
+    k, v = _rand((40, 3, D), 1), _rand((40, 3, D), 2)
+    slots = O.quantize(f, k, v)
+    assert slots.shape == (40, 3, f.slot_bytes)
+    raw = f.off_scales + 2 * f.num_scales
+    assert np.all(slots[..., raw:] == 0)         # padding stays zero
+    kh, vh = O.dequantize(f, slots)
+    kd, vd = O.dequantize_f64(f, slots)
+    np.testing.assert_allclose(kh, kd, rtol=0, atol=2e-5)
+    np.testing.assert_allclose(vh, vd, rtol=0, atol=2e-5)
+    # expected quantization error for Gaussian data, roughly
+    rel = np.linalg.norm(kh - k) / np.linalg.norm(k)
+    assert rel < (0.12 if dtype == "q4_0" else 0.22)
+    # rotated dequant + explicit inverse rotation == unrotated dequant
+    kr, vr = O.dequantize(f, slots, rotated=True)
+    s = O.signs(D) if f.use_signs else np.ones(D, np.float32)
+    np.testing.assert_array_equal(O.fwht(kr, f.k_block) * s, kh)
+    np.testing.assert_array_equal(O.fwht(vr, f.v_block) * s, vh)
+
+
+def test_quantize_is_deterministic_and_positional():
+    f = O.format_init("octave_k3v4", 128, 64)
+    k, v = _rand((16, 2, 128), 3), _rand((16, 2, 128), 4)
+    a = O.quantize(f, k, v)
+    b = O.quantize(f, k[::-1].copy(), v[::-1].copy())[::-1]
+    assert np.array_equal(a, b)
+
+
+def test_q4_0_slot_on_grid_round_trip():
+    # K/V whose rotation lands on the Q4_0 grid dequantize exactly:
+    # build the rotated values first and rotate back (FWHT is an involution
+    # and exact for these small multiples of 1/16).
+    rng = np.random.default_rng(9)
+    D = 256
+    f = O.format_init("q4_0", D)
+    kr = (rng.integers(-8, 8, (4, 1, D)) * 0.5).astype(np.float32)
+    kr[..., ::32] = -4.0
+    k = O.fwht(kr, D)
+    assert np.array_equal(O.fwht(k, D), kr)       # exact involution on this grid
+    slots = O.quantize(f, k, k)
+    got_r, _ = O.dequantize(f, slots, rotated=True)
+    assert np.array_equal(got_r, kr)
+
+
+def test_fwht_reduces_q4_error_on_outlier_data():
+    # Sanity of the kind Strata's audit reports (int4 error with and without
+    # the rotation on outlier data); not a gate on the exact figures.
+    rng = np.random.default_rng(10)
+    D = 256
+    x = rng.standard_normal((512, D)).astype(np.float32)
+    x[:, [3, 77, 140, 201]] *= 20
+    f = O.format_init("q4_0", D)
+    kh, _ = O.dequantize(f, O.quantize(f, x[:, None], x[:, None]))
+    with_rot = np.linalg.norm(kh[:, 0] - x) / np.linalg.norm(x)
+    xh = np.empty_like(x)
+    for t in range(512):
+        for b in range(D // 32):
+            c, d16 = O.q4_0_block(x[t, 32 * b:32 * b + 32])
+            xh[t, 32 * b:32 * b + 32] = _q4_dequant(c, d16)
+    without = np.linalg.norm(xh - x) / np.linalg.norm(x)
+    assert with_rot < 0.7 * without
