@@ -1,0 +1,277 @@
+// hkv_api.hip -- the C ABI of libhkv: argument checks, format setup and
+// kernel enqueue.  See include/hkv.h for the contract of every entry point.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "hkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hkv_status fail(hkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+hkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(HKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
+
+// Fixed sign pattern of length n: SplitMix64 (Steele, Lea & Flood, OOPSLA
+// 2014) started from state n; output word k gives signs 64k .. 64k+63, a set
+// bit meaning -1.
+void make_sign_bits(int n, uint32_t* words) {
+  uint64_t state = (uint64_t)n;
+  for (int k = 0; k < (n + 63) / 64; ++k) {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    words[2 * k] = (uint32_t)(z & 0xffffffffu);
+    if (2 * k + 1 < HKV_MAX_HEAD / 32) words[2 * k + 1] = (uint32_t)(z >> 32);
+  }
+}
+
+// Re-derive every dependent field and compare, so a corrupted or hand-made
+// descriptor is refused before anything is enqueued.
+hkv_status check_format(const hkv_format* f) {
+  if (!f) return fail(HKV_ERR_INVALID_ARG, "format is NULL");
+  static const char* names[] = {"q4_0", "octave_k3v4", "octave_k3v3", "octave_k3v3_compact"};
+  const char* name = nullptr;
+  if (f->kind == HKV_KIND_Q4_0) {
+    name = names[0];
+  } else if (f->kind == HKV_KIND_OCTAVE) {
+    name = f->compact ? names[3] : (f->v_bits == 4 ? names[1] : names[2]);
+  } else {
+    return fail(HKV_ERR_INVALID_ARG, "format: unknown kind %d", f->kind);
+  }
+  hkv_format g;
+  const hkv_status st = hkv_format_init(&g, name, f->head_size, f->rope_dim, f->page_size);
+  if (st != HKV_OK) return st;
+  if (std::memcmp(&g, f, sizeof(g)) != 0)
+    return fail(HKV_ERR_INVALID_ARG, "format descriptor is inconsistent; use hkv_format_init");
+  return HKV_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+namespace hkv {
+
+DevFmt to_dev(const hkv_format& f) {
+  DevFmt d;
+  std::memset(&d, 0, sizeof(d));
+  d.kind = f.kind;
+  d.D = f.head_size;
+  d.rope = f.rope_dim;
+  d.v_bits = f.v_bits;
+  d.compact = f.compact;
+  d.page_size = f.page_size;
+  d.k_block = f.k_block;
+  d.v_block = f.v_block;
+  d.k_wide = f.k_wide_dim;
+  d.off_k_nope = f.off_k_nope;
+  d.off_v = f.off_v;
+  d.off_scales = f.off_scales;
+  d.num_k_scales = f.num_k_scales;
+  d.num_scales = f.num_scales;
+  d.slot_bytes = f.slot_bytes;
+  d.use_signs = f.kind == HKV_KIND_OCTAVE;
+  // The transform's 1/sqrt(block) is applied as one fp32 multiply by the
+  // fp32-rounded constant.
+  d.k_norm = (float)(1.0 / std::sqrt((double)f.k_block));
+  d.v_norm = (float)(1.0 / std::sqrt((double)f.v_block));
+  std::memcpy(d.sign_bits, f.sign_bits, sizeof(d.sign_bits));
+  return d;
+}
+
+}  // namespace hkv
+
+extern "C" {
+
+const char* hkv_last_error(void) { return g_err; }
+
+const char* hkv_version(void) { return "hkv 0.1 (gfx950)"; }
+
+hkv_status hkv_format_init(hkv_format* f, const char* cache_dtype, int32_t head_size,
+                           int32_t rope_dim, int32_t page_size) {
+  if (!f || !cache_dtype) return fail(HKV_ERR_INVALID_ARG, "format_init: NULL argument");
+  if (page_size < 1 || page_size > 1024)
+    return fail(HKV_ERR_INVALID_ARG, "page_size must be in [1, 1024], got %d", page_size);
+  hkv_format g;
+  std::memset(&g, 0, sizeof(g));
+  const int d = head_size;
+  g.head_size = d;
+  g.page_size = page_size;
+  if (std::strcmp(cache_dtype, "q4_0") == 0) {
+    // Q4_0 + FWHT over the head (Strata PR #21): blocks of 32 with an fp16
+    // scale, no sign flips.
+    if (d != 64 && d != 128 && d != 256)
+      return fail(HKV_ERR_INVALID_ARG, "q4_0 needs head_size 64, 128 or 256, got %d", d);
+    g.kind = HKV_KIND_Q4_0;
+    g.rope_dim = 0;
+    g.v_bits = 4;
+    g.k_block = d;
+    g.v_block = d;
+    g.k_wide_dim = d;
+    g.off_k_nope = d / 2;
+    g.off_v = d / 2;
+    g.off_scales = d;
+    g.num_k_scales = d / 32;
+    g.num_scales = d / 16;
+    g.slot_bytes = d + d / 8;
+    g.kernel_code = 0;
+    *f = g;
+    return HKV_OK;
+  }
+  int v_bits, compact;
+  if (std::strcmp(cache_dtype, "octave_k3v4") == 0) {
+    v_bits = 4, compact = 0;
+  } else if (std::strcmp(cache_dtype, "octave_k3v3") == 0) {
+    v_bits = 3, compact = 0;
+  } else if (std::strcmp(cache_dtype, "octave_k3v3_compact") == 0) {
+    v_bits = 3, compact = 1;
+  } else {
+    return fail(HKV_ERR_INVALID_ARG, "unknown cache dtype '%s'", cache_dtype);
+  }
+  // OctaveFormat validation (vLLM rocm_octave docs).
+  constexpr int kBlock = 64;
+  if (compact && !is_pow2(d))
+    return fail(HKV_ERR_INVALID_ARG, "compact Octave K needs a power-of-two head_size, got %d", d);
+  if (d <= 0 || rope_dim < 0 || rope_dim % kBlock || d % kBlock)
+    return fail(HKV_ERR_INVALID_ARG,
+                "Octave needs head_size and rope_dim in multiples of 64; got head_size=%d, rope_dim=%d",
+                d, rope_dim);
+  if (rope_dim > d)
+    return fail(HKV_ERR_INVALID_ARG, "rope_dim %d exceeds head_size %d", rope_dim, d);
+  if (d > HKV_MAX_HEAD)
+    return fail(HKV_ERR_UNSUPPORTED, "head_size %d exceeds %d", d, HKV_MAX_HEAD);
+  g.kind = HKV_KIND_OCTAVE;
+  g.rope_dim = rope_dim;
+  g.v_bits = v_bits;
+  g.compact = compact;
+  g.k_block = compact ? d : kBlock;
+  g.v_block = is_pow2(d) ? d : kBlock;
+  g.k_wide_dim = compact ? 0 : rope_dim;
+  g.off_k_nope = g.k_wide_dim * 4 / 8;
+  g.off_v = g.off_k_nope + (d - g.k_wide_dim) * 3 / 8;
+  g.off_scales = g.off_v + d * v_bits / 8;
+  g.num_k_scales = compact ? 1 : d / kBlock;
+  g.num_scales = g.num_k_scales + 1;
+  const int raw = g.off_scales + 2 * g.num_scales;
+  const int al = compact ? 4 : 8;
+  g.slot_bytes = (raw + al - 1) / al * al;
+  g.kernel_code = v_bits + (compact ? 16 : 0);
+  make_sign_bits(d, g.sign_bits);
+  *f = g;
+  return HKV_OK;
+}
+
+hkv_status hkv_quantize_append(const hkv_format* f, const void* key, const void* value,
+                               hkv_dtype in_dtype, int64_t num_tokens, int32_t num_kv_heads,
+                               const int64_t* slot_mapping, uint8_t* cache, void* stream) {
+  hkv_status st = check_format(f);
+  if (st != HKV_OK) return st;
+  if (num_tokens < 0 || num_kv_heads <= 0)
+    return fail(HKV_ERR_INVALID_ARG, "quantize_append: num_tokens=%lld num_kv_heads=%d",
+                (long long)num_tokens, num_kv_heads);
+  if (in_dtype != HKV_F32 && in_dtype != HKV_F16)
+    return fail(HKV_ERR_INVALID_ARG, "quantize_append: bad input dtype %d", (int)in_dtype);
+  if (num_tokens == 0) return HKV_OK;
+  if (!key || !value || !slot_mapping || !cache)
+    return fail(HKV_ERR_INVALID_ARG, "quantize_append: NULL pointer");
+  if (!aligned(cache, 16)) return fail(HKV_ERR_INVALID_ARG, "cache must be 16-byte aligned");
+  if (num_tokens * num_kv_heads > 0x7fffffffLL)
+    return fail(HKV_ERR_UNSUPPORTED, "quantize_append: too many rows");
+  const hipError_t e = hkv::launch_quantize_append(hkv::to_dev(*f), key, value, in_dtype == HKV_F16,
+                                                   num_tokens, num_kv_heads, slot_mapping, cache,
+                                                   (hipStream_t)stream);
+  return e == hipSuccess ? HKV_OK : hip_fail(e, "quantize_append launch");
+}
+
+hkv_status hkv_dequantize(const hkv_format* f, const uint8_t* cache, int32_t num_kv_heads,
+                          const int64_t* slot_ids, int64_t num_tokens, int32_t rotated,
+                          float* k_out, float* v_out, void* stream) {
+  hkv_status st = check_format(f);
+  if (st != HKV_OK) return st;
+  if (num_tokens < 0 || num_kv_heads <= 0)
+    return fail(HKV_ERR_INVALID_ARG, "dequantize: num_tokens=%lld num_kv_heads=%d",
+                (long long)num_tokens, num_kv_heads);
+  if (num_tokens == 0) return HKV_OK;
+  if (!cache || !slot_ids || !k_out || !v_out)
+    return fail(HKV_ERR_INVALID_ARG, "dequantize: NULL pointer");
+  if (!aligned(cache, 16)) return fail(HKV_ERR_INVALID_ARG, "cache must be 16-byte aligned");
+  if (num_tokens * num_kv_heads > 0x7fffffffLL)
+    return fail(HKV_ERR_UNSUPPORTED, "dequantize: too many rows");
+  const hipError_t e = hkv::launch_dequantize(hkv::to_dev(*f), cache, num_kv_heads, slot_ids,
+                                              num_tokens, rotated != 0, k_out, v_out,
+                                              (hipStream_t)stream);
+  return e == hipSuccess ? HKV_OK : hip_fail(e, "dequantize launch");
+}
+
+size_t hkv_decode_workspace_bytes(const hkv_format* f, int32_t num_queries, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t max_klen,
+                                  int32_t queries_per_seq) {
+  if (check_format(f) != HKV_OK || num_queries < 0) return 0;
+  hkv::DecodePlan p;
+  if (!hkv::plan_decode(hkv::to_dev(*f), num_queries, num_q_heads, num_kv_heads, max_klen,
+                        queries_per_seq, &p))
+    return 0;
+  return p.workspace_bytes;
+}
+
+hkv_status hkv_decode_attention(const hkv_format* f, const void* query, hkv_dtype q_dtype,
+                                int32_t num_queries, int32_t num_q_heads, int32_t num_kv_heads,
+                                const uint8_t* cache, const int32_t* block_table,
+                                int32_t max_pages_per_req, const int32_t* q_to_req,
+                                const int32_t* q_to_klen, int32_t max_klen,
+                                int32_t queries_per_seq, float sm_scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  hkv_status st = check_format(f);
+  if (st != HKV_OK) return st;
+  if (num_queries < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(HKV_ERR_INVALID_ARG,
+                "decode: need num_q_heads a positive multiple of num_kv_heads (%d, %d), "
+                "num_queries >= 0 (%d)", num_q_heads, num_kv_heads, num_queries);
+  if (queries_per_seq < 1 || queries_per_seq > 8 || num_queries % queries_per_seq)
+    return fail(HKV_ERR_INVALID_ARG,
+                "decode: queries_per_seq must be in [1, 8] and divide num_queries (%d, %d)",
+                queries_per_seq, num_queries);
+  if (q_dtype != HKV_F32 && q_dtype != HKV_F16)
+    return fail(HKV_ERR_INVALID_ARG, "decode: bad query dtype %d", (int)q_dtype);
+  if (max_klen < 0) return fail(HKV_ERR_INVALID_ARG, "decode: max_klen < 0");
+  if (!std::isfinite(sm_scale)) return fail(HKV_ERR_INVALID_ARG, "decode: sm_scale not finite");
+  if (num_queries == 0) return HKV_OK;
+  if (!query || !cache || !block_table || !q_to_req || !q_to_klen || !out)
+    return fail(HKV_ERR_INVALID_ARG, "decode: NULL pointer");
+  if (max_pages_per_req <= 0) return fail(HKV_ERR_INVALID_ARG, "decode: max_pages_per_req <= 0");
+  if (!aligned(cache, 16)) return fail(HKV_ERR_INVALID_ARG, "cache must be 16-byte aligned");
+  const hkv::DevFmt d = hkv::to_dev(*f);
+  hkv::DecodePlan p;
+  if (!hkv::plan_decode(d, num_queries, num_q_heads, num_kv_heads, max_klen, queries_per_seq, &p))
+    return fail(HKV_ERR_UNSUPPORTED,
+                "decode: unsupported shape (query rows per KV head = %d x %d must be <= 32)",
+                num_q_heads / num_kv_heads, queries_per_seq);
+  if (workspace_bytes < p.workspace_bytes || (p.workspace_bytes && !workspace))
+    return fail(HKV_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
+                p.workspace_bytes, workspace_bytes);
+  if (workspace && !aligned(workspace, 16))
+    return fail(HKV_ERR_INVALID_ARG, "decode: workspace must be 16-byte aligned");
+  const hipError_t e = hkv::launch_decode(d, p, query, q_dtype == HKV_F16, num_q_heads,
+                                          num_kv_heads, cache, block_table, max_pages_per_req,
+                                          q_to_req, q_to_klen, sm_scale, out, workspace,
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? HKV_OK : hip_fail(e, "decode launch");
+}
+
+}  // extern "C"

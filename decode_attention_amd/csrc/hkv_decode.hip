@@ -1,0 +1,457 @@
+// hkv_decode.hip -- split-K paged decode attention over the rotated,
+// quantized cache, and the split merge that rotates the output back.
+//
+// What is computed (vLLM API docs "vllm.v1.attention.ops.rocm_octave",
+// reference_attention and module text; Strata pull request #21, "How" item 2
+// and the merge note): for query token i and query head h,
+//   out[i,h] = R_V^-1 sum_t softmax_t(scale * <R_K q[i,h], k'_t>) v'_t
+// over the first q_to_klen[i] tokens of sequence q_to_req[i], where k'_t, v'_t
+// are the cached codes dequantized in the rotated space and R_K, R_V the
+// sign-flip + Walsh-Hadamard rotations of K and V.  Scores use the rotated
+// query (the rotation is orthogonal, so <R q, R k> = <q, k>), values are
+// dequantized in registers inside an online-softmax accumulation, and the
+// output is rotated back once per query head.
+//
+// Generic kernel: grid (split, KV head, query group); 4 waves per workgroup.
+// A query group is n_q consecutive query tokens of one sequence; its
+// G * n_q query rows (G = query heads per KV head) share every K/V load.
+// Each wave streams 64-token tiles: the tile's slots are copied into LDS
+// with coalesced loads; scores are computed lane-per-token (the rotated,
+// pre-scaled query rows sit in LDS and are read as broadcasts); the online
+// softmax state is per row; P.V is computed lane-per-dimension.
+#include "hkv_internal.h"
+
+namespace hkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kTile = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecArgs {
+  const void* query;
+  int q_f16;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int n_q;
+  int rows;
+  int rows_pad;     // rows rounded up to the kernel's row count (partial records per split)
+  int num_queries;
+  const uint8_t* cache;
+  const int32_t* block_table;
+  int max_pages;
+  const int32_t* q_to_req;
+  const int32_t* q_to_klen;
+  float q_scale;  // sm_scale * log2(e): scores live in the exp2 domain
+  int tokens_per_split;
+  int num_splits;
+  float* ws;
+  int pstride;    // floats per partial record: 4 + D (m, l, pad, pad, o[D])
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t lds_word(const uint32_t* p, int byte_off) {
+  return p[byte_off >> 2];
+}
+
+// Code values (exact small integers) of K dims [d0, d0+32) of a slot held in
+// LDS as words, and the fp32 factor that turns them into rotated-space values.
+__device__ __forceinline__ void k_chunk(const DevFmt& f, const uint32_t* s, int d0,
+                                        float (&cv)[32], float& sc) {
+  const uint8_t* sb = (const uint8_t*)s;
+  if (f.kind == HKV_KIND_Q4_0) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t word = lds_word(s, d0 / 2 + 4 * w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        cv[8 * w + j] = (float)((int)((word >> (8 * (j & 3) + 4 * (j >> 2))) & 15u) - 8);
+    }
+    sc = h2f(rd16(sb + f.off_scales + 2 * (d0 >> 5)));
+    return;
+  }
+  const bool three = f.compact || d0 >= f.k_wide;
+  const int si = f.compact ? 0 : (d0 >> 6);
+  sc = h2f(rd16(sb + f.off_scales + 2 * si)) / (float)kLutOne;
+  if (!three) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t word = lds_word(s, d0 / 2 + 4 * w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        cv[8 * w + j] = (float)lut_value((int)((word >> (8 * (j & 3) + 4 * (j >> 2))) & 15u), 4);
+    }
+    return;
+  }
+  const int seg = f.compact ? 0 : f.off_k_nope;
+  const int n = f.compact ? f.D : f.D - f.k_wide;
+  const int i0 = f.compact ? d0 : d0 - f.k_wide;
+  const uint32_t lo0 = lds_word(s, seg + i0 / 4), lo1 = lds_word(s, seg + i0 / 4 + 4);
+  const uint32_t hi = lds_word(s, seg + n / 4 + i0 / 8);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t lo = (j < 16) ? lo0 : lo1;
+    const int c = (int)((lo >> (8 * (j & 3) + 2 * ((j >> 2) & 3))) & 3u) |
+                  (int)(((hi >> (8 * (j & 3) + (j >> 2))) & 1u) << 2);
+    cv[j] = (float)lut_value(c, 3);
+  }
+}
+
+// Rotated-space value of V dim d of a slot held in LDS.
+__device__ __forceinline__ float v_lds(const DevFmt& f, const uint32_t* s, int d) {
+  return v_value(f, (const uint8_t*)s, d);
+}
+
+template <int E, int R>
+__global__ __launch_bounds__(256) void decode_generic_kernel(DevFmt f, DecArgs a) {
+  constexpr int D = E * kWave;
+  extern __shared__ __align__(16) uint32_t smem[];
+  const int slot_words = f.slot_bytes / 4;
+  const int tstride = slot_words | 1;  // odd word stride: conflict-free lane-per-token reads
+  float* qs = (float*)smem;                               // [R][D]
+  float* pb = qs + R * D;                                 // [waves][R][kTile]
+  float* ml = pb + kWaves * R * kTile;                    // [waves][R][2]
+  uint32_t* tiles = (uint32_t*)(ml + kWaves * R * 2);     // [waves][kTile][tstride]
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int split = blockIdx.x, kvh = blockIdx.y, gi = blockIdx.z;
+  const int q0 = gi * a.n_q;
+  const int req = a.q_to_req[q0];
+  int kmax = 0;
+  for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
+  const int t_begin = split * a.tokens_per_split;
+  const int t_end = min(t_begin + a.tokens_per_split, kmax);
+  float* part = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits + split) * R * a.pstride;
+
+  if (t_begin >= t_end) {  // nothing to attend to in this split
+    for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
+      part[r * a.pstride + 0] = -INFINITY;
+      part[r * a.pstride + 1] = 0.0f;
+    }
+    return;
+  }
+
+  // Query rows: rotate like K (signs, then the K-block transform), fold in
+  // the softmax scale and log2(e); rows beyond a.rows are zero.
+  for (int r = wave; r < R; r += kWaves) {
+    float x[E];
+    if (r < a.rows) {
+      const int j = r / a.group, g = r % a.group;
+      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int d = kWave * e + lane;
+        x[e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * D + d])
+                       : ((const float*)a.query)[qrow * D + d];
+        if (f.use_signs) x[e] = apply_sign(f, x[e], d);
+      }
+      fwht_strided<E>(x, f.k_block, f.k_norm);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) qs[r * D + kWave * e + lane] = x[e] * a.q_scale;
+  }
+  __syncthreads();
+
+  int klen_row[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) klen_row[r] = (r < a.rows) ? a.q_to_klen[q0 + r / a.group] : 0;
+
+  float m[R], l[R], o[R][E];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[r][e] = 0.0f;
+  }
+
+  uint32_t* tile = tiles + wave * kTile * tstride;
+  float* pw = pb + wave * R * kTile;
+  const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
+
+  for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += kWaves * kTile) {
+    const int nvalid = min(kTile, t_end - t0);
+    // Stage the tile's slots in LDS (consecutive lanes read consecutive words).
+    for (int k = lane; k < nvalid * slot_words; k += kWave) {
+      const int tt = k / slot_words, w = k - tt * slot_words;
+      const int t = t0 + tt;
+      const uint32_t* src = (const uint32_t*)slot_ptr(f, a.cache, bt[t / f.page_size],
+                                                      t % f.page_size, a.num_kv_heads, kvh);
+      tile[tt * tstride + w] = src[w];
+    }
+    wave_sync_lds();
+
+    // Scores, lane per token.
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = 0.0f;
+    const uint32_t* my = tile + min(lane, nvalid - 1) * tstride;
+    for (int d0 = 0; d0 < D; d0 += 32) {
+      float cv[32], sc;
+      k_chunk(f, my, d0, cv, sc);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float4* qv = (const float4*)(qs + r * D + d0);
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float4 q4 = qv[j];
+          acc = fmaf(q4.x, cv[4 * j + 0], acc);
+          acc = fmaf(q4.y, cv[4 * j + 1], acc);
+          acc = fmaf(q4.z, cv[4 * j + 2], acc);
+          acc = fmaf(q4.w, cv[4 * j + 3], acc);
+        }
+        s[r] = fmaf(acc, sc, s[r]);
+      }
+    }
+    // Online softmax update (exp2 domain), per row.
+    const int t = t0 + lane;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float sr = (lane < nvalid && t < klen_row[r]) ? s[r] : -INFINITY;
+      const float mt = wave_max(sr);
+      const float mn = fmaxf(m[r], mt);
+      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m[r] - mn);
+      const float p = (sr == -INFINITY) ? 0.0f : exp2f(sr - mn);
+      l[r] = fmaf(l[r], alpha, p);
+      m[r] = mn;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[r][e] *= alpha;
+      pw[r * kTile + lane] = p;
+    }
+    wave_sync_lds();
+
+    // P.V, lane per dimension (dims E*lane .. E*lane+E-1).
+    for (int tt = 0; tt < nvalid; ++tt) {
+      const uint32_t* sl = tile + tt * tstride;
+      float vv[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) vv[e] = v_lds(f, sl, E * lane + e);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float p = pw[r * kTile + tt];
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[r][e] = fmaf(p, vv[e], o[r][e]);
+      }
+    }
+    wave_sync_lds();
+  }
+
+  // Merge the waves of the workgroup.  l holds per-lane partial sums.
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float lr = wave_tree_sum(l[r]);
+    if (lane == 0) {
+      ml[(wave * R + r) * 2 + 0] = m[r];
+      ml[(wave * R + r) * 2 + 1] = lr;
+    }
+  }
+  __syncthreads();
+  float* ob = qs;  // reuse the query area: [R][D]
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[(w * R + r) * 2]);
+    const float fw = (m[r] == -INFINITY) ? 0.0f : exp2f(m[r] - M);
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[r][e] *= fw;
+  }
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float* dst = &ob[r * D + E * lane + e];
+          *dst = (w == 0) ? o[r][e] : (*dst + o[r][e]);
+        }
+    }
+    __syncthreads();
+  }
+  for (int r = wave; r < a.rows; r += kWaves) {
+    float M = -INFINITY, L = 0.0f;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[(w * R + r) * 2]);
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = ml[(w * R + r) * 2];
+      if (mw != -INFINITY) L += ml[(w * R + r) * 2 + 1] * exp2f(mw - M);
+    }
+    float* pr = part + r * a.pstride;
+    if (lane == 0) {
+      pr[0] = M;
+      pr[1] = L;
+    }
+    for (int d = lane; d < D; d += kWave) pr[4 + d] = ob[r * D + d];
+  }
+}
+
+// Merge the split partials of one (query, head) row, normalise, rotate the
+// output back (transform with the V block, then the signs) and store fp32.
+template <int E>
+__global__ __launch_bounds__(256) void merge_kernel(DevFmt f, DecArgs a, float* out) {
+  constexpr int D = E * kWave;
+  const int lane = lane_id();
+  const int64_t rowid = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (rowid >= (int64_t)a.num_queries * a.num_q_heads) return;
+  const int i = (int)(rowid / a.num_q_heads);
+  const int h = (int)(rowid % a.num_q_heads);
+  const int gi = i / a.n_q, j = i % a.n_q;
+  const int kvh = h / a.group, g = h % a.group;
+  const int r = j * a.group + g;
+  const int Rp = a.rows_pad;
+  const float* base = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride;
+  float M = -INFINITY;
+  for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, base[((size_t)s * Rp + r) * a.pstride]);
+  float L = 0.0f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.num_splits; ++s) {
+      const float* pr = base + ((size_t)s * Rp + r) * a.pstride;
+      const float ms = pr[0];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - M);
+      L = fmaf(pr[1], w, L);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(pr[4 + kWave * e + lane], w, acc[e]);
+    }
+  }
+  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] *= inv;
+  fwht_strided<E>(acc, f.v_block, f.v_norm);
+  float* dst = out + ((int64_t)i * a.num_q_heads + h) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = kWave * e + lane;
+    dst[d] = f.use_signs ? apply_sign(f, acc[e], d) : acc[e];
+  }
+}
+
+int round_rows(int rows) {
+  int R = 1;
+  while (R < rows) R <<= 1;
+  return R;
+}
+
+size_t generic_lds_bytes(const DevFmt& f, int R) {
+  const int tstride = (f.slot_bytes / 4) | 1;
+  return sizeof(float) * ((size_t)R * f.D + (size_t)kWaves * R * kTile + (size_t)kWaves * R * 2) +
+         sizeof(uint32_t) * (size_t)kWaves * kTile * tstride;
+}
+
+template <int E, int R>
+hipError_t launch_generic_er(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
+  const size_t lds = generic_lds_bytes(f, R);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_generic_kernel<E, R>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  decode_generic_kernel<E, R><<<grid, dim3(kWaves * kWave), lds, s>>>(f, a);
+  return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_generic_e(const DevFmt& f, const DecArgs& a, int R, dim3 grid, hipStream_t s) {
+  switch (R) {
+    case 1: return launch_generic_er<E, 1>(f, a, grid, s);
+    case 2: return launch_generic_er<E, 2>(f, a, grid, s);
+    case 4: return launch_generic_er<E, 4>(f, a, grid, s);
+    case 8: return launch_generic_er<E, 8>(f, a, grid, s);
+    case 16: return launch_generic_er<E, 16>(f, a, grid, s);
+    case 32: return launch_generic_er<E, 32>(f, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_heads,
+                 int max_klen, int queries_per_seq, DecodePlan* p) {
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return false;
+  if (queries_per_seq < 1 || queries_per_seq > 8 || num_queries % queries_per_seq) return false;
+  DecodePlan q;
+  q.group = num_q_heads / num_kv_heads;
+  q.n_q = queries_per_seq;
+  q.rows = q.group * q.n_q;
+  if (q.rows > 32) return false;
+  q.num_groups = num_queries / queries_per_seq;
+  q.tokens_per_split = 1024;
+  q.num_splits = max_klen > 0 ? (max_klen + q.tokens_per_split - 1) / q.tokens_per_split : 1;
+  q.partial_floats = 4 + (size_t)f.D;
+  const int R = round_rows(q.rows);
+  q.workspace_bytes = sizeof(float) * q.partial_floats * R * (size_t)q.num_splits *
+                      (size_t)q.num_groups * (size_t)num_kv_heads;
+  if (generic_lds_bytes(f, R) > 160 * 1024) return false;
+  q.kernel = 0;
+  *p = q;
+  return true;
+}
+
+hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query, bool q_f16,
+                         int num_q_heads, int num_kv_heads, const uint8_t* cache,
+                         const int32_t* block_table, int max_pages_per_req,
+                         const int32_t* q_to_req, const int32_t* q_to_klen, float sm_scale,
+                         float* out, void* workspace, hipStream_t s) {
+  if (p.num_groups == 0) return hipSuccess;
+  DecArgs a;
+  a.query = query;
+  a.q_f16 = q_f16 ? 1 : 0;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = p.group;
+  a.n_q = p.n_q;
+  a.rows = p.rows;
+  a.rows_pad = round_rows(p.rows);
+  a.num_queries = p.num_groups * p.n_q;
+  a.cache = cache;
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_req;
+  a.q_to_req = q_to_req;
+  a.q_to_klen = q_to_klen;
+  a.q_scale = sm_scale * kLog2e;
+  a.tokens_per_split = p.tokens_per_split;
+  a.num_splits = p.num_splits;
+  a.ws = (float*)workspace;
+  a.pstride = (int)p.partial_floats;
+  const int R = round_rows(p.rows);
+  const dim3 grid(p.num_splits, num_kv_heads, p.num_groups);
+  hipError_t e;
+  switch (f.D / kWave) {
+    case 1: e = launch_generic_e<1>(f, a, R, grid, s); break;
+    case 2: e = launch_generic_e<2>(f, a, R, grid, s); break;
+    case 3: e = launch_generic_e<3>(f, a, R, grid, s); break;
+    case 4: e = launch_generic_e<4>(f, a, R, grid, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.num_groups * p.n_q * num_q_heads;
+  const dim3 mgrid((unsigned)((rows + kWaves - 1) / kWaves));
+  switch (f.D / kWave) {
+    case 1: merge_kernel<1><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
+    case 2: merge_kernel<2><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
+    case 3: merge_kernel<3><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
+    case 4: merge_kernel<4><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hkv

@@ -89,7 +89,7 @@ class Workload:
         if n == 0:
             return np.zeros(0, np.int64)
         return np.concatenate([np.arange(self.seq_start[b + 1] - n, self.seq_start[b + 1])
-                               for b in range(self.cfg.batch)]).astype(np.int64)
+                               for b in range(len(self.lengths))]).astype(np.int64)
 
 
 def _draw(rng: np.random.Generator, shape, scale_ch: Optional[np.ndarray], dtype: str,
@@ -110,8 +110,9 @@ def _draw(rng: np.random.Generator, shape, scale_ch: Optional[np.ndarray], dtype
 
 
 def make_workload(cfg: Config, seed: Optional[int] = None, batch: Optional[int] = None,
-                  seq_len: Optional[int] = None) -> Workload:
-    """Build the seeded workload of `cfg`; batch / seq_len may be shrunk for tests."""
+                  seq_len: Optional[int] = None, min_len: Optional[int] = None) -> Workload:
+    """Build the seeded workload of `cfg`; batch / seq_len / min_len may be
+    changed for tests (min_len makes the lengths vary)."""
     if seed is None:
         seed = 1000 + cfg.index
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -122,8 +123,9 @@ def make_workload(cfg: Config, seed: Optional[int] = None, batch: Optional[int] 
     n_out = cfg.n_outliers if cfg.n_outliers else int(math.ceil(cfg.outlier_frac * D))
     chans = np.sort(rng.choice(D, size=n_out, replace=False)) if n_out else np.zeros(0, np.int64)
 
-    if cfg.min_len is not None:
-        lo = min(cfg.min_len, Lmax)
+    lo_len = cfg.min_len if min_len is None else min_len
+    if lo_len is not None:
+        lo = min(lo_len, Lmax)
         lengths = rng.integers(lo, Lmax + 1, size=B).astype(np.int64)
     else:
         lengths = np.full(B, Lmax, np.int64)
@@ -167,7 +169,7 @@ def packed_bytes(w: Workload, slot_bytes: int) -> int:
     """Packed K/V bytes one decode call reads: sum over (sequence, KV head) of
     the longest klen among its queries times the slot size."""
     total = 0
-    for b in range(w.cfg.batch):
+    for b in range(len(w.lengths)):
         kl = w.q_to_klen[w.q_to_req == b]
         if len(kl):
             total += int(max(0, kl.max())) * w.cfg.num_kv_heads * slot_bytes

@@ -301,10 +301,20 @@ int32_t orc_bucket(float y, int32_t bits) {
   return code;
 }
 
-/* READING of the unspecified reduction order of a torch sum: pairwise tree;
- * while the count is even, add the upper half onto the lower half, then add
- * what is left from left to right.  Each product is rounded on its own. */
+/* READING of the unspecified reduction order of a torch sum: pairwise tree.
+ * When n = 64*m with m > 1 not a power of two, the m blocks of 64 are first
+ * added elementwise from left to right; then, while the count is even, the
+ * upper half is added onto the lower half; what is left is added from left
+ * to right.  Each product is rounded on its own. */
 static float tree_sum(float* t, int32_t n) {
+  if (n > 64 && n % 64 == 0 && !is_pow2(n / 64)) {
+    for (int32_t i = 0; i < 64; ++i) {
+      float acc = t[i];
+      for (int32_t b = 1; b < n / 64; ++b) acc = acc + t[64 * b + i];
+      t[i] = acc;
+    }
+    n = 64;
+  }
   while (n > 1 && n % 2 == 0) {
     const int32_t h = n / 2;
     for (int32_t i = 0; i < h; ++i) t[i] = t[i] + t[i + h];

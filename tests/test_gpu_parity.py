@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: packed cache bytes and dequantized values bit-exact; attention within
+|gpu - oracle| <= 2e-3 + 1e-3 * |oracle| elementwise (fp32 path vs the fp64
+definition).  Inputs come from the seeded workload generator; the oracle
+never sees anything the GPU produced.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_amd import hkv
+from decode_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-3
+DEV = "cuda:0"
+
+
+def _gpu_cache(f, w):
+    cfg = w.cfg
+    cache = hkv.new_cache(f, w.num_pages, cfg.num_kv_heads, DEV)
+    hkv.quantize_append(f, torch.from_numpy(w.key).to(DEV), torch.from_numpy(w.value).to(DEV),
+                        torch.from_numpy(w.slot_mapping).to(DEV), cache)
+    return cache
+
+
+def _oracle_cache(fo, w, shape):
+    slots = O.quantize(fo, w.key.astype(np.float32), w.value.astype(np.float32))
+    ref = np.zeros(shape, np.uint8)
+    P = w.cfg.page_size
+    ref[w.slot_mapping // P, :, w.slot_mapping % P] = slots
+    return ref, slots
+
+
+def _decode(f, w, cache, scale, qps=None):
+    cfg = w.cfg
+    return hkv.decode_attention(f, torch.from_numpy(w.query).to(DEV), cache,
+                                torch.from_numpy(w.block_table).to(DEV),
+                                torch.from_numpy(w.q_to_req).to(DEV),
+                                torch.from_numpy(w.q_to_klen).to(DEV), w.max_klen,
+                                cfg.n_q if qps is None else qps, scale)
+
+
+def _assert_close(got, ref, what):
+    got = got.astype(np.float64)
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; "
+                           f"max abs err {err.max():.3e}")
+    return float(err.max())
+
+
+SMALL = {   # config -> reduced sizes that still span several tiles, splits and a ragged tail
+    1: dict(),
+    2: dict(seq_len=2100),
+    3: dict(batch=2, seq_len=1537),
+    4: dict(batch=3, seq_len=700, min_len=300),
+    5: dict(batch=3, seq_len=1300, min_len=200),
+}
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
+def test_quantize_append_bit_exact(ci):
+    cfg = W.CONFIGS[ci]
+    w = W.make_workload(cfg, **SMALL[ci])
+    f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
+    fo = O.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim)
+    got = _gpu_cache(f, w).cpu().numpy()
+    ref, _ = _oracle_cache(fo, w, got.shape)
+    diff = got != ref
+    assert not diff.any(), f"config {ci}: {diff.sum()} bytes differ"
+
+
+@pytest.mark.parametrize("dtype,D,R", [("q4_0", 256, 0), ("q4_0", 128, 0), ("q4_0", 64, 0),
+                                       ("octave_k3v4", 128, 64), ("octave_k3v3", 128, 64),
+                                       ("octave_k3v3_compact", 256, 64), ("octave_k3v4", 192, 64),
+                                       ("octave_k3v4", 256, 128), ("octave_k3v3_compact", 64, 0),
+                                       ("octave_k3v4", 128, 0), ("octave_k3v4", 128, 128)])
+@pytest.mark.parametrize("in_dtype", [np.float32, np.float16])
+def test_quantize_and_dequantize_formats(dtype, D, R, in_dtype):
+    rng = np.random.default_rng(D + R)
+    T, H, P = 50, 3, 16
+    k = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
+    v = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
+    k[3] = 0
+    v[4, 1] = 0
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
+    pages = (T + P - 1) // P
+    sm = rng.permutation(pages * P)[:T].astype(np.int64)
+    sm[7] = -1                                         # skipped token
+    cache = hkv.new_cache(f, pages, H, DEV)
+    cache.fill_(0xA5)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    got = cache.cpu().numpy()
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    keep = sm >= 0
+    assert np.array_equal(got[sm[keep] // P, :, sm[keep] % P], slots[keep])
+    untouched = np.ones(pages * P, bool)
+    untouched[sm[keep]] = False
+    flat = got.transpose(0, 2, 1, 3).reshape(pages * P, H, -1)
+    assert np.all(flat[untouched] == 0xA5)             # nothing else written
+    for rotated in (True, False):
+        ids = torch.from_numpy(sm).to(DEV)
+        kd, vd = hkv.dequantize(f, cache, ids, rotated=rotated)
+        kr, vr = O.dequantize(fo, slots, rotated=rotated)
+        kd, vd = kd.cpu().numpy(), vd.cpu().numpy()
+        assert np.array_equal(kd[keep].view(np.uint32), kr[keep].view(np.uint32))
+        assert np.array_equal(vd[keep].view(np.uint32), vr[keep].view(np.uint32))
+        assert np.all(kd[~keep] == 0) and np.all(vd[~keep] == 0)
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
+def test_decode_matches_oracle(ci):
+    cfg = W.CONFIGS[ci]
+    w = W.make_workload(cfg, **SMALL[ci])
+    f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
+    fo = O.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim)
+    cache = _gpu_cache(f, w)
+    ref_cache, _ = _oracle_cache(fo, w, tuple(cache.shape))
+    scale = W.default_sm_scale(cfg.head_size)
+    got = _decode(f, w, cache, scale).cpu().numpy()
+    ref = O.attention(fo, w.query.astype(np.float32), ref_cache, w.block_table, w.q_to_req,
+                      w.q_to_klen, scale)
+    _assert_close(got, ref, f"config {ci}")
+
+
+@pytest.mark.parametrize("dtype,D,R,Hq,Hkv", [("q4_0", 256, 0, 16, 2), ("q4_0", 128, 0, 4, 4),
+                                              ("q4_0", 64, 0, 6, 3),
+                                              ("octave_k3v4", 128, 64, 32, 8),
+                                              ("octave_k3v3", 128, 64, 8, 1),
+                                              ("octave_k3v3_compact", 256, 64, 32, 4),
+                                              ("octave_k3v4", 192, 64, 4, 2)])
+def test_decode_edge_lengths(dtype, D, R, Hq, Hkv):
+    # klen 0, 1, one page, page +- 1, a split boundary +- 1 and a long ragged one
+    lens = [1, 15, 16, 17, 1023, 1024, 1025, 2500, 3]
+    rng = np.random.default_rng(D + Hq)
+    P = 16
+    T = sum(lens)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    pages = [(L + P - 1) // P for L in lens]
+    perm = rng.permutation(sum(pages))
+    bt = np.zeros((len(lens), max(pages)), np.int32)
+    sm = np.empty(T, np.int64)
+    off = t0 = 0
+    for b, L in enumerate(lens):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+        pos = np.arange(L)
+        sm[t0:t0 + L] = bt[b, pos // P].astype(np.int64) * P + pos % P
+        t0 += L
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
+    cache = hkv.new_cache(f, sum(pages), Hkv, DEV)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    ref_cache = np.zeros(tuple(cache.shape), np.uint8)
+    ref_cache[sm // P, :, sm % P] = slots
+    q_to_req = np.arange(len(lens), dtype=np.int32).repeat(2)
+    q_to_klen = np.array([[L, L - 1] for L in lens], np.int32).reshape(-1)
+    q_to_klen[1] = 0                 # klen 0 -> zero row
+    q_to_klen[-1] = -5               # negative -> zero row
+    q = rng.standard_normal((len(q_to_req), Hq, D)).astype(np.float32)
+    scale = W.default_sm_scale(D)
+    for qps in (1, 2):
+        got = hkv.decode_attention(f, torch.from_numpy(q).to(DEV), cache,
+                                   torch.from_numpy(bt).to(DEV), torch.from_numpy(q_to_req).to(DEV),
+                                   torch.from_numpy(q_to_klen).to(DEV), int(q_to_klen.max()), qps,
+                                   scale).cpu().numpy()
+        ref = O.attention(fo, q, ref_cache, bt, q_to_req, q_to_klen, scale)
+        _assert_close(got, ref, f"{dtype} qps={qps}")
+        assert np.all(got[1] == 0) and np.all(got[-1] == 0)
+
+
+def test_decode_is_deterministic_and_page_relabel_invariant():
+    cfg = W.CONFIGS[2]
+    w = W.make_workload(cfg, seq_len=3000)
+    f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
+    cache = _gpu_cache(f, w)
+    scale = W.default_sm_scale(cfg.head_size)
+    a = _decode(f, w, cache, scale).cpu().numpy()
+    b = _decode(f, w, cache, scale).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # relabel physical pages: identical result
+    perm = torch.randperm(cache.shape[0], generator=torch.Generator().manual_seed(0))
+    cache2 = torch.empty_like(cache)
+    cache2[perm.to(DEV)] = cache
+    w2 = W.Workload(**{**w.__dict__, "block_table": perm.numpy()[w.block_table].astype(np.int32)})
+    c = _decode(f, w2, cache2, scale).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+def test_requantize_reproduces_bytes():
+    cfg = W.CONFIGS[5]
+    w = W.make_workload(cfg, batch=2, seq_len=600)
+    f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
+    a = _gpu_cache(f, w).cpu().numpy()
+    b = _gpu_cache(f, w).cpu().numpy()
+    assert np.array_equal(a, b)
