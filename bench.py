@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: quantize-append of the
+new tokens of every sequence (FWHT + quantize + pack into the paged cache),
+then decode attention of the query tokens over the quantized cache (query
+rotation, in-register dequantization inside an online softmax, split merge,
+output rotated back).  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is packed-KV bytes the decode reads per step
+divided by the step time (GB/s); `roofline` rates the decode call (split
+kernel + merge kernel) against the 8 TB/s HBM peak; `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config 3]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = ("decode-attn packed-KV GB/s (% HBM peak) at 128K ctx; "
+          "quantize-append tokens/s")
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=3)
+    p.add_argument("--copies", type=int, default=0,
+                   help="cache copies rotated between steps (0: enough to exceed the "
+                        "256 MB Infinity Cache twice)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-threads", type=int, default=0)
+    p.add_argument("--profile", action="store_true",
+                   help="short run for a profiler: no CPU baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of 256 MiB (calibrates the HBM "
+                        "byte counters of rocprofv3)")
+    return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = (256 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "decode_attention_amd", "csrc")
+    for n in sorted(os.listdir(d)):
+        with open(os.path.join(d, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per decode call from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t
+
+
+def cpu_baseline(cfg, w, threads: int, scale: float):
+    """The oracle, as it is, on the host cores: quantize the appended rows and
+    run the fp64 attention for every query, one query per thread."""
+    import oracle as O
+    from decode_attention_amd import workloads as W
+
+    fo = O.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim)
+    S = fo.slot_bytes
+    # Oracle cache of the whole workload (setup, not timed), built in parallel.
+    T = w.key.shape[0]
+    slots = np.zeros((T, cfg.num_kv_heads, S), np.uint8)
+    chunks = np.array_split(np.arange(T), max(1, threads))
+
+    def qwork(ix):
+        if len(ix):
+            slots[ix[0]:ix[-1] + 1] = O.quantize(fo, w.key[ix[0]:ix[-1] + 1].astype(np.float32),
+                                                 w.value[ix[0]:ix[-1] + 1].astype(np.float32))
+    th = [threading.Thread(target=qwork, args=(c,)) for c in chunks]
+    [t.start() for t in th]
+    [t.join() for t in th]
+    cache = np.zeros((w.num_pages, cfg.num_kv_heads, cfg.page_size, S), np.uint8)
+    cache[w.slot_mapping // cfg.page_size, :, w.slot_mapping % cfg.page_size] = slots
+    rows = w.append_rows()
+    qf = w.query.astype(np.float32)
+    kf = w.key[rows].astype(np.float32)
+    vf = w.value[rows].astype(np.float32)
+    groups = [np.nonzero(w.q_to_req == b)[0] for b in range(len(w.lengths))]
+    n_threads = min(threads, len(groups))
+    results = [None] * len(groups)
+
+    def awork(gi):
+        for g in range(gi, len(groups), n_threads):
+            ix = groups[g]
+            results[g] = O.attention(fo, qf[ix], cache, w.block_table, w.q_to_req[ix],
+                                     w.q_to_klen[ix], scale)
+    t0 = time.perf_counter()
+    O.quantize(fo, kf, vf)
+    th = [threading.Thread(target=awork, args=(i,)) for i in range(n_threads)]
+    [t.start() for t in th]
+    [t.join() for t in th]
+    dt = time.perf_counter() - t0
+    nbytes = W.packed_bytes(w, S)
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": n_threads,
+            "kind": "oracle",
+            "sample": (f"the full step of the workload: quantize of {len(rows)} appended token "
+                       f"rows and fp64 attention of {len(w.q_to_req)} queries over "
+                       f"{nbytes} packed-KV bytes; {dt:.2f} s wall on {n_threads} threads")}
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described in DESIGN.md, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_attention_amd import hkv
+    from decode_attention_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.config]
+    w = W.make_workload(cfg)
+    f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
+    scale = W.default_sm_scale(cfg.head_size)
+    B, Hkv, Hq, D = len(w.lengths), cfg.num_kv_heads, cfg.num_q_heads, cfg.head_size
+
+    key = torch.from_numpy(w.key).to(dev)
+    value = torch.from_numpy(w.value).to(dev)
+    slot_mapping = torch.from_numpy(w.slot_mapping).to(dev)
+    rows = torch.from_numpy(w.append_rows()).to(dev)
+    new_k = key[rows].contiguous()
+    new_v = value[rows].contiguous()
+    new_sm = slot_mapping[rows].contiguous()
+    query = torch.from_numpy(w.query).to(dev)
+    block_table = torch.from_numpy(w.block_table).to(dev)
+    q_to_req = torch.from_numpy(w.q_to_req).to(dev)
+    q_to_klen = torch.from_numpy(w.q_to_klen).to(dev)
+    out = torch.empty((len(w.q_to_req), Hq, D), dtype=torch.float32, device=dev)
+    ws_bytes = hkv.decode_workspace_bytes(f, len(w.q_to_req), Hq, Hkv, w.max_klen, cfg.n_q)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    cache_bytes = w.num_pages * Hkv * cfg.page_size * f.slot_bytes
+    copies = args.copies or max(2, -(-2 * INFINITY_CACHE_BYTES // cache_bytes))
+    caches = [hkv.new_cache(f, w.num_pages, Hkv, dev) for _ in range(copies)]
+
+    # Bulk build of every cache copy (quantize-append of all tokens), timed.
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for c in caches:
+        hkv.quantize_append(f, key, value, slot_mapping, c)
+    e1.record()
+    torch.cuda.synchronize()
+    bulk_ms = e0.elapsed_time(e1) / copies
+    total_tokens = key.shape[0]
+    del key, value
+    torch.cuda.empty_cache()
+
+    def step(i):
+        c = caches[i % copies]
+        hkv.quantize_append(f, new_k, new_v, new_sm, c)
+        hkv.decode_attention(f, query, c, block_table, q_to_req, q_to_klen, w.max_klen, cfg.n_q,
+                             scale, out=out, workspace=workspace)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # Per-launch durations of the decode call and of the append, on the stream
+    # they run on (torch's current stream), events around each launch.
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    n_t = max(args.steps, 20)
+    decode_ms = timed(lambda i: hkv.decode_attention(
+        f, query, caches[i % copies], block_table, q_to_req, q_to_klen, w.max_klen, cfg.n_q,
+        scale, out=out, workspace=workspace), n_t)
+    append_ms = timed(lambda i: hkv.quantize_append(f, new_k, new_v, new_sm, caches[i % copies]),
+                      n_t)
+
+    packed = W.packed_bytes(w, f.slot_bytes)
+    value = packed / (ms_per_step * 1e-3) / 1e9
+    achieved = packed / (decode_ms * 1e-3) / 1e9
+    traffic = load_traffic(cfg.name)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "cache_dtype": cfg.cache_dtype, "batch": B,
+                   "context": int(w.max_klen), "head_size": D, "q_heads": Hq, "kv_heads": Hkv,
+                   "page_size": cfg.page_size, "queries_per_seq": cfg.n_q,
+                   "append_tokens_per_seq": cfg.n_append, "cache_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_call"],
+                     "kernel": "hkv_decode_attention (split-K kernel + merge kernel)",
+                     "bytes_per_call": packed, "us_per_call": round(decode_ms * 1e3, 3)},
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "append_us": round(append_ms * 1e3, 3),
+        "append_tokens_per_s": round(len(rows) / (append_ms * 1e-3), 1),
+        "bulk_quantize_tokens_per_s": round(total_tokens / (bulk_ms * 1e-3), 1),
+        "bulk_quantize_gbps": round((2 * total_tokens * Hkv * D * w.key.itemsize +
+                                     total_tokens * Hkv * f.slot_bytes) / (bulk_ms * 1e-3) / 1e9,
+                                    3),
+    }
+    if not args.no_cpu_baseline and not args.profile:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        rec["cpu_baseline"] = cpu_baseline(cfg, w, threads, scale)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

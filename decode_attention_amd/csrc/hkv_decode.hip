@@ -19,48 +19,10 @@
 // with coalesced loads; scores are computed lane-per-token (the rotated,
 // pre-scaled query rows sit in LDS and are read as broadcasts); the online
 // softmax state is per row; P.V is computed lane-per-dimension.
-#include "hkv_internal.h"
+#include "hkv_decode_common.h"
 
 namespace hkv {
 namespace {
-
-constexpr int kWaves = 4;
-constexpr int kTile = 64;
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct DecArgs {
-  const void* query;
-  int q_f16;
-  int num_q_heads;
-  int num_kv_heads;
-  int group;
-  int n_q;
-  int rows;
-  int rows_pad;     // rows rounded up to the kernel's row count (partial records per split)
-  int num_queries;
-  const uint8_t* cache;
-  const int32_t* block_table;
-  int max_pages;
-  const int32_t* q_to_req;
-  const int32_t* q_to_klen;
-  float q_scale;  // sm_scale * log2(e): scores live in the exp2 domain
-  int tokens_per_split;
-  int num_splits;
-  float* ws;
-  int pstride;    // floats per partial record: 4 + D (m, l, pad, pad, o[D])
-};
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
-  return v;
-}
-
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __device__ __forceinline__ uint32_t lds_word(const uint32_t* p, int byte_off) {
   return p[byte_off >> 2];
@@ -187,13 +149,14 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DevFmt f, DecArgs a
 
   for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += kWaves * kTile) {
     const int nvalid = min(kTile, t_end - t0);
-    // Stage the tile's slots in LDS (consecutive lanes read consecutive words).
-    for (int k = lane; k < nvalid * slot_words; k += kWave) {
-      const int tt = k / slot_words, w = k - tt * slot_words;
+    // Stage the tile's slots in LDS: one slot per step, its words spread over
+    // the lanes (a coalesced run of slot_bytes); the page lookup is uniform.
+#pragma unroll 8
+    for (int tt = 0; tt < nvalid; ++tt) {
       const int t = t0 + tt;
       const uint32_t* src = (const uint32_t*)slot_ptr(f, a.cache, bt[t / f.page_size],
                                                       t % f.page_size, a.num_kv_heads, kvh);
-      tile[tt * tstride + w] = src[w];
+      for (int w = lane; w < slot_words; w += kWave) tile[tt * tstride + w] = src[w];
     }
     wave_sync_lds();
 
@@ -302,12 +265,14 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DevFmt f, DecArgs a
 
 // Merge the split partials of one (query, head) row, normalise, rotate the
 // output back (transform with the V block, then the signs) and store fp32.
+// One workgroup per row: the four waves take every fourth split.
 template <int E>
 __global__ __launch_bounds__(256) void merge_kernel(DevFmt f, DecArgs a, float* out) {
   constexpr int D = E * kWave;
+  __shared__ float red[kWaves][D + 2];
   const int lane = lane_id();
-  const int64_t rowid = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (rowid >= (int64_t)a.num_queries * a.num_q_heads) return;
+  const int wave = threadIdx.x >> 6;
+  const int64_t rowid = blockIdx.x;
   const int i = (int)(rowid / a.num_q_heads);
   const int h = (int)(rowid % a.num_q_heads);
   const int gi = i / a.n_q, j = i % a.n_q;
@@ -315,21 +280,39 @@ __global__ __launch_bounds__(256) void merge_kernel(DevFmt f, DecArgs a, float* 
   const int r = j * a.group + g;
   const int Rp = a.rows_pad;
   const float* base = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride;
+  // Global max of the split maxima.
   float M = -INFINITY;
-  for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, base[((size_t)s * Rp + r) * a.pstride]);
+  for (int s = threadIdx.x; s < a.num_splits; s += blockDim.x)
+    M = fmaxf(M, base[((size_t)s * Rp + r) * a.pstride]);
+  M = wave_max(M);
+  if (lane == 0) red[wave][0] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+  __syncthreads();
   float L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < a.num_splits; ++s) {
+#pragma unroll 4
+    for (int s = wave; s < a.num_splits; s += kWaves) {
       const float* pr = base + ((size_t)s * Rp + r) * a.pstride;
       const float ms = pr[0];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
+      const float w = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
       L = fmaf(pr[1], w, L);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = fmaf(pr[4 + kWave * e + lane], w, acc[e]);
     }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[wave][kWave * e + lane] = acc[e];
+  if (lane == 0) red[wave][D] = L;
+  __syncthreads();
+  if (wave != 0) return;
+  L = red[0][D] + red[1][D] + red[2][D] + red[3][D];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = kWave * e + lane;
+    acc[e] = (red[0][d] + red[1][d]) + (red[2][d] + red[3][d]);
   }
   const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
 #pragma unroll
@@ -384,6 +367,9 @@ hipError_t launch_generic_e(const DevFmt& f, const DecArgs& a, int R, dim3 grid,
 
 }  // namespace
 
+bool q4_mfma_supported(const DevFmt& f, int rows);
+hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
+
 bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_heads,
                  int max_klen, int queries_per_seq, DecodePlan* p) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return false;
@@ -394,14 +380,14 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   q.rows = q.group * q.n_q;
   if (q.rows > 32) return false;
   q.num_groups = num_queries / queries_per_seq;
-  q.tokens_per_split = 1024;
+  q.kernel = q4_mfma_supported(f, q.rows) ? 1 : 0;
+  q.tokens_per_split = q.kernel == 1 ? 2048 : 1024;
   q.num_splits = max_klen > 0 ? (max_klen + q.tokens_per_split - 1) / q.tokens_per_split : 1;
-  q.partial_floats = 4 + (size_t)f.D;
-  const int R = round_rows(q.rows);
+  q.partial_floats = kPartialHead + (size_t)f.D;
+  const int R = q.kernel == 1 ? 8 : round_rows(q.rows);
   q.workspace_bytes = sizeof(float) * q.partial_floats * R * (size_t)q.num_splits *
                       (size_t)q.num_groups * (size_t)num_kv_heads;
-  if (generic_lds_bytes(f, R) > 160 * 1024) return false;
-  q.kernel = 0;
+  if (q.kernel == 0 && generic_lds_bytes(f, R) > 160 * 1024) return false;
   *p = q;
   return true;
 }
@@ -420,7 +406,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   a.group = p.group;
   a.n_q = p.n_q;
   a.rows = p.rows;
-  a.rows_pad = round_rows(p.rows);
+  a.rows_pad = p.kernel == 1 ? 8 : round_rows(p.rows);
   a.num_queries = p.num_groups * p.n_q;
   a.cache = cache;
   a.block_table = block_table;
@@ -435,7 +421,9 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   const int R = round_rows(p.rows);
   const dim3 grid(p.num_splits, num_kv_heads, p.num_groups);
   hipError_t e;
-  switch (f.D / kWave) {
+  if (p.kernel == 1) {
+    e = launch_decode_q4_mfma(f, a, grid, s);
+  } else switch (f.D / kWave) {
     case 1: e = launch_generic_e<1>(f, a, R, grid, s); break;
     case 2: e = launch_generic_e<2>(f, a, R, grid, s); break;
     case 3: e = launch_generic_e<3>(f, a, R, grid, s); break;
@@ -444,7 +432,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   }
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.num_groups * p.n_q * num_q_heads;
-  const dim3 mgrid((unsigned)((rows + kWaves - 1) / kWaves));
+  const dim3 mgrid((unsigned)rows);
   switch (f.D / kWave) {
     case 1: merge_kernel<1><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
     case 2: merge_kernel<2><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
