@@ -297,10 +297,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DevFmt f, DecArgs a, float* 
     for (int s = wave; s < a.num_splits; s += kWaves) {
       const float* pr = base + ((size_t)s * Rp + r) * a.pstride;
       const float ms = pr[0];
-      const float w = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+      if (ms == -INFINITY) continue;  // empty split: its o words are never written
+      const float w = exp2f(ms - M);
       L = fmaf(pr[1], w, L);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(pr[4 + kWave * e + lane], w, acc[e]);
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(pr[kPartialHead + kWave * e + lane], w, acc[e]);
     }
   }
 #pragma unroll

@@ -35,6 +35,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 256;        // head size handled here
 constexpr int kNB = kD / 32;   // Q4_0 blocks per head vector
@@ -43,6 +44,7 @@ constexpr int kT = 16;         // tokens per tile
 constexpr int kQMaxI = 32639;  // largest |q| code of the two-plane int8 split
 constexpr float kQMax = 32639.0f;
 constexpr int kVStride = kT + 4;  // padded token stride of the transposed V tile
+constexpr float kLazy = 8.0f;     // log2 headroom before the running max is raised
 
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
@@ -87,7 +89,6 @@ __device__ __forceinline__ void load_tile(Tile& x, const uint8_t* slot, int gq, 
 
 __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArgs a) {
   __shared__ __align__(16) int8_t qB[kNB][16][32];      // B operand bytes: [block][column][dim]
-  __shared__ int corr[kNB][16];                          // -8 * block sum of each plane
   __shared__ float qsc[kRows];                           // per-row score scale
   __shared__ __align__(16) uint32_t vt[kWaves][kNB][4][kVStride];  // V words, token-minor
   __shared__ __align__(16) uint4 scl[kWaves][2][kT];          // K / V scale chunks
@@ -147,36 +148,26 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
       const int d = kWave * e + lane;
       qB[d >> 5][r][d & 31] = (int8_t)hi;
       qB[d >> 5][8 + r][d & 31] = (int8_t)lo;
-      int shi = hi, slo = lo;
-#pragma unroll
-      for (int m = 16; m >= 1; m >>= 1) {
-        shi += __shfl_xor(shi, m, kWave);
-        slo += __shfl_xor(slo, m, kWave);
-      }
-      if ((lane & 31) == 0) {
-        corr[d >> 5][r] = -8 * shi;
-        corr[d >> 5][8 + r] = -8 * slo;
-      }
     }
-    if (lane == 0) qsc[r] = (qmax / kQMax) * a.q_scale;
+    if (lane == 0) qsc[r] = (qmax / kQMax) * a.q_scale * 0.0625f;
   }
   __syncthreads();
 
   const int n = lane & 15;   // score column (row r = n & 7, plane = n >> 3)
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of a tile in the score layout
-  long qb[kNB];
-  int cin[kNB];
-#pragma unroll
-  for (int b = 0; b < kNB; ++b) {
-    qb[b] = *(const long*)&qB[b][n][8 * g];
-    cin[b] = corr[b][n];
-  }
   const int row = n & 7;
   const float qs = qsc[row];
   const int klen_row = row < a.rows ? a.q_to_klen[q0 + row / a.group] : 0;
-  const bool live_row = (n < 8) && (row < a.rows);
+  const bool live_row = row < a.rows;  // lanes n and n + 8 carry the same row
   const uint32_t vsel = (uint32_t)(n & 3) | (0x0Cu << 8) | ((uint32_t)(4 + (n & 3)) << 16) |
                         (0x0Cu << 24);
+  // Nibble masks kept in VGPRs so that mask-and-bias fuses into v_and_or_b32.
+  uint32_t m0f, mf0;
+  asm volatile("v_mov_b32 %0, 0x0f0f0f0f" : "=v"(m0f));
+  asm volatile("v_mov_b32 %0, 0xf0f0f0f0" : "=v"(mf0));
+  int kmin = kmax;
+  for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
+  const int t_lim = min(t_end, kmin);  // tiles ending at or before this need no mask
   const half2_t c1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const half2_t c16 = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2_t c72 = {(_Float16)-72.0f, (_Float16)-72.0f};
@@ -209,65 +200,76 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
   };
   load_pids(0);
 
-  Tile cur, nxt;
-  if (my_tiles > 0) load_tile(cur, tile_slot(0), gq, scale_lane, scale_kind);
-  for (int k = 0; k < my_tiles; ++k) {
-    const int t0 = t_begin + kT * (wave + kWaves * k);
-    if (k + 1 < my_tiles) {
-      if (((k + 1) & 63) == 0) load_pids(k + 1);
-      load_tile(nxt, tile_slot(k + 1), gq, scale_lane, scale_kind);
+  // Three tile buffers: while a tile is processed the next two are in flight.
+  auto fetch = [&](Tile& x, int k) {
+    if (k < my_tiles) {
+      if (k > 0 && (k & 63) == 0) load_pids(k);
+      load_tile(x, tile_slot(k), gq, scale_lane, scale_kind);
     }
-
+  };
+  auto process = [&](const Tile& cur, int k) {
+    const int t0 = t_begin + kT * (wave + kWaves * k);
     // K words: word gq of block w (k0) and of block 4+w (k1).
     uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
     lanegroup_transpose(kw[0], kw[1], kw[2], kw[3]);
     lanegroup_transpose(kw[4], kw[5], kw[6], kw[7]);
     // V words and scales to LDS.
-    vt[wave][gq][0][tl] = cur.v0.x;
-    vt[wave][gq][1][tl] = cur.v0.y;
-    vt[wave][gq][2][tl] = cur.v0.z;
-    vt[wave][gq][3][tl] = cur.v0.w;
-    vt[wave][4 + gq][0][tl] = cur.v1.x;
-    vt[wave][4 + gq][1][tl] = cur.v1.y;
-    vt[wave][4 + gq][2][tl] = cur.v1.z;
-    vt[wave][4 + gq][3][tl] = cur.v1.w;
+    uint32_t* vw = &vt[wave][0][0][tl];
+    vw[((gq) * 4 + 0) * kVStride] = cur.v0.x;
+    vw[((gq) * 4 + 1) * kVStride] = cur.v0.y;
+    vw[((gq) * 4 + 2) * kVStride] = cur.v0.z;
+    vw[((gq) * 4 + 3) * kVStride] = cur.v0.w;
+    vw[((4 + gq) * 4 + 0) * kVStride] = cur.v1.x;
+    vw[((4 + gq) * 4 + 1) * kVStride] = cur.v1.y;
+    vw[((4 + gq) * 4 + 2) * kVStride] = cur.v1.z;
+    vw[((4 + gq) * 4 + 3) * kVStride] = cur.v1.w;
     if (scale_lane) scl[wave][scale_kind][tl] = cur.sc;
     wave_sync_lds();
-    uint4 ks[4], vs[4];
+    uint4 ks[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ks[i] = scl[wave][0][4 * g + i];
-      vs[i] = scl[wave][1][4 * g + i];
-    }
+    for (int i = 0; i < 4; ++i) ks[i] = scl[wave][0][4 * g + i];
 
-    // Scores.
+    // Scores: per block an int32 tile (16 (code - 8) x int8 planes) scaled
+    // by the token's block scale into fp32; the 1/16 is in the row scale.
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int4_t zero4 = {0, 0, 0, 0};
+    int4_t C;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      const uint32_t w = kw[b];
-      const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-      const long A = (long)((uint64_t)lo | ((uint64_t)hi << 32));
-      int4_t C = {cin[b], cin[b], cin[b], cin[b]};
-      C = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, qb[b], C, 0, 0, 0);
+      // Flipping bit 3 of a code turns it into the 4-bit two's complement of
+      // (code - 8); placed in the high nibble of a byte it reads as the int8
+      // 16 * (code - 8).  Low nibbles are dims 0..3, high nibbles dims 4..7.
+      const uint32_t x = kw[b] ^ 0x88888888u;
+      const int2_t A2 = {(int)((x << 4) & mf0), (int)(x & mf0)};
+      C = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, A2),
+                                                 *(const long*)&qB[b][n][8 * g], zero4, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = fmaf((float)C[i], scale_of(ks[i], b), acc[i]);
     }
     float s[4];
+    const bool full = t0 + kT <= t_lim;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float pt = ror8(acc[i]);
       const float hiv = n < 8 ? acc[i] : pt, lov = n < 8 ? pt : acc[i];
-      float v = fmaf(hiv, 256.0f, lov) * qs;
-      const int tok = t0 + 4 * g + i;
-      s[i] = (tok < t_end && tok < klen_row) ? v : -INFINITY;
+      s[i] = fmaf(hiv, 256.0f, lov) * qs;
     }
-    // Online softmax (exp2 domain), one row per score column.
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 4 * g + i;
+        s[i] = (tok < t_end && tok < klen_row) ? s[i] : -INFINITY;
+      }
+    }
+    // Online softmax in the exp2 domain.  The running maximum is raised only
+    // when a tile exceeds it by more than kLazy, so p <= 2^kLazy and the
+    // rescale of the accumulators is rare.
     float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float m_new = fmaxf(m_run, mt);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
       l_run *= alpha;
       float al[4];
 #pragma unroll
@@ -282,34 +284,81 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
       m_run = m_new;
     }
     float p[4];
+    const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;  // rows with nothing valid yet
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+      p[i] = exp2f(s[i] - m_ref);  // exp2(-inf) = 0
       l_run += p[i];
       p[i] = live_row ? p[i] : 0.0f;
     }
 
-    // P.V.
+    // P.V.  A rows 0-7 carry p rounded to fp16, rows 8-15 the residual
+    // p - p_hi (scaled by 2^12 to stay in the normal fp16 range); B carries
+    // (code - 8) * v_scale split exactly into an fp16 high part and the fp16
+    // residual (a 4-bit integer times an 11-bit mantissa has <= 15 bits), so
+    // P.V keeps ~22 bits of p and the exact dequantized values.
+    half2_t a01, a23;
+    {
+      const half2_t h01 = {(_Float16)p[0], (_Float16)p[1]};
+      const half2_t h23 = {(_Float16)p[2], (_Float16)p[3]};
+      const half2_t r01 = {(_Float16)((p[0] - (float)h01[0]) * 4096.0f),
+                           (_Float16)((p[1] - (float)h01[1]) * 4096.0f)};
+      const half2_t r23 = {(_Float16)((p[2] - (float)h23[0]) * 4096.0f),
+                           (_Float16)((p[3] - (float)h23[1]) * 4096.0f)};
+      a01 = n < 8 ? h01 : r01;
+      a23 = n < 8 ? h23 : r23;
+    }
+    const half4_t A = {a01[0], a01[1], a23[0], a23[1]};
+    uint4 vs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vs[i] = scl[wave][1][4 * g + i];
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const uint4 W = *(const uint4*)&vt[wave][b][n >> 2][4 * g];
       const uint32_t x01 = __builtin_amdgcn_perm(W.y, W.x, vsel);
       const uint32_t x23 = __builtin_amdgcn_perm(W.w, W.z, vsel);
-      const half2_t l0 = as_h2((x01 & 0x000F000Fu) | 0x64006400u) + c1032;
-      const half2_t l1 = as_h2((x23 & 0x000F000Fu) | 0x64006400u) + c1032;
-      const half2_t h0 = __builtin_elementwise_fma(as_h2((x01 & 0x00F000F0u) | 0x64006400u), c16, c72);
-      const half2_t h1 = __builtin_elementwise_fma(as_h2((x23 & 0x00F000F0u) | 0x64006400u), c16, c72);
-      half4_t A;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) A[i] = (_Float16)(p[i] * scale_of(vs[i], b));
-      const half4_t Bl = {l0[0], l0[1], l1[0], l1[1]};
-      const half4_t Bh = {h0[0], h0[1], h1[0], h1[1]};
-      o[b][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bl, o[b][0], 0, 0, 0);
-      o[b][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bh, o[b][1], 0, 0, 0);
+      const half2_t l01 = as_h2((x01 & m0f) | 0x64006400u) + c1032;
+      const half2_t l23 = as_h2((x23 & m0f) | 0x64006400u) + c1032;
+      const half2_t g01 = __builtin_elementwise_fma(as_h2((x01 & mf0) | 0x64006400u), c16, c72);
+      const half2_t g23 = __builtin_elementwise_fma(as_h2((x23 & mf0) | 0x64006400u), c16, c72);
+      // v_scale of block b for the token pairs (t0, t1) and (t2, t3).
+      constexpr uint32_t kSel[2] = {0x05040100u, 0x07060302u};
+      const uint32_t w0 = (b >> 1) == 0 ? vs[0].x : (b >> 1) == 1 ? vs[0].y : (b >> 1) == 2 ? vs[0].z : vs[0].w;
+      const uint32_t w1 = (b >> 1) == 0 ? vs[1].x : (b >> 1) == 1 ? vs[1].y : (b >> 1) == 2 ? vs[1].z : vs[1].w;
+      const uint32_t w2 = (b >> 1) == 0 ? vs[2].x : (b >> 1) == 1 ? vs[2].y : (b >> 1) == 2 ? vs[2].z : vs[2].w;
+      const uint32_t w3 = (b >> 1) == 0 ? vs[3].x : (b >> 1) == 1 ? vs[3].y : (b >> 1) == 2 ? vs[3].z : vs[3].w;
+      const half2_t d01 = as_h2(__builtin_amdgcn_perm(w1, w0, kSel[b & 1]));
+      const half2_t d23 = as_h2(__builtin_amdgcn_perm(w3, w2, kSel[b & 1]));
+      const half2_t l01h = l01 * d01, l23h = l23 * d23, g01h = g01 * d01, g23h = g23 * d23;
+      const half2_t l01l = __builtin_elementwise_fma(l01, d01, -l01h);
+      const half2_t l23l = __builtin_elementwise_fma(l23, d23, -l23h);
+      const half2_t g01l = __builtin_elementwise_fma(g01, d01, -g01h);
+      const half2_t g23l = __builtin_elementwise_fma(g23, d23, -g23h);
+      o[b][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, (half4_t){l01h[0], l01h[1], l23h[0], l23h[1]}, o[b][0], 0, 0, 0);
+      o[b][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, (half4_t){l01l[0], l01l[1], l23l[0], l23l[1]}, o[b][0], 0, 0, 0);
+      o[b][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, (half4_t){g01h[0], g01h[1], g23h[0], g23h[1]}, o[b][1], 0, 0, 0);
+      o[b][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, (half4_t){g01l[0], g01l[1], g23l[0], g23l[1]}, o[b][1], 0, 0, 0);
     }
     wave_sync_lds();
-    cur = nxt;
+  };
+  Tile ta, tb, tc;
+  fetch(ta, 0);
+  fetch(tb, 1);
+  for (int k = 0; k < my_tiles; ++k) {
+    fetch(tc, k + 2);
+    process(ta, k);
+    ta = tb;
+    tb = tc;
   }
+
+  // Rows 8-15 of the P.V tiles hold the residual part (x 2^12): fold them in.
+#pragma unroll
+  for (int b = 0; b < kNB; ++b)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[b][m][i] = fmaf(__shfl_xor(o[b][m][i], 32, kWave), 1.0f / 4096.0f, o[b][m][i]);
 
   // ---- merge the four waves ----------------------------------------------
   float lsum = l_run + __shfl_xor(l_run, 16, kWave);
