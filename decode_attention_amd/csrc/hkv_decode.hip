@@ -265,11 +265,18 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DevFmt f, DecArgs a
 
 // Merge the split partials of one (query, head) row, normalise, rotate the
 // output back (transform with the V block, then the signs) and store fp32.
-// One workgroup per row: the four waves take every fourth split.
+// One workgroup per row; wave w takes splits w, w + kMergeWaves, ...  Only
+// the splits that start below the row's own klen are visited: each of those
+// holds at least one of the row's tokens, so its whole record was written and
+// is finite, and no split is skipped by a data-dependent branch (which would
+// serialise the loads).
+constexpr int kMergeWaves = 8;
+
 template <int E>
-__global__ __launch_bounds__(256) void merge_kernel(DevFmt f, DecArgs a, float* out) {
+__global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, DecArgs a,
+                                                                   float* out) {
   constexpr int D = E * kWave;
-  __shared__ float red[kWaves][D + 2];
+  __shared__ float red[kMergeWaves][D + 2];
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int64_t rowid = blockIdx.x;
@@ -279,41 +286,48 @@ __global__ __launch_bounds__(256) void merge_kernel(DevFmt f, DecArgs a, float* 
   const int kvh = h / a.group, g = h % a.group;
   const int r = j * a.group + g;
   const int Rp = a.rows_pad;
+  const int klen = a.q_to_klen[i];
+  const int n_live = klen <= 0 ? 0 : min(a.num_splits, (klen + a.tokens_per_split - 1) /
+                                                           a.tokens_per_split);
   const float* base = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride;
+  const size_t sstride = (size_t)Rp * a.pstride;
   // Global max of the split maxima.
   float M = -INFINITY;
-  for (int s = threadIdx.x; s < a.num_splits; s += blockDim.x)
-    M = fmaxf(M, base[((size_t)s * Rp + r) * a.pstride]);
+  for (int s = threadIdx.x; s < n_live; s += blockDim.x) M = fmaxf(M, base[s * sstride + r * a.pstride]);
   M = wave_max(M);
   if (lane == 0) red[wave][0] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+  M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, red[w][0]);
   __syncthreads();
   float L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  if (M != -INFINITY) {
+  const float* pr = base + (size_t)r * a.pstride + kPartialHead + lane;
 #pragma unroll 4
-    for (int s = wave; s < a.num_splits; s += kWaves) {
-      const float* pr = base + ((size_t)s * Rp + r) * a.pstride;
-      const float ms = pr[0];
-      if (ms == -INFINITY) continue;  // empty split: its o words are never written
-      const float w = exp2f(ms - M);
-      L = fmaf(pr[1], w, L);
+  for (int s = wave; s < n_live; s += kMergeWaves) {
+    const float* ps = pr + s * sstride;
+    const float w = exp2f(ps[-kPartialHead - lane] - M);
+    L = fmaf(ps[1 - kPartialHead - lane], w, L);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(pr[kPartialHead + kWave * e + lane], w, acc[e]);
-    }
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(ps[kWave * e], w, acc[e]);
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) red[wave][kWave * e + lane] = acc[e];
   if (lane == 0) red[wave][D] = L;
   __syncthreads();
   if (wave != 0) return;
-  L = red[0][D] + red[1][D] + red[2][D] + red[3][D];
+  L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) L += red[w][D];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int d = kWave * e + lane;
-    acc[e] = (red[0][d] + red[1][d]) + (red[2][d] + red[3][d]);
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) t += red[w][d];
+    acc[e] = t;
   }
   const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
 #pragma unroll
@@ -435,10 +449,10 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   const int64_t rows = (int64_t)p.num_groups * p.n_q * num_q_heads;
   const dim3 mgrid((unsigned)rows);
   switch (f.D / kWave) {
-    case 1: merge_kernel<1><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
-    case 2: merge_kernel<2><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
-    case 3: merge_kernel<3><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
-    case 4: merge_kernel<4><<<mgrid, dim3(kWaves * kWave), 0, s>>>(f, a, out); break;
+    case 1: merge_kernel<1><<<mgrid, dim3(kMergeWaves * kWave), 0, s>>>(f, a, out); break;
+    case 2: merge_kernel<2><<<mgrid, dim3(kMergeWaves * kWave), 0, s>>>(f, a, out); break;
+    case 3: merge_kernel<3><<<mgrid, dim3(kMergeWaves * kWave), 0, s>>>(f, a, out); break;
+    case 4: merge_kernel<4><<<mgrid, dim3(kMergeWaves * kWave), 0, s>>>(f, a, out); break;
   }
   return hipGetLastError();
 }

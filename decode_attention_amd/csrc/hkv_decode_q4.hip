@@ -41,12 +41,12 @@ constexpr int kD = 256;        // head size handled here
 constexpr int kNB = kD / 32;   // Q4_0 blocks per head vector
 constexpr int kRows = 8;       // query rows per KV head
 constexpr int kT = 16;         // tokens per tile
+constexpr int kSlot = kD + kD / 8;  // Q4_0 slot bytes at head size 256
 constexpr int kQMaxI = 32639;  // largest |q| code of the two-plane int8 split
 constexpr float kQMax = 32639.0f;
 constexpr int kVStride = kT + 4;  // padded token stride of the transposed V tile
 constexpr float kLazy = 8.0f;     // log2 headroom before the running max is raised
 
-__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
 // 4x4 transpose across the four 16-lane groups: register w of group g
 // receives register g of group w.
@@ -168,9 +168,6 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
   int kmin = kmax;
   for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
   const int t_lim = min(t_end, kmin);  // tiles ending at or before this need no mask
-  const half2_t c1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const half2_t c16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const half2_t c72 = {(_Float16)-72.0f, (_Float16)-72.0f};
 
   float4_t o[kNB][2];
 #pragma unroll
@@ -181,7 +178,8 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
   // page.  The page ids of 64 tiles at a time are fetched one per lane and
   // broadcast from there, so no tile waits on a page-table load.
   const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
-  const int ps = f.page_size;
+  const int ps = f.page_size;                 // a power of two, multiple of kT
+  const int ps_shift = 31 - __builtin_clz(ps);
   const int nt = (t_end - t_begin + kT - 1) / kT;              // tiles in the split
   const int my_tiles = nt > wave ? (nt - wave + kWaves - 1) / kWaves : 0;
   const int tl = lane & 15, gq = lane >> 4;
@@ -190,17 +188,20 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
   int pid = 0;
   auto load_pids = [&](int k0) {
     const int k = k0 + lane;
-    if (k < my_tiles) pid = bt[(t_begin + kT * (wave + kWaves * k)) / ps];
+    if (k < my_tiles) pid = bt[(t_begin + kT * (wave + kWaves * k)) >> ps_shift];
   };
+  // Tile k starts at token t0 of page `pid` (uniform): its slots are one
+  // contiguous run of kT * slot_bytes; lane (tl, gq) reads token tl of it.
   auto tile_slot = [&](int k) -> const uint8_t* {
     const int t0 = t_begin + kT * (wave + kWaves * k);
-    const int tok = min(t0 + tl, t_end - 1);
-    const int page = __shfl(pid, k & 63, kWave);
-    return slot_ptr(f, a.cache, page, tok % ps, a.num_kv_heads, kvh);
+    const int page = __builtin_amdgcn_readfirstlane(__shfl(pid, k & 63, kWave));
+    const uint8_t* base = a.cache + ((((int64_t)page * a.num_kv_heads + kvh) << ps_shift) +
+                                     (t0 & (ps - 1))) * (int64_t)kSlot;
+    const int tlc = min(tl, t_end - 1 - t0);
+    return base + tlc * kSlot;
   };
   load_pids(0);
 
-  // Three tile buffers: while a tile is processed the next two are in flight.
   auto fetch = [&](Tile& x, int k) {
     if (k < my_tiles) {
       if (k > 0 && (k & 63) == 0) load_pids(k);
@@ -297,58 +298,59 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
     // (code - 8) * v_scale split exactly into an fp16 high part and the fp16
     // residual (a 4-bit integer times an 11-bit mantissa has <= 15 bits), so
     // P.V keeps ~22 bits of p and the exact dequantized values.
-    half2_t a01, a23;
+    half4_t A;
     {
-      const half2_t h01 = {(_Float16)p[0], (_Float16)p[1]};
-      const half2_t h23 = {(_Float16)p[2], (_Float16)p[3]};
-      const half2_t r01 = {(_Float16)((p[0] - (float)h01[0]) * 4096.0f),
-                           (_Float16)((p[1] - (float)h01[1]) * 4096.0f)};
-      const half2_t r23 = {(_Float16)((p[2] - (float)h23[0]) * 4096.0f),
-                           (_Float16)((p[3] - (float)h23[1]) * 4096.0f)};
-      a01 = n < 8 ? h01 : r01;
-      a23 = n < 8 ? h23 : r23;
+      const half4_t h = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      const half4_t r = {(_Float16)((p[0] - (float)h[0]) * 4096.0f),
+                         (_Float16)((p[1] - (float)h[1]) * 4096.0f),
+                         (_Float16)((p[2] - (float)h[2]) * 4096.0f),
+                         (_Float16)((p[3] - (float)h[3]) * 4096.0f)};
+      A = n < 8 ? h : r;
     }
-    const half4_t A = {a01[0], a01[1], a23[0], a23[1]};
     uint4 vs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) vs[i] = scl[wave][1][4 * g + i];
+    const half4_t c1032x4 = {(_Float16)-1032.0f, (_Float16)-1032.0f, (_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half4_t c16x4 = {(_Float16)0.0625f, (_Float16)0.0625f, (_Float16)0.0625f, (_Float16)0.0625f};
+    const half4_t c72x4 = {(_Float16)-72.0f, (_Float16)-72.0f, (_Float16)-72.0f, (_Float16)-72.0f};
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const uint4 W = *(const uint4*)&vt[wave][b][n >> 2][4 * g];
+      // Byte (n & 3) of the V word of tokens t0..t3 -> halves (t0, t1), (t2, t3).
       const uint32_t x01 = __builtin_amdgcn_perm(W.y, W.x, vsel);
       const uint32_t x23 = __builtin_amdgcn_perm(W.w, W.z, vsel);
-      const half2_t l01 = as_h2((x01 & m0f) | 0x64006400u) + c1032;
-      const half2_t l23 = as_h2((x23 & m0f) | 0x64006400u) + c1032;
-      const half2_t g01 = __builtin_elementwise_fma(as_h2((x01 & mf0) | 0x64006400u), c16, c72);
-      const half2_t g23 = __builtin_elementwise_fma(as_h2((x23 & mf0) | 0x64006400u), c16, c72);
-      // v_scale of block b for the token pairs (t0, t1) and (t2, t3).
+      const uint2 lw = {(x01 & m0f) | 0x64006400u, (x23 & m0f) | 0x64006400u};
+      const uint2 hw = {(x01 & mf0) | 0x64006400u, (x23 & mf0) | 0x64006400u};
+      const half4_t lo = __builtin_bit_cast(half4_t, lw) + c1032x4;
+      const half4_t hi = __builtin_elementwise_fma(__builtin_bit_cast(half4_t, hw), c16x4, c72x4);
+      // v_scale of block b for tokens t0..t3.
       constexpr uint32_t kSel[2] = {0x05040100u, 0x07060302u};
       const uint32_t w0 = (b >> 1) == 0 ? vs[0].x : (b >> 1) == 1 ? vs[0].y : (b >> 1) == 2 ? vs[0].z : vs[0].w;
       const uint32_t w1 = (b >> 1) == 0 ? vs[1].x : (b >> 1) == 1 ? vs[1].y : (b >> 1) == 2 ? vs[1].z : vs[1].w;
       const uint32_t w2 = (b >> 1) == 0 ? vs[2].x : (b >> 1) == 1 ? vs[2].y : (b >> 1) == 2 ? vs[2].z : vs[2].w;
       const uint32_t w3 = (b >> 1) == 0 ? vs[3].x : (b >> 1) == 1 ? vs[3].y : (b >> 1) == 2 ? vs[3].z : vs[3].w;
-      const half2_t d01 = as_h2(__builtin_amdgcn_perm(w1, w0, kSel[b & 1]));
-      const half2_t d23 = as_h2(__builtin_amdgcn_perm(w3, w2, kSel[b & 1]));
-      const half2_t l01h = l01 * d01, l23h = l23 * d23, g01h = g01 * d01, g23h = g23 * d23;
-      const half2_t l01l = __builtin_elementwise_fma(l01, d01, -l01h);
-      const half2_t l23l = __builtin_elementwise_fma(l23, d23, -l23h);
-      const half2_t g01l = __builtin_elementwise_fma(g01, d01, -g01h);
-      const half2_t g23l = __builtin_elementwise_fma(g23, d23, -g23h);
-      o[b][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, (half4_t){l01h[0], l01h[1], l23h[0], l23h[1]}, o[b][0], 0, 0, 0);
-      o[b][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, (half4_t){l01l[0], l01l[1], l23l[0], l23l[1]}, o[b][0], 0, 0, 0);
-      o[b][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, (half4_t){g01h[0], g01h[1], g23h[0], g23h[1]}, o[b][1], 0, 0, 0);
-      o[b][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, (half4_t){g01l[0], g01l[1], g23l[0], g23l[1]}, o[b][1], 0, 0, 0);
+      const half4_t dv = __builtin_bit_cast(half4_t, (uint2){__builtin_amdgcn_perm(w1, w0, kSel[b & 1]),
+                                                             __builtin_amdgcn_perm(w3, w2, kSel[b & 1])});
+      const half4_t loh = lo * dv, hih = hi * dv;
+      const half4_t lol = __builtin_elementwise_fma(lo, dv, -loh);
+      const half4_t hil = __builtin_elementwise_fma(hi, dv, -hih);
+      o[b][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, loh, o[b][0], 0, 0, 0);
+      o[b][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, lol, o[b][0], 0, 0, 0);
+      o[b][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, hih, o[b][1], 0, 0, 0);
+      o[b][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, hil, o[b][1], 0, 0, 0);
     }
     wave_sync_lds();
   };
-  Tile ta, tb, tc;
+  // Two tile buffers, unrolled by two: one tile is in flight while the other
+  // is processed, and no registers are copied between iterations.
+  Tile ta, tb;
   fetch(ta, 0);
-  fetch(tb, 1);
-  for (int k = 0; k < my_tiles; ++k) {
-    fetch(tc, k + 2);
+  for (int k = 0; k < my_tiles; k += 2) {
+    fetch(tb, k + 1);
     process(ta, k);
-    ta = tb;
-    tb = tc;
+    if (k + 1 >= my_tiles) break;
+    fetch(ta, k + 2);
+    process(tb, k + 1);
   }
 
   // Rows 8-15 of the P.V tiles hold the residual part (x 2^12): fold them in.
@@ -414,7 +416,8 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
 }  // namespace
 
 bool q4_mfma_supported(const DevFmt& f, int rows) {
-  return f.kind == HKV_KIND_Q4_0 && f.D == kD && rows <= kRows && f.page_size % kT == 0;
+  const bool pow2 = (f.page_size & (f.page_size - 1)) == 0;
+  return f.kind == HKV_KIND_Q4_0 && f.D == kD && rows <= kRows && f.page_size % kT == 0 && pow2;
 }
 
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
