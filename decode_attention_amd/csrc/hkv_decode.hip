@@ -21,6 +21,8 @@
 // softmax state is per row; P.V is computed lane-per-dimension.
 #include "hkv_decode_common.h"
 
+#include <algorithm>
+
 namespace hkv {
 namespace {
 
@@ -385,6 +387,8 @@ hipError_t launch_generic_e(const DevFmt& f, const DecArgs& a, int R, dim3 grid,
 bool q4_mfma_supported(const DevFmt& f, int rows);
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
 
+constexpr int64_t kTargetSplitsWgs = 512;
+
 bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_heads,
                  int max_klen, int queries_per_seq, DecodePlan* p) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return false;
@@ -396,7 +400,19 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   if (q.rows > 32) return false;
   q.num_groups = num_queries / queries_per_seq;
   q.kernel = q4_mfma_supported(f, q.rows) ? 1 : 0;
-  q.tokens_per_split = q.kernel == 1 ? 2048 : 1024;
+  // Split size: enough splits that (sequence group, KV head, split) fills the
+  // chip about two workgroups deep, in whole 64-token steps (every wave of a
+  // split then owns whole tiles), capped where the per-split fixed cost
+  // (query set-up, partial record) is well amortised.
+  {
+    const int64_t units = (int64_t)q.num_groups * num_kv_heads;
+    const int cap = q.kernel == 1 ? 2048 : 1024;
+    int64_t tps = units > 0 ? ((int64_t)max(max_klen, 1) * units + kTargetSplitsWgs - 1) /
+                                  kTargetSplitsWgs
+                            : cap;
+    tps = (tps + 63) / 64 * 64;
+    q.tokens_per_split = (int)std::min<int64_t>(cap, std::max<int64_t>(64, tps));
+  }
   q.num_splits = max_klen > 0 ? (max_klen + q.tokens_per_split - 1) / q.tokens_per_split : 1;
   q.partial_floats = kPartialHead + (size_t)f.D;
   const int R = q.kernel == 1 ? 8 : round_rows(q.rows);

@@ -137,10 +137,11 @@ def test_decode_matches_oracle(ci):
                                               ("octave_k3v3_compact", 256, 64, 32, 4),
                                               ("octave_k3v4", 192, 64, 4, 2)])
 def test_decode_edge_lengths(dtype, D, R, Hq, Hkv):
-    # klen 0, 1, one page, page +- 1, split boundaries +- 1 (1024 and 2048 tokens
-    # per split both occur) and a long ragged one; with two queries per sequence
-    # the second query sees one token less, so for the lengths 1025 and 2049 it
-    # has no token in the last split that the first query uses.
+    # klen 0, 1, one page, page +- 1, 1024 and 2048 +- 1 (split boundaries for
+    # the split sizes these shapes get: multiples of 64 that divide them) and a
+    # long ragged one; with two queries per sequence the second query sees one
+    # token less, so for the lengths 1025 and 2049 it has no token in the last
+    # split that the first query uses.
     lens = [1, 15, 16, 17, 1023, 1024, 1025, 2047, 2049, 2500, 3]
     rng = np.random.default_rng(D + Hq)
     P = 16
