@@ -208,3 +208,41 @@ def test_requantize_reproduces_bytes():
     a = _gpu_cache(f, w).cpu().numpy()
     b = _gpu_cache(f, w).cpu().numpy()
     assert np.array_equal(a, b)
+
+
+def _full_size_check(ci, seqs, n_slot_samples=4096):
+    """A workload at its full size, decoded in the launch configuration the
+    benchmark times; the oracle checks sampled slots bit for bit and every
+    output row of the sequences in `seqs` (it quantizes those sequences
+    itself: nothing it uses comes from the GPU)."""
+    cfg = W.CONFIGS[ci]
+    w = W.make_workload(cfg)
+    f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
+    fo = O.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim)
+    cache = _gpu_cache(f, w)
+    scale = W.default_sm_scale(cfg.head_size)
+    got = _decode(f, w, cache, scale).cpu().numpy()
+    P = cfg.page_size
+    # sampled slots, bit-exact
+    rng = np.random.default_rng(7)
+    rows = rng.choice(w.key.shape[0], size=min(n_slot_samples, w.key.shape[0]), replace=False)
+    slots = O.quantize(fo, w.key[rows].astype(np.float32), w.value[rows].astype(np.float32))
+    sm = w.slot_mapping[rows]
+    gpu_slots = cache[torch.from_numpy(sm // P).to(DEV), :, torch.from_numpy(sm % P).to(DEV)]
+    assert np.array_equal(gpu_slots.cpu().numpy(), slots)
+    # the decode rows of the chosen sequences against the oracle's own cache
+    sub = W.subset(w, seqs)
+    ref_cache = np.zeros(tuple(cache.shape), np.uint8)
+    for b in range(len(seqs)):
+        r0, r1 = sub.seq_start[b], sub.seq_start[b + 1]
+        sl = O.quantize(fo, sub.key[r0:r1].astype(np.float32), sub.value[r0:r1].astype(np.float32))
+        sm_b = sub.slot_mapping[r0:r1]
+        ref_cache[sm_b // P, :, sm_b % P] = sl
+    ref = O.attention(fo, sub.query.astype(np.float32), ref_cache, sub.block_table, sub.q_to_req,
+                      sub.q_to_klen, scale)
+    qsel = np.concatenate([np.nonzero(w.q_to_req == b)[0] for b in seqs])
+    _assert_close(got[qsel], ref, f"config {ci} full size, sequences {seqs}")
+
+
+def test_decode_full_size_q4_0_128k():
+    _full_size_check(3, [0, 3])
