@@ -401,15 +401,15 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   q.num_groups = num_queries / queries_per_seq;
   q.kernel = q4_mfma_supported(f, q.rows) ? 1 : 0;
   // Split size: enough splits that (sequence group, KV head, split) fills the
-  // chip about two workgroups deep, in whole 64-token steps (every wave of a
-  // split then owns whole tiles), capped where the per-split fixed cost
-  // (query set-up, partial record) is well amortised.
+  // chip with one resident round of workgroups (the MFMA kernel: one
+  // 8-wave workgroup per CU; the generic kernel: two 4-wave ones), in whole
+  // 64-token steps, capped where the per-split fixed cost (query set-up,
+  // partial record) is well amortised.
   {
     const int64_t units = (int64_t)q.num_groups * num_kv_heads;
-    const int cap = q.kernel == 1 ? 2048 : 1024;
-    int64_t tps = units > 0 ? ((int64_t)max(max_klen, 1) * units + kTargetSplitsWgs - 1) /
-                                  kTargetSplitsWgs
-                            : cap;
+    const int cap = q.kernel == 1 ? 4096 : 1024;
+    const int64_t target = q.kernel == 1 ? kTargetSplitsWgs / 2 : kTargetSplitsWgs;
+    int64_t tps = units > 0 ? ((int64_t)max(max_klen, 1) * units + target - 1) / target : cap;
     tps = (tps + 63) / 64 * 64;
     q.tokens_per_split = (int)std::min<int64_t>(cap, std::max<int64_t>(64, tps));
   }

@@ -51,10 +51,23 @@ constexpr float kQMax = 32639.0f;
 constexpr int kKStride = 4 * kNB + 4;  // dwords per token of the K tile ([word][block] + pad)
 constexpr int kVStride = kT + 4;       // padded token stride of the transposed V tile
 constexpr float kLazy = 8.0f;          // log2 headroom before the running max is raised
-constexpr int kMaxWaveTiles = kWave;   // page ids of a wave's tiles are held one per lane
+constexpr int kQWaves = 8;             // waves per workgroup (two per SIMD)
+constexpr int kMaxSplitTiles = 256;    // page ids of a split's tiles held in LDS
 
 __device__ __forceinline__ float ror8(float v) {  // lane l <- lane (l ^ 8) within 16
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+
+// Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 with the lane-swap
+// instructions (no LDS round trip): swapping a copy of v with itself leaves
+// the partner's value in one of the two results.
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float f16lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
@@ -86,14 +99,17 @@ __device__ __forceinline__ uint4 lds_u4(const uint32_t* p) {
 struct __align__(16) Q4Lds {
   int8_t qB[kNB][16][32];  // B operand bytes: [block][column][dim]
   float qsc[kRows];        // per-row score scale
-  float mlw[kWaves][kRows][2];
+  float mlw[kQWaves][kRows][2];
+  int pid[kMaxSplitTiles];  // page of each tile of the split
+  int next_unit;            // work queue: the next unit no wave has taken
+  int pad_[3];
   union {
     struct {
-      uint32_t kt[kWaves][2][kT][kKStride];           // [tile of unit][token][word * 8 + block]
-      uint32_t vt[kWaves][2][2][kNB][4][kVStride];    // [buf][tile][block][word][token]
-      uint32_t st[kWaves][2][2][2][4][kT];            // [buf][tile][K|V][scale word][token]
+      uint32_t kt[kQWaves][2][kT][kKStride];           // [tile of unit][token][word * 8 + block]
+      uint32_t vt[kQWaves][2][2][kNB][4][kVStride];    // [buf][tile][block][word][token]
+      uint32_t st[kQWaves][2][2][2][4][kT];            // [buf][tile][K|V][scale word][token]
     } s;
-    float ob[kRows][kD];  // wave merge, after the stream
+    float ob[kQWaves][kRows][kD];  // wave merge, after the stream
   } u;
 };
 
@@ -102,7 +118,7 @@ static_assert(sizeof(Q4Lds::u.s.st[0][0][0]) == 2 * 4 * kT * sizeof(uint32_t),
 static_assert(sizeof(Q4Lds::u.s.vt[0][0][0]) == kNB * 4 * kVStride * sizeof(uint32_t),
               "V tile stride");
 
-__global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArgs a) {
+__global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevFmt f, DecArgs a) {
   __shared__ Q4Lds L;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -124,8 +140,47 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
     return;
   }
 
-  // ---- query rows -> rotated, scaled int8 planes (B operand) --------------
-  for (int r = wave; r < kRows; r += kWaves) {
+  // ---- page ids, first tiles, query planes ---------------------------------
+  // The split is a queue of units of two consecutive 16-token tiles.  Wave w
+  // starts with units w and w + 8 and then takes the next untaken unit, so
+  // the two waves sharing a SIMD finish together however the issue slots
+  // fall between them.
+  const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
+  const int ps = f.page_size;                 // a power of two, multiple of kT
+  const int ps_shift = 31 - __builtin_clz(ps);
+  const int nt = (t_end - t_begin + kT - 1) / kT;              // tiles in the split
+  const int nu = (nt + 1) >> 1;                                // units in the split
+  for (int t = threadIdx.x; t < nt; t += blockDim.x) L.pid[t] = bt[(t_begin + kT * t) >> ps_shift];
+  if (threadIdx.x == 0) L.next_unit = 2 * kQWaves;
+  const int tl = lane & 15, gq = lane >> 4;
+  const int scale_kind = (lane >> 4) & 1;
+  // Tile k of the split (clamped to the last tile: the scores of a tile past
+  // the end are masked, so reloading the last one keeps every load in
+  // bounds), from its page id.
+  auto fetch_pid = [&](Tile& x, int kc, int page) {
+    const int t0 = t_begin + kT * kc;
+    const uint8_t* base = a.cache + ((((int64_t)page * a.num_kv_heads + kvh) << ps_shift) +
+                                     (t0 & (ps - 1))) * (int64_t)kSlot;
+    const int tlc = min(tl, t_end - 1 - t0);
+    load_tile(x, base + tlc * kSlot, gq, scale_kind);
+  };
+  auto fetch = [&](Tile& x, int k) {
+    const int kc = min(k, nt - 1);
+    fetch_pid(x, kc, __builtin_amdgcn_readfirstlane(L.pid[kc]));
+  };
+  // The first unit's tiles are requested before the query work, with page
+  // ids read directly, so their latency overlaps it.
+  Tile ta, tb;
+  const bool has_work = wave < nu;
+  if (has_work) {
+    const int k0 = 2 * wave, k1 = min(2 * wave + 1, nt - 1);
+    fetch_pid(ta, k0, bt[(t_begin + kT * k0) >> ps_shift]);
+    fetch_pid(tb, k1, bt[(t_begin + kT * k1) >> ps_shift]);
+  }
+
+  // Query row `wave` -> rotated, scaled int8 planes (B operand).
+  {
+    const int r = wave;
     float x[4];
     if (r < a.rows) {
       const int j = r / a.group, g = r % a.group;
@@ -161,22 +216,24 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
     }
     if (lane == 0) L.qsc[r] = (qmax / kQMax) * a.q_scale * 0.0625f;
   }
-  __syncthreads();
-
   const int n = lane & 15;   // score column (row r = n & 7, plane = n >> 3)
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of a tile in the score layout
   const int row = n & 7;
-  const float qs = L.qsc[row];
   const int klen_row = row < a.rows ? a.q_to_klen[q0 + row / a.group] : 0;
+  int kmin = kmax;
+  for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
+  __syncthreads();
+
+  const float qs = L.qsc[row];
   const bool live_row = row < a.rows;  // lanes n and n + 8 carry the same row
+  const float alpha_a = live_row ? (n < 8 ? 1.0f : 4096.0f) : 0.0f;
+  const float beta_a = live_row ? (n < 8 ? 0.0f : -4096.0f) : 0.0f;
   const uint32_t vsel = (uint32_t)(n & 3) | (0x0Cu << 8) | ((uint32_t)(4 + (n & 3)) << 16) |
                         (0x0Cu << 24);
   // Nibble masks kept in VGPRs so that mask-and-bias fuses into v_and_or_b32.
   uint32_t m0f, mf0;
   asm volatile("v_mov_b32 %0, 0x0f0f0f0f" : "=v"(m0f));
   asm volatile("v_mov_b32 %0, 0xf0f0f0f0" : "=v"(mf0));
-  int kmin = kmax;
-  for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
   const int t_lim = min(t_end, kmin);  // tiles ending at or before this need no mask
 
   float4_t o[kNB][2];
@@ -184,30 +241,7 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
   for (int b = 0; b < kNB; ++b) o[b][0] = o[b][1] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // Tiles of this wave: tile k starts at token t_begin + 16 (wave + 4 k) and
-  // lies in one page.  Lane k holds the page id of tile k.
-  const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
-  const int ps = f.page_size;                 // a power of two, multiple of kT
-  const int ps_shift = 31 - __builtin_clz(ps);
-  const int nt = (t_end - t_begin + kT - 1) / kT;              // tiles in the split
-  const int my_tiles = nt > wave ? (nt - wave + kWaves - 1) / kWaves : 0;
-  const int tl = lane & 15, gq = lane >> 4;
-  const int scale_kind = (lane >> 4) & 1;
-  int pid = 0;
-  if (lane < my_tiles) pid = bt[(t_begin + kT * (wave + kWaves * lane)) >> ps_shift];
-
-  if (my_tiles > 0) {
-    // Tile k (clamped to the last tile: the scores of a tile past the end are
-    // masked, so reloading the last one keeps every load in bounds).
-    auto fetch = [&](Tile& x, int k) {
-      const int kc = min(k, my_tiles - 1);
-      const int t0 = t_begin + kT * (wave + kWaves * kc);
-      const int page = __builtin_amdgcn_readlane(pid, kc);
-      const uint8_t* base = a.cache + ((((int64_t)page * a.num_kv_heads + kvh) << ps_shift) +
-                                       (t0 & (ps - 1))) * (int64_t)kSlot;
-      const int tlc = min(tl, t_end - 1 - t0);
-      load_tile(x, base + tlc * kSlot, gq, scale_kind);
-    };
+  if (has_work) {
 
     // Scores of one tile (raw: before masking) from its registers, in two
     // halves (blocks 0-3, then 4-7); its V words and scales go to LDS buffer
@@ -297,18 +331,19 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
       stage_s_join(st, sc);
     };
 
-    // Softmax of a unit (tiles k0, k0 + 1): mask, running max, p, and the
-    // P.V A operand (k = 8 g + j: j < 4 tile k0 token 4g+j, else tile k0+1).
-    auto stage_m = [&](const float (&sa)[4], const float (&sb)[4], int k0, half8_t& A) {
+    // Softmax of unit u (tiles 2u, 2u + 1): mask, running max, p, and the
+    // P.V A operand (k = 8 g + j: j < 4 tile 2u token 4g+j, else tile 2u+1).
+    auto stage_m = [&](const float (&sa)[4], const float (&sb)[4], int u, half8_t& A) {
       float s[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[i] = sa[i];
         s[4 + i] = sb[i];
       }
-      const int t0a = t_begin + kT * (wave + kWaves * k0);
-      const int t0b = t0a + kT * kWaves;
+      const int t0a = t_begin + 2 * kT * u;
+      const int t0b = t0a + kT;
       if (!(t0b + kT <= t_lim)) {
+        asm volatile("" ::: "memory");  // keep this a branch: only edge units mask
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ta_ = t0a + 4 * g + i, tb_ = t0b + 4 * g + i;
@@ -321,8 +356,7 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
       // the rescale of the accumulators is rare.
       float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                        fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      mt = max_xor16_32(mt);
       if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
         const float m_new = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
@@ -341,14 +375,12 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
       }
       const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;  // rows with nothing valid yet
       // Rows 0-7 of A carry fp16(p), rows 8-15 fp16((p - fp16(p)) * 2^12):
-      // a lane-dependent multiply-add gives either from the same operations.
-      const float alpha_a = n < 8 ? 1.0f : 4096.0f;
-      const float beta_a = n < 8 ? 0.0f : -4096.0f;
+      // a lane-dependent multiply-add gives either from the same operations
+      // (and zero for the padding rows past the group).
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float p = exp2f(s[i] - m_ref);  // exp2(-inf) = 0
+        const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);  // exp2(-inf) = 0
         l_run += p;
-        p = live_row ? p : 0.0f;
         const _Float16 h = (_Float16)p;
         A[i] = (_Float16)fmaf((float)h, beta_a, p * alpha_a);
       }
@@ -408,110 +440,117 @@ __global__ __launch_bounds__(256, 2) void decode_q4_mfma_kernel(DevFmt f, DecArg
       }
     };
 
-    Tile ta, tb;
     float sa[4], sb[4];
-    fetch(ta, 0);
-    fetch(tb, 1);
+    int u_cur = wave, u_nxt = wave + kQWaves;
     stage_s(ta, 0, 0, sa);
-    fetch(ta, 2);
+    fetch(ta, 2 * u_nxt);
     stage_s(tb, 1, 0, sb);
-    fetch(tb, 3);
-    const int nu = (my_tiles + 1) >> 1;
+    fetch(tb, 2 * u_nxt + 1);
+    int buf = 0;
     half8_t A;
-    for (int u = 0; u + 1 < nu; ++u) {
-      stage_m(sa, sb, 2 * u, A);
-      // One basic block: P.V of unit u and the scores of unit u + 1 in eight
-      // groups; the matrix-core work issued at the end of a group runs while
-      // the next group's VALU work issues, and the groups bound how much the
-      // scheduler holds in registers at once.
-      const int pb = u & 1, sbuf = (u + 1) & 1;
+    while (u_nxt < nu) {
+      int u_nn = 0;
+      if (lane == 0) u_nn = atomicAdd(&L.next_unit, 1);
+      u_nn = __builtin_amdgcn_readfirstlane(u_nn);
+      stage_m(sa, sb, u_cur, A);
+      // One basic block: P.V of unit u_cur and the scores of unit u_nxt in
+      // eight groups; the matrix-core work issued at the end of a group runs
+      // while the next group's VALU work issues, and the groups bound how
+      // much the scheduler holds in registers at once.
+      const int sbuf = buf ^ 1;
       SState st;
-      stage_p(A, pb, 0, 1);
+      stage_p(A, buf, 0, 1);
       __builtin_amdgcn_sched_barrier(0);
       stage_s0(ta, 0, sbuf, st);
       stage_s_blocks(0, sbuf, 0, st);
       __builtin_amdgcn_sched_barrier(0);
-      stage_p(A, pb, 1, 1);
+      stage_p(A, buf, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
       stage_s_blocks(0, sbuf, 2, st);
       stage_s_join(st, sa);
-      fetch(ta, 2 * u + 4);
+      fetch(ta, 2 * u_nn);
       __builtin_amdgcn_sched_barrier(0);
-      stage_p(A, pb, 2, 1);
+      stage_p(A, buf, 2, 1);
       __builtin_amdgcn_sched_barrier(0);
       stage_s0(tb, 1, sbuf, st);
       stage_s_blocks(1, sbuf, 0, st);
       __builtin_amdgcn_sched_barrier(0);
-      stage_p(A, pb, 3, 1);
+      stage_p(A, buf, 3, 1);
       __builtin_amdgcn_sched_barrier(0);
       stage_s_blocks(1, sbuf, 2, st);
       stage_s_join(st, sb);
-      fetch(tb, 2 * u + 5);
+      fetch(tb, 2 * u_nn + 1);
       // Keep these loads here: moved into the next iteration's head they
       // collide with the accumulators' registers and force copies of them.
       __builtin_amdgcn_sched_barrier(0);
+      u_cur = u_nxt;
+      u_nxt = u_nn;
+      buf = sbuf;
     }
-    stage_m(sa, sb, 2 * (nu - 1), A);
-    stage_p(A, (nu - 1) & 1, 0, kNB / 2);
+    stage_m(sa, sb, u_cur, A);
+    stage_p(A, buf, 0, kNB / 2);
   }
 
-  // Rows 8-15 of the P.V tiles hold the residual part (x 2^12): fold them in.
+  // Rows 8-15 of the P.V tiles (lanes 32-63) hold the residual part (x 2^12):
+  // fold them into rows 0-7 (lanes 0-31), which are the only ones used below.
 #pragma unroll
   for (int b = 0; b < kNB; ++b)
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[b][m][i] = fmaf(__shfl_xor(o[b][m][i], 32, kWave), 1.0f / 4096.0f, o[b][m][i]);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = __float_as_uint(o[b][m][i]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        o[b][m][i] = fmaf(__uint_as_float(sw[1]), 1.0f / 4096.0f, o[b][m][i]);
+      }
 
-  // ---- merge the four waves ----------------------------------------------
+  // ---- merge the waves ----------------------------------------------------
   float lsum = l_run + __shfl_xor(l_run, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
   if (g == 0 && n < kRows) {
     L.mlw[wave][n][0] = m_run;
     L.mlw[wave][n][1] = lsum;
   }
-  __syncthreads();
-  // This lane's output rows are 4*g + i (rows >= 8 hold nothing).
-  float fw[4];
+  __syncthreads();  // every wave is past the stream: L.u may now hold ob
+  // This lane's output rows are 4*g + i (lanes 0-31: rows 0-7).
+  if (g < 2) {
+    float fw[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (4 * g + i) & 7;
-    float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
-    const float mw = L.mlw[wave][r][0];
-    fw[i] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-  }
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w && g < 2) {
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      float M = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < kNB; ++b)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int d = 32 * b + 8 * (n >> 2) + (n & 3) + 4 * m;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* dst = &L.u.ob[4 * g + i][d];
-            const float v = o[b][m][i] * fw[i];
-            *dst = (w == 0) ? v : (*dst + v);
-          }
-        }
+      for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
+      const float mw = L.mlw[wave][r][0];
+      fw[i] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
     }
-    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < kNB; ++b)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int d = 32 * b + 8 * (n >> 2) + (n & 3) + 4 * m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = o[b][m][i] * fw[i];
+      }
   }
-  for (int r = wave; r < a.rows; r += kWaves) {
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.rows * kD; idx += blockDim.x) {
+    const int r = idx / kD, d = idx % kD;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kQWaves; ++w) acc += L.u.ob[w][r][d];
+    part[r * a.pstride + kPartialHead + d] = acc;
+  }
+  if (threadIdx.x < a.rows) {
+    const int r = threadIdx.x;
     float M = -INFINITY, L_ = 0.0f;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
+    for (int w = 0; w < kQWaves; ++w) {
       const float mw = L.mlw[w][r][0];
       if (mw != -INFINITY) L_ += L.mlw[w][r][1] * exp2f(mw - M);
     }
-    float* pr = part + r * a.pstride;
-    if (lane == 0) {
-      pr[0] = M;
-      pr[1] = L_;
-    }
-    for (int d = lane; d < kD; d += kWave) pr[kPartialHead + d] = L.u.ob[r][d];
+    part[r * a.pstride + 0] = M;
+    part[r * a.pstride + 1] = L_;
   }
 }
 
@@ -523,10 +562,9 @@ bool q4_mfma_supported(const DevFmt& f, int rows) {
 }
 
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
-  // Each lane holds the page id of one of its wave's tiles.
-  if ((a.tokens_per_split + kT * kWaves - 1) / (kT * kWaves) > kMaxWaveTiles)
-    return hipErrorInvalidValue;
-  decode_q4_mfma_kernel<<<grid, dim3(kWaves * kWave), 0, s>>>(f, a);
+  // The page ids of a split's tiles are held in LDS.
+  if ((a.tokens_per_split + kT - 1) / kT > kMaxSplitTiles) return hipErrorInvalidValue;
+  decode_q4_mfma_kernel<<<grid, dim3(kQWaves * kWave), 0, s>>>(f, a);
   return hipGetLastError();
 }
 
