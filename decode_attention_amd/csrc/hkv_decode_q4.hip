@@ -108,6 +108,7 @@ struct __align__(16) Q4Lds {
       uint32_t kt[kQWaves][2][kT][kKStride];           // [tile of unit][token][word * 8 + block]
       uint32_t vt[kQWaves][2][2][kNB][4][kVStride];    // [buf][tile][block][word][token]
       uint32_t st[kQWaves][2][2][2][4][kT];            // [buf][tile][K|V][scale word][token]
+      uint32_t st_dup[kQWaves][4][2 * kT];             // stores of lanes 32-63 (never read)
     } s;
     float ob[kQWaves][kRows][kD];  // wave merge, after the stream
   } u;
@@ -125,6 +126,24 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
   const int lane = threadIdx.x & 63;
   const int split = blockIdx.x, kvh = blockIdx.y, gi = blockIdx.z;
   const int q0 = gi * a.n_q;
+  // Query row `wave`: its loads go out first, independent of the page table.
+  float qx[4];
+  {
+    const int r = wave;
+    if (r < a.rows) {
+      const int j = r / a.group, g = r % a.group;
+      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = kWave * e + lane;
+        qx[e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
+                        : ((const float*)a.query)[qrow * kD + d];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qx[e] = 0.0f;
+    }
+  }
   const int req = a.q_to_req[q0];
   int kmax = 0;
   for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
@@ -182,21 +201,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
   {
     const int r = wave;
     float x[4];
-    if (r < a.rows) {
-      const int j = r / a.group, g = r % a.group;
-      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = kWave * e + lane;
-        x[e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
-                       : ((const float*)a.query)[qrow * kD + d];
-        if (f.use_signs) x[e] = apply_sign(f, x[e], d);
-      }
-      fwht_strided<4>(x, f.k_block, f.k_norm);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = 0.0f;
-    }
+    for (int e = 0; e < 4; ++e) x[e] = f.use_signs ? apply_sign(f, qx[e], kWave * e + lane) : qx[e];
+    if (r < a.rows) fwht_strided<4>(x, f.k_block, f.k_norm);
     float qmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
@@ -225,6 +232,12 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
   __syncthreads();
 
   const float qs = L.qsc[row];
+  // The query's B operand of every block, held in registers for the whole stream.
+  long qreg[kNB];
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) qreg[b] = *(const long*)&L.qB[b][n][8 * g];
+  const float w_own = n < 8 ? 256.0f * qs : qs;
+  const float w_partner = n < 8 ? qs : 256.0f * qs;
   const bool live_row = row < a.rows;  // lanes n and n + 8 carry the same row
   const float alpha_a = live_row ? (n < 8 ? 1.0f : 4096.0f) : 0.0f;
   const float beta_a = live_row ? (n < 8 ? 0.0f : -4096.0f) : 0.0f;
@@ -269,12 +282,14 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
       vw[((4 + gq) * 4 + 1) * kVStride] = x.v1.y;
       vw[((4 + gq) * 4 + 2) * kVStride] = x.v1.z;
       vw[((4 + gq) * 4 + 3) * kVStride] = x.v1.w;
-      {  // lanes 32-63 store the same values as lanes 0-31
-        uint32_t* sw = &L.u.s.st[wave][buf][half][scale_kind][0][tl];
-        sw[0 * kT] = x.sc.x;
-        sw[1 * kT] = x.sc.y;
-        sw[2 * kT] = x.sc.z;
-        sw[3 * kT] = x.sc.w;
+      {  // lanes 32-63 hold copies of lanes 0-31's chunks: they store to a dummy row
+        uint32_t* sw = lane < 32 ? &L.u.s.st[wave][buf][half][scale_kind][0][tl]
+                                 : &L.u.s.st_dup[wave][0][lane - 32];
+        const int ss = lane < 32 ? kT : 2 * kT;
+        sw[0 * ss] = x.sc.x;
+        sw[1 * ss] = x.sc.y;
+        sw[2 * ss] = x.sc.z;
+        sw[3 * ss] = x.sc.w;
       }
       wave_sync_lds();
       // Word g of every block of token n: the A operand of 8 score MFMAs.
@@ -300,13 +315,12 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int b = 2 * bp + h;
-          // Flipping bit 3 of a code turns it into the 4-bit two's complement
-          // of (code - 8); placed in the high nibble of a byte it reads as the
-          // int8 16 * (code - 8).  Low nibbles are dims 0..3, high 4..7.
-          const uint32_t xw = st.kw[b] ^ 0x88888888u;
-          const int2_t A2 = {(int)((xw << 4) & mf0), (int)(xw & mf0)};
-          const int4_t C = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-              __builtin_bit_cast(long, A2), *(const long*)&L.qB[b][n][8 * g], zero4, 0, 0, 0);
+          // A code c in the high nibble of a byte with bit 7 flipped reads as
+          // the int8 16 (c - 8).  Low nibbles are dims 0..3, high 4..7.
+          const uint32_t w = st.kw[b];
+          const int2_t A2 = {(int)(((w << 4) & mf0) ^ 0x80808080u), (int)((w & mf0) ^ 0x80808080u)};
+          const int4_t C = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, A2),
+                                                                 qreg[b], zero4, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t w = word_of(kw4, i);
@@ -315,13 +329,11 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
         }
       }
     };
+    // Lane n < 8 holds the hi plane and lane n + 8 the lo plane of a row:
+    // both form qs (256 hi + lo) from their own value and the partner's.
     auto stage_s_join = [&](const SState& st, float (&sc)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pt = ror8(st.acc[i]);
-        const float hiv = n < 8 ? st.acc[i] : pt, lov = n < 8 ? pt : st.acc[i];
-        sc[i] = fmaf(hiv, 256.0f, lov) * qs;
-      }
+      for (int i = 0; i < 4; ++i) sc[i] = fmaf(st.acc[i], w_own, ror8(st.acc[i]) * w_partner);
     };
     auto stage_s = [&](const Tile& x, int half, int buf, float (&sc)[4]) {
       SState st;
