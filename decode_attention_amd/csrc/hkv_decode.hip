@@ -386,6 +386,12 @@ hipError_t launch_generic_e(const DevFmt& f, const DecArgs& a, int R, dim3 grid,
 
 bool q4_mfma_supported(const DevFmt& f, int rows);
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
+bool oct_k3v4_mfma_supported(const DevFmt& f, int rows);
+hipError_t launch_decode_oct_k3v4(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
+
+// Decode kernels: 0 the generic VALU kernel (every format), 1 the Q4_0 MFMA
+// kernel (head size 256), 2 the Octave k3v4 MFMA kernel (head size 128).
+constexpr int kKernelGeneric = 0, kKernelQ4 = 1, kKernelOctK3v4 = 2;
 
 constexpr int64_t kTargetSplitsWgs = 512;
 
@@ -399,7 +405,9 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   q.rows = q.group * q.n_q;
   if (q.rows > 32) return false;
   q.num_groups = num_queries / queries_per_seq;
-  q.kernel = q4_mfma_supported(f, q.rows) ? 1 : 0;
+  q.kernel = q4_mfma_supported(f, q.rows)         ? kKernelQ4
+             : oct_k3v4_mfma_supported(f, q.rows) ? kKernelOctK3v4
+                                                  : kKernelGeneric;
   // Split size: enough splits that (sequence group, KV head, split) fills the
   // chip with one resident round of workgroups (the MFMA kernel: one
   // 8-wave workgroup per CU; the generic kernel: two 4-wave ones), in whole
@@ -407,18 +415,19 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   // partial record) is well amortised.
   {
     const int64_t units = (int64_t)q.num_groups * num_kv_heads;
-    const int cap = q.kernel == 1 ? 4096 : 1024;
-    const int64_t target = q.kernel == 1 ? kTargetSplitsWgs / 2 : kTargetSplitsWgs;
+    const bool mfma = q.kernel != kKernelGeneric;
+    const int cap = mfma ? 4096 : 1024;
+    const int64_t target = mfma ? kTargetSplitsWgs / 2 : kTargetSplitsWgs;
     int64_t tps = units > 0 ? ((int64_t)max(max_klen, 1) * units + target - 1) / target : cap;
     tps = (tps + 63) / 64 * 64;
     q.tokens_per_split = (int)std::min<int64_t>(cap, std::max<int64_t>(64, tps));
   }
   q.num_splits = max_klen > 0 ? (max_klen + q.tokens_per_split - 1) / q.tokens_per_split : 1;
   q.partial_floats = kPartialHead + (size_t)f.D;
-  const int R = q.kernel == 1 ? 8 : round_rows(q.rows);
+  const int R = q.kernel != kKernelGeneric ? 8 : round_rows(q.rows);
   q.workspace_bytes = sizeof(float) * q.partial_floats * R * (size_t)q.num_splits *
                       (size_t)q.num_groups * (size_t)num_kv_heads;
-  if (q.kernel == 0 && generic_lds_bytes(f, R) > 160 * 1024) return false;
+  if (q.kernel == kKernelGeneric && generic_lds_bytes(f, R) > 160 * 1024) return false;
   *p = q;
   return true;
 }
@@ -437,7 +446,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   a.group = p.group;
   a.n_q = p.n_q;
   a.rows = p.rows;
-  a.rows_pad = p.kernel == 1 ? 8 : round_rows(p.rows);
+  a.rows_pad = p.kernel != kKernelGeneric ? 8 : round_rows(p.rows);
   a.num_queries = p.num_groups * p.n_q;
   a.cache = cache;
   a.block_table = block_table;
@@ -452,8 +461,10 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   const int R = round_rows(p.rows);
   const dim3 grid(p.num_splits, num_kv_heads, p.num_groups);
   hipError_t e;
-  if (p.kernel == 1) {
+  if (p.kernel == kKernelQ4) {
     e = launch_decode_q4_mfma(f, a, grid, s);
+  } else if (p.kernel == kKernelOctK3v4) {
+    e = launch_decode_oct_k3v4(f, a, grid, s);
   } else switch (f.D / kWave) {
     case 1: e = launch_generic_e<1>(f, a, R, grid, s); break;
     case 2: e = launch_generic_e<2>(f, a, R, grid, s); break;

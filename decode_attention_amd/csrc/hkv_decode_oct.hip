@@ -1,0 +1,494 @@
+// hkv_decode_oct.hip -- split-K paged decode attention over the Octave
+// k3v4 cache on the matrix cores (gfx950): head size 128 with 64 RoPE dims
+// (4-bit K codes), 64 NoPE dims (3-bit), 4-bit V, up to 8 query rows per KV
+// head.
+//
+// What is computed is reference_attention of the vLLM docs page
+// "vllm.v1.attention.ops.rocm_octave" in the rotated space the module text
+// describes: the query takes the K rotation (sign flips, 64-dim blocks),
+// codes are dequantized as LUT[c] * scale / 64 (reference_dequantize), and
+// the output is rotated back with the V transform and the signs.
+//
+// The stream and its driver follow the Q4_0 kernel (8-wave workgroups with a
+// queue of 32-token units in LDS; P.V of one unit and the scores of the next
+// in one branch-free block); the format-specific parts:
+//  * A tile (16 tokens x 128-byte slots) is loaded as two 16-byte chunks per
+//    lane and stored in LDS transposed, [slot word][token], so a K operand is
+//    two words of one token and a V operand is one word of four tokens.
+//  * Scores on v_mfma_i32_16x16x64_i8, one per 64-dim scale block: A = the
+//    int8 codebook values of the codes (looked up with v_perm_b32; 16-entry
+//    tables take two lookups and a per-byte select on the code's top bit),
+//    B = the rotated query as two int8 planes.  Each block's int32 result is
+//    scaled by the token's fp16 block scale.
+//  * P.V on v_mfma_f32_16x16x32_f16: B = the codebook value as an exact fp16
+//    (the biased byte LUT[c] + 128 under an 0x64 high byte is 1152 + LUT[c]),
+//    so no residual is needed on this side; the token's V scale multiplies p
+//    in the A operand (rows 0-7 fp16(p s), rows 8-15 the residual x 2^12).
+#include "hkv_decode_common.h"
+
+namespace hkv {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;            // head size handled here
+constexpr int kRope = 64;          // leading K dims with 4-bit codes
+constexpr int kSlot = 128;         // slot bytes of octave_k3v4 at head size 128
+constexpr int kSlotW = kSlot / 4;  // slot words
+constexpr int kWNope = 8;          // slot word of the NoPE low-bit plane (byte 32)
+constexpr int kWNopeHi = 12;       // NoPE high-bit plane (byte 48)
+constexpr int kWV = 14;            // V codes (byte 56)
+constexpr int kWScale = 30;        // K scales (RoPE | NoPE << 16); word 31: V scale
+constexpr int kVGroups = kD / 32;  // V word groups: 4 words = 32 dims each
+constexpr int kRows = 8;           // query rows per KV head
+constexpr int kT = 16;             // tokens per tile
+constexpr int kTS = kT + 4;        // token stride (words) of the transposed tile
+constexpr int kQMaxI = 32639;      // largest |q| code of the two-plane int8 split
+constexpr float kQMax = 32639.0f;
+constexpr float kLazy = 8.0f;      // log2 headroom before the running max is raised
+constexpr int kQWaves = 8;         // waves per workgroup (two per SIMD)
+constexpr int kMaxSplitTiles = 256;
+
+// Codebook bytes for v_perm_b32 lookups: entries 4i..4i+3 in word i.
+constexpr uint32_t lut_word(const int* lut, int i, int bias) {
+  return (uint32_t)((lut[4 * i] + bias) & 255) | ((uint32_t)((lut[4 * i + 1] + bias) & 255) << 8) |
+         ((uint32_t)((lut[4 * i + 2] + bias) & 255) << 16) |
+         ((uint32_t)((lut[4 * i + 3] + bias) & 255) << 24);
+}
+constexpr uint32_t kK4[4] = {lut_word(kLut4, 0, 0), lut_word(kLut4, 1, 0), lut_word(kLut4, 2, 0),
+                             lut_word(kLut4, 3, 0)};
+constexpr uint32_t kK3[2] = {lut_word(kLut3, 0, 0), lut_word(kLut3, 1, 0)};
+constexpr uint32_t kV4[4] = {lut_word(kLut4, 0, 128), lut_word(kLut4, 1, 128),
+                             lut_word(kLut4, 2, 128), lut_word(kLut4, 3, 128)};
+
+__device__ __forceinline__ float ror8(float v) {  // lane l <- lane (l ^ 8) within 16
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ uint4 lds_u4(const uint32_t* p) {
+  return *(const uint4*)__builtin_assume_aligned(p, 16);
+}
+
+// 0xFF in each byte whose bit 7 is set in y, else 0x00 (v_perm_b32
+// sign-replicating selectors 8-11 read bit 7 of bytes 1, 3 of the low and
+// high source words).
+__device__ __forceinline__ uint32_t byte_sign_mask(uint32_t y) {
+  return __builtin_amdgcn_perm(y << 8, y, 0x090B080Au);
+}
+
+// 16-entry byte lookup of four codes (one per byte, bits 0-2 in s7, the
+// select mask m from bit 3): entries 0-7 in (t0, t1), 8-15 in (t2, t3).
+__device__ __forceinline__ uint32_t lut16(uint32_t s7, uint32_t m, uint32_t t0, uint32_t t1,
+                                          uint32_t t2, uint32_t t3) {
+  const uint32_t lo = __builtin_amdgcn_perm(t1, t0, s7);
+  const uint32_t hi = __builtin_amdgcn_perm(t3, t2, s7);
+  return (hi & m) | (lo & ~m);
+}
+
+// int8 codebook values of the 8 codes in a 4-bit packed word (byte j holds
+// codes j (low nibble) and 4 + j (high nibble)): {codes 0-3, codes 4-7}.
+__device__ __forceinline__ void k4_word(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = lut16(w & 0x07070707u, byte_sign_mask(w << 4), kK4[0], kK4[1], kK4[2], kK4[3]);
+  hi = lut16((w >> 4) & 0x07070707u, byte_sign_mask(w), kK4[0], kK4[1], kK4[2], kK4[3]);
+}
+
+struct Tile {
+  uint4 c0, c1;  // chunks q and q + 4 (16 bytes each) of token tl
+};
+
+struct __align__(16) OctLds {
+  int8_t qB[kD / 64][16][64];  // B operand bytes: [64-dim block][column][dim]
+  float qsc[kRows];
+  float mlw[kQWaves][kRows][2];
+  int pid[kMaxSplitTiles];
+  int next_unit;
+  int pad_[3];
+  union {
+    uint32_t tt[kQWaves][2][2][kSlotW][kTS];  // [buf][tile][slot word][token]
+    float ob[kQWaves][kRows][kD];
+  } u;
+};
+
+__global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(DevFmt f, DecArgs a) {
+  __shared__ OctLds L;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int lane = threadIdx.x & 63;
+  const int split = blockIdx.x, kvh = blockIdx.y, gi = blockIdx.z;
+  const int q0 = gi * a.n_q;
+  // Query row `wave`: its loads go out first, independent of the page table.
+  float qx[2];
+  {
+    const int r = wave;
+    if (r < a.rows) {
+      const int j = r / a.group, g = r % a.group;
+      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int d = kWave * e + lane;
+        qx[e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
+                        : ((const float*)a.query)[qrow * kD + d];
+      }
+    } else {
+      qx[0] = qx[1] = 0.0f;
+    }
+  }
+  const int req = a.q_to_req[q0];
+  int kmax = 0;
+  for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
+  const int t_begin = split * a.tokens_per_split;
+  const int t_end = min(t_begin + a.tokens_per_split, kmax);
+  float* part = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits + split) * kRows *
+                           a.pstride;
+  if (t_begin >= t_end) {
+    for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
+      part[r * a.pstride + 0] = -INFINITY;
+      part[r * a.pstride + 1] = 0.0f;
+    }
+    return;
+  }
+
+  // ---- page ids, first tiles, query planes ---------------------------------
+  const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
+  const int ps = f.page_size;  // a power of two, multiple of kT
+  const int ps_shift = 31 - __builtin_clz(ps);
+  const int nt = (t_end - t_begin + kT - 1) / kT;
+  const int nu = (nt + 1) >> 1;
+  for (int t = threadIdx.x; t < nt; t += blockDim.x) L.pid[t] = bt[(t_begin + kT * t) >> ps_shift];
+  if (threadIdx.x == 0) L.next_unit = 2 * kQWaves;
+  const int tl = lane & 15, gq = lane >> 4;
+  auto fetch_pid = [&](Tile& x, int kc, int page) {
+    const int t0 = t_begin + kT * kc;
+    const uint8_t* base = a.cache + ((((int64_t)page * a.num_kv_heads + kvh) << ps_shift) +
+                                     (t0 & (ps - 1))) * (int64_t)kSlot;
+    const uint8_t* slot = base + min(tl, t_end - 1 - t0) * kSlot;
+    x.c0 = *(const uint4*)(slot + 16 * gq);
+    x.c1 = *(const uint4*)(slot + 16 * (4 + gq));
+  };
+  auto fetch = [&](Tile& x, int k) {
+    const int kc = min(k, nt - 1);
+    fetch_pid(x, kc, __builtin_amdgcn_readfirstlane(L.pid[kc]));
+  };
+  Tile ta, tb;
+  const bool has_work = wave < nu;
+  if (has_work) {
+    const int k0 = 2 * wave, k1 = min(2 * wave + 1, nt - 1);
+    fetch_pid(ta, k0, bt[(t_begin + kT * k0) >> ps_shift]);
+    fetch_pid(tb, k1, bt[(t_begin + kT * k1) >> ps_shift]);
+  }
+  {
+    const int r = wave;
+    float x[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) x[e] = f.use_signs ? apply_sign(f, qx[e], kWave * e + lane) : qx[e];
+    if (r < a.rows) fwht_strided<2>(x, f.k_block, f.k_norm);
+    float qmax = fmaxf(fabsf(x[0]), fabsf(x[1]));
+    qmax = wave_max(qmax);
+    const float inv = qmax > 0.0f ? kQMax / qmax : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      int qi = (int)rintf(x[e] * inv);
+      qi = min(kQMaxI, max(-kQMaxI, qi));
+      const int hi = (qi + 128) >> 8;
+      const int lo = qi - hi * 256;
+      const int d = kWave * e + lane;
+      L.qB[d >> 6][r][d & 63] = (int8_t)hi;
+      L.qB[d >> 6][8 + r][d & 63] = (int8_t)lo;
+    }
+    // 1/64: the codebook scale (LUT_ONE) of the K values.
+    if (lane == 0) L.qsc[r] = (qmax / kQMax) * a.q_scale * (1.0f / 64.0f);
+  }
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int row = n & 7;
+  const int klen_row = row < a.rows ? a.q_to_klen[q0 + row / a.group] : 0;
+  int kmin = kmax;
+  for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
+  __syncthreads();
+
+  const float qs = L.qsc[row];
+  const float w_own = n < 8 ? 256.0f * qs : qs;
+  const float w_partner = n < 8 ? qs : 256.0f * qs;
+  int4_t qreg[kD / 64];
+#pragma unroll
+  for (int c = 0; c < kD / 64; ++c) qreg[c] = *(const int4_t*)&L.qB[c][n][16 * g];
+  const bool live_row = row < a.rows;
+  const float alpha_a = live_row ? (n < 8 ? 1.0f : 4096.0f) : 0.0f;
+  const float beta_a = live_row ? (n < 8 ? 0.0f : -4096.0f) : 0.0f;
+  // Gathers byte (n & 3) of a word of tokens t0..t3 into bytes 0..3.
+  const int jb = n & 3;
+  const uint32_t gsel_lo = (uint32_t)jb | ((uint32_t)(jb + 4) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
+  const uint32_t gsel_hi = 0x0Cu | (0x0Cu << 8) | ((uint32_t)jb << 16) | ((uint32_t)(jb + 4) << 24);
+  const int t_lim = min(t_end, kmin);
+  // The bit of code 16 g + 4 i + j of the NoPE segment in the high plane
+  // word: 4 (g & 1) + i of byte j.
+  const int hsh = 4 * (g & 1);
+
+  float4_t o[kVGroups][2];
+#pragma unroll
+  for (int b = 0; b < kVGroups; ++b) o[b][0] = o[b][1] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  if (has_work) {
+    // Scores of one tile (before masking) from its registers; the tile goes
+    // to LDS buffer `buf` for the P.V of the unit.
+    auto stage_s = [&](const Tile& x, int half, int buf, float (&sc)[4]) {
+      uint32_t* tw = &L.u.tt[wave][buf][half][0][tl];
+      tw[(4 * gq + 0) * kTS] = x.c0.x;
+      tw[(4 * gq + 1) * kTS] = x.c0.y;
+      tw[(4 * gq + 2) * kTS] = x.c0.z;
+      tw[(4 * gq + 3) * kTS] = x.c0.w;
+      tw[(16 + 4 * gq + 0) * kTS] = x.c1.x;
+      tw[(16 + 4 * gq + 1) * kTS] = x.c1.y;
+      tw[(16 + 4 * gq + 2) * kTS] = x.c1.z;
+      tw[(16 + 4 * gq + 3) * kTS] = x.c1.w;
+      wave_sync_lds();
+      const uint32_t* tr = &L.u.tt[wave][buf][half][0][0];
+      // RoPE block: words 2g, 2g + 1 of token n (dims 16 g .. 16 g + 15).
+      const uint32_t r0 = tr[(2 * g) * kTS + n], r1 = tr[(2 * g + 1) * kTS + n];
+      int4_t A0;
+      {
+        uint32_t l0, h0, l1, h1;
+        k4_word(r0, l0, h0);
+        k4_word(r1, l1, h1);
+        A0 = (int4_t){(int)l0, (int)h0, (int)l1, (int)h1};
+      }
+      // NoPE block: low-bit plane word g, high-bit plane word g >> 1.
+      const uint32_t lw = tr[(kWNope + g) * kTS + n];
+      const uint32_t hw = tr[(kWNopeHi + (g >> 1)) * kTS + n] >> hsh;
+      int4_t A1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
+        A1[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
+      }
+      const int4_t zero4 = {0, 0, 0, 0};
+      const int4_t C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qreg[0], zero4, 0, 0, 0);
+      const int4_t C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qreg[1], zero4, 0, 0, 0);
+      // K scales (RoPE | NoPE << 16) of tokens 4g..4g+3.
+      const uint4 ks = lds_u4(&tr[kWScale * kTS + 4 * g]);
+      const uint32_t ksw[4] = {ks.x, ks.y, ks.z, ks.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float acc = fmaf((float)C0[i], h2f((uint16_t)(ksw[i] & 0xffffu)),
+                               (float)C1[i] * h2f((uint16_t)(ksw[i] >> 16)));
+        sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+      }
+    };
+
+    // Softmax of unit u (tiles 2u, 2u + 1) and the P.V A operand: p times
+    // the token's V scale (the 1/64 of the codebook is taken out of p and
+    // put back into l at the end).
+    auto stage_m = [&](const float (&sa)[4], const float (&sb)[4], int u, int buf, half8_t& A) {
+      float s[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = sa[i];
+        s[4 + i] = sb[i];
+      }
+      const int t0a = t_begin + 2 * kT * u;
+      const int t0b = t0a + kT;
+      if (!(t0b + kT <= t_lim)) {
+        asm volatile("" ::: "memory");  // keep this a branch: only edge units mask
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ta_ = t0a + 4 * g + i, tb_ = t0b + 4 * g + i;
+          s[i] = (ta_ < t_end && ta_ < klen_row) ? s[i] : -INFINITY;
+          s[4 + i] = (tb_ < t_end && tb_ < klen_row) ? s[4 + i] : -INFINITY;
+        }
+      }
+      float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      mt = max_xor16_32(mt);
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+        l_run *= alpha;
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (4 * g + i) & 7, kWave);
+#pragma unroll
+        for (int b = 0; b < kVGroups; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[b][0][i] *= al[i];
+            o[b][1][i] *= al[i];
+          }
+        m_run = m_new;
+      }
+      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+      const uint4 va = lds_u4(&L.u.tt[wave][buf][0][kWScale + 1][4 * g]);
+      const uint4 vb = lds_u4(&L.u.tt[wave][buf][1][kWScale + 1][4 * g]);
+      const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[i] - m_ref - 6.0f);  // p / 64
+        l_run += p;
+        const float pv = p * h2f((uint16_t)(vw[i] & 0xffffu));
+        const _Float16 h = (_Float16)pv;
+        A[i] = (_Float16)fmaf((float)h, beta_a, pv * alpha_a);
+      }
+    };
+
+    // P.V of a unit from LDS buffer `buf`, V word groups [w0, w0 + nw).
+    auto stage_p = [&](const half8_t& A, int buf, int w0, int nw) {
+      const half8_t c1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
+                             (_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
+                             (_Float16)-1152.0f, (_Float16)-1152.0f};
+      const uint32_t* va = &L.u.tt[wave][buf][0][0][4 * g];
+      const uint32_t* vb = &L.u.tt[wave][buf][1][0][4 * g];
+#pragma unroll
+      for (int W = w0; W < w0 + nw; ++W) {
+        const int wrd = kWV + 4 * W + (n >> 2);
+        const uint4 Wa = lds_u4(va + wrd * kTS), Wb = lds_u4(vb + wrd * kTS);
+        // Byte (n & 3) of the word of tokens 4g..4g+3 of each tile.
+        const uint32_t ga = __builtin_amdgcn_perm(Wa.y, Wa.x, gsel_lo) |
+                            __builtin_amdgcn_perm(Wa.w, Wa.z, gsel_hi);
+        const uint32_t gb = __builtin_amdgcn_perm(Wb.y, Wb.x, gsel_lo) |
+                            __builtin_amdgcn_perm(Wb.w, Wb.z, gsel_hi);
+        // Biased codebook bytes of the low (dim 8w + j) and high (8w + 4 + j) nibbles.
+        const uint32_t la = lut16(ga & 0x07070707u, byte_sign_mask(ga << 4), kV4[0], kV4[1], kV4[2], kV4[3]);
+        const uint32_t ha = lut16((ga >> 4) & 0x07070707u, byte_sign_mask(ga), kV4[0], kV4[1], kV4[2], kV4[3]);
+        const uint32_t lb = lut16(gb & 0x07070707u, byte_sign_mask(gb << 4), kV4[0], kV4[1], kV4[2], kV4[3]);
+        const uint32_t hb = lut16((gb >> 4) & 0x07070707u, byte_sign_mask(gb), kV4[0], kV4[1], kV4[2], kV4[3]);
+        // Under an 0x64 high byte a biased byte b reads as the fp16 1024 + b.
+        const uint4 lw = {__builtin_amdgcn_perm(0x64646464u, la, 0x04010400u),
+                          __builtin_amdgcn_perm(0x64646464u, la, 0x04030402u),
+                          __builtin_amdgcn_perm(0x64646464u, lb, 0x04010400u),
+                          __builtin_amdgcn_perm(0x64646464u, lb, 0x04030402u)};
+        const uint4 hw = {__builtin_amdgcn_perm(0x64646464u, ha, 0x04010400u),
+                          __builtin_amdgcn_perm(0x64646464u, ha, 0x04030402u),
+                          __builtin_amdgcn_perm(0x64646464u, hb, 0x04010400u),
+                          __builtin_amdgcn_perm(0x64646464u, hb, 0x04030402u)};
+        const half8_t lo = __builtin_bit_cast(half8_t, lw) + c1152;
+        const half8_t hi = __builtin_bit_cast(half8_t, hw) + c1152;
+        o[W][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, lo, o[W][0], 0, 0, 0);
+        o[W][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, hi, o[W][1], 0, 0, 0);
+      }
+    };
+
+    float sa[4], sb[4];
+    int u_cur = wave, u_nxt = wave + kQWaves;
+    stage_s(ta, 0, 0, sa);
+    fetch(ta, 2 * u_nxt);
+    stage_s(tb, 1, 0, sb);
+    fetch(tb, 2 * u_nxt + 1);
+    int buf = 0;
+    half8_t A;
+    while (u_nxt < nu) {
+      int u_nn = 0;
+      if (lane == 0) u_nn = atomicAdd(&L.next_unit, 1);
+      u_nn = __builtin_amdgcn_readfirstlane(u_nn);
+      stage_m(sa, sb, u_cur, buf, A);
+      // One basic block: P.V of unit u_cur and the scores of unit u_nxt.
+      const int sbuf = buf ^ 1;
+      stage_p(A, buf, 0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_s(ta, 0, sbuf, sa);
+      fetch(ta, 2 * u_nn);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_p(A, buf, 2, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_s(tb, 1, sbuf, sb);
+      fetch(tb, 2 * u_nn + 1);
+      // Keep these loads here (moved into the next iteration's head they
+      // would collide with the accumulators' registers).
+      __builtin_amdgcn_sched_barrier(0);
+      u_cur = u_nxt;
+      u_nxt = u_nn;
+      buf = sbuf;
+    }
+    stage_m(sa, sb, u_cur, buf, A);
+    stage_p(A, buf, 0, kVGroups);
+  }
+
+  // Rows 8-15 of the P.V tiles (lanes 32-63) hold the residual part (x 2^12):
+  // fold them into rows 0-7 (lanes 0-31).
+#pragma unroll
+  for (int b = 0; b < kVGroups; ++b)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = __float_as_uint(o[b][m][i]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        o[b][m][i] = fmaf(__uint_as_float(sw[1]), 1.0f / 4096.0f, o[b][m][i]);
+      }
+
+  // ---- merge the waves ----------------------------------------------------
+  float lsum = l_run + __shfl_xor(l_run, 16, kWave);
+  lsum += __shfl_xor(lsum, 32, kWave);
+  if (g == 0 && n < kRows) {
+    L.mlw[wave][n][0] = m_run;
+    L.mlw[wave][n][1] = lsum * 64.0f;  // p was kept as p / 64
+  }
+  __syncthreads();
+  if (g < 2) {
+    float fw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
+      const float mw = L.mlw[wave][r][0];
+      fw[i] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+    }
+#pragma unroll
+    for (int b = 0; b < kVGroups; ++b)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int d = 32 * b + 8 * (n >> 2) + (n & 3) + 4 * m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = o[b][m][i] * fw[i];
+      }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.rows * kD; idx += blockDim.x) {
+    const int r = idx / kD, d = idx % kD;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kQWaves; ++w) acc += L.u.ob[w][r][d];
+    part[r * a.pstride + kPartialHead + d] = acc;
+  }
+  if (threadIdx.x < a.rows) {
+    const int r = threadIdx.x;
+    float M = -INFINITY, L_ = 0.0f;
+    for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
+    for (int w = 0; w < kQWaves; ++w) {
+      const float mw = L.mlw[w][r][0];
+      if (mw != -INFINITY) L_ += L.mlw[w][r][1] * exp2f(mw - M);
+    }
+    part[r * a.pstride + 0] = M;
+    part[r * a.pstride + 1] = L_;
+  }
+}
+
+}  // namespace
+
+bool oct_k3v4_mfma_supported(const DevFmt& f, int rows) {
+  const bool pow2 = (f.page_size & (f.page_size - 1)) == 0;
+  return f.kind == HKV_KIND_OCTAVE && !f.compact && f.D == kD && f.k_wide == kRope &&
+         f.v_bits == 4 && f.slot_bytes == kSlot && f.off_k_nope == 4 * kWNope &&
+         f.off_v == 4 * kWV && f.off_scales == 4 * kWScale && f.num_k_scales == 2 &&
+         f.k_block == 64 && rows <= kRows && f.page_size % kT == 0 && pow2;
+}
+
+hipError_t launch_decode_oct_k3v4(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
+  if ((a.tokens_per_split + kT - 1) / kT > kMaxSplitTiles) return hipErrorInvalidValue;
+  decode_oct_k3v4_kernel<<<grid, dim3(kQWaves * kWave), 0, s>>>(f, a);
+  return hipGetLastError();
+}
+
+}  // namespace hkv
