@@ -386,11 +386,12 @@ hipError_t launch_generic_e(const DevFmt& f, const DecArgs& a, int R, dim3 grid,
 
 bool q4_mfma_supported(const DevFmt& f, int rows);
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
-bool oct_k3v4_mfma_supported(const DevFmt& f, int rows);
-hipError_t launch_decode_oct_k3v4(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
+bool oct_mfma_supported(const DevFmt& f, int rows);
+hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
 
 // Decode kernels: 0 the generic VALU kernel (every format), 1 the Q4_0 MFMA
-// kernel (head size 256), 2 the Octave k3v4 MFMA kernel (head size 128).
+// kernel (head size 256), 2 the Octave MFMA kernel (k3v4 at head size 128,
+// k3v3 compact at 256).
 constexpr int kKernelGeneric = 0, kKernelQ4 = 1, kKernelOctK3v4 = 2;
 
 constexpr int64_t kTargetSplitsWgs = 512;
@@ -405,9 +406,21 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   q.rows = q.group * q.n_q;
   if (q.rows > 32) return false;
   q.num_groups = num_queries / queries_per_seq;
-  q.kernel = q4_mfma_supported(f, q.rows)         ? kKernelQ4
-             : oct_k3v4_mfma_supported(f, q.rows) ? kKernelOctK3v4
-                                                  : kKernelGeneric;
+  auto mfma_kernel = [&](int rows) {
+    return q4_mfma_supported(f, rows)    ? kKernelQ4
+           : oct_mfma_supported(f, rows) ? kKernelOctK3v4
+                                         : kKernelGeneric;
+  };
+  q.kernel = mfma_kernel(q.rows);
+  // More rows than the matrix-core kernels take (they hold 8 query rows per
+  // KV head): when one query token's heads fit, every query becomes its own
+  // group (each streams the sequence's K/V through its own workgroups).
+  if (q.kernel == kKernelGeneric && q.n_q > 1 && mfma_kernel(q.group) != kKernelGeneric) {
+    q.n_q = 1;
+    q.rows = q.group;
+    q.num_groups = num_queries;
+    q.kernel = mfma_kernel(q.rows);
+  }
   // Split size: enough splits that (sequence group, KV head, split) fills the
   // chip with one resident round of workgroups (the MFMA kernel: one
   // 8-wave workgroup per CU; the generic kernel: two 4-wave ones), in whole
@@ -464,7 +477,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   if (p.kernel == kKernelQ4) {
     e = launch_decode_q4_mfma(f, a, grid, s);
   } else if (p.kernel == kKernelOctK3v4) {
-    e = launch_decode_oct_k3v4(f, a, grid, s);
+    e = launch_decode_oct(f, a, grid, s);
   } else switch (f.D / kWave) {
     case 1: e = launch_generic_e<1>(f, a, R, grid, s); break;
     case 2: e = launch_generic_e<2>(f, a, R, grid, s); break;

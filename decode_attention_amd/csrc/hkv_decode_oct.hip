@@ -1,7 +1,9 @@
-// hkv_decode_oct.hip -- split-K paged decode attention over the Octave
-// k3v4 cache on the matrix cores (gfx950): head size 128 with 64 RoPE dims
-// (4-bit K codes), 64 NoPE dims (3-bit), 4-bit V, up to 8 query rows per KV
-// head.
+// hkv_decode_oct.hip -- split-K paged decode attention over Octave caches on
+// the matrix cores (gfx950), up to 8 query rows per KV head, for two layouts:
+//  * k3v4 at head size 128 with 64 RoPE dims: 4-bit K codes for the RoPE
+//    block, 3-bit for the NoPE block (one scale each), 4-bit V (128-byte slots);
+//  * k3v3 compact at head size 256: 3-bit K and V, one scale each (196-byte
+//    slots).
 //
 // What is computed is reference_attention of the vLLM docs page
 // "vllm.v1.attention.ops.rocm_octave" in the rotated space the module text
@@ -12,9 +14,9 @@
 // The stream and its driver follow the Q4_0 kernel (8-wave workgroups with a
 // queue of 32-token units in LDS; P.V of one unit and the scores of the next
 // in one branch-free block); the format-specific parts:
-//  * A tile (16 tokens x 128-byte slots) is loaded as two 16-byte chunks per
-//    lane and stored in LDS transposed, [slot word][token], so a K operand is
-//    two words of one token and a V operand is one word of four tokens.
+//  * A tile (16 slots) is loaded in 16-byte chunks of one token each and
+//    stored in LDS transposed, [slot word][token], so a K operand is words of
+//    one token and a V operand is one word of four tokens.
 //  * Scores on v_mfma_i32_16x16x64_i8, one per 64-dim scale block: A = the
 //    int8 codebook values of the codes (looked up with v_perm_b32; 16-entry
 //    tables take two lookups and a per-byte select on the code's top bit),
@@ -33,15 +35,29 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;            // head size handled here
-constexpr int kRope = 64;          // leading K dims with 4-bit codes
-constexpr int kSlot = 128;         // slot bytes of octave_k3v4 at head size 128
-constexpr int kSlotW = kSlot / 4;  // slot words
-constexpr int kWNope = 8;          // slot word of the NoPE low-bit plane (byte 32)
-constexpr int kWNopeHi = 12;       // NoPE high-bit plane (byte 48)
-constexpr int kWV = 14;            // V codes (byte 56)
-constexpr int kWScale = 30;        // K scales (RoPE | NoPE << 16); word 31: V scale
-constexpr int kVGroups = kD / 32;  // V word groups: 4 words = 32 dims each
+// Slot layouts (slot words; vLLM docs, module text and OctaveFormat).
+struct FmtK3V4 {            // octave_k3v4, head size 128, rope 64
+  static constexpr bool kCompact = false;
+  static constexpr int kD = 128;
+  static constexpr int kSlot = 128;
+  static constexpr int kWNope = 8;    // NoPE low-bit plane (byte 32)
+  static constexpr int kWNopeHi = 12; // NoPE high-bit plane (byte 48)
+  static constexpr int kWV = 14;      // V codes (byte 56)
+  static constexpr int kWScale = 30;  // K scales (RoPE | NoPE << 16); word 31: V scale
+  static constexpr int kChunks = 2;   // 16-byte chunks per lane and tile
+  static constexpr int kAcc = kD / 32 * 2;  // P.V accumulator tiles
+};
+struct FmtK3V3C {           // octave_k3v3_compact, head size 256
+  static constexpr bool kCompact = true;
+  static constexpr int kD = 256;
+  static constexpr int kSlot = 196;
+  static constexpr int kWKHi = 16;    // K high-bit plane (byte 64)
+  static constexpr int kWV = 24;      // V low-bit plane (byte 96)
+  static constexpr int kWVHi = 40;    // V high-bit plane (byte 160)
+  static constexpr int kWScale = 48;  // K scale | V scale << 16
+  static constexpr int kChunks = 3;   // 12 chunks of 16 bytes per slot: 3 per lane
+  static constexpr int kAcc = kD / 16;
+};
 constexpr int kRows = 8;           // query rows per KV head
 constexpr int kT = 16;             // tokens per tile
 constexpr int kTS = kT + 4;        // token stride (words) of the transposed tile
@@ -62,6 +78,7 @@ constexpr uint32_t kK4[4] = {lut_word(kLut4, 0, 0), lut_word(kLut4, 1, 0), lut_w
 constexpr uint32_t kK3[2] = {lut_word(kLut3, 0, 0), lut_word(kLut3, 1, 0)};
 constexpr uint32_t kV4[4] = {lut_word(kLut4, 0, 128), lut_word(kLut4, 1, 128),
                              lut_word(kLut4, 2, 128), lut_word(kLut4, 3, 128)};
+constexpr uint32_t kV3[2] = {lut_word(kLut3, 0, 128), lut_word(kLut3, 1, 128)};
 
 __device__ __forceinline__ float ror8(float v) {  // lane l <- lane (l ^ 8) within 16
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
@@ -103,11 +120,17 @@ __device__ __forceinline__ void k4_word(uint32_t w, uint32_t& lo, uint32_t& hi) 
   hi = lut16((w >> 4) & 0x07070707u, byte_sign_mask(w), kK4[0], kK4[1], kK4[2], kK4[3]);
 }
 
+// Chunks q, q + 4, q + 8 (16 bytes each) of token tl (k3v4: the first two),
+// and for the compact layout the 4-byte scale word.
 struct Tile {
-  uint4 c0, c1;  // chunks q and q + 4 (16 bytes each) of token tl
+  uint4 c[3];
+  uint32_t sw;
 };
 
+template <class F>
 struct __align__(16) OctLds {
+  static constexpr int kD = F::kD;
+  static constexpr int kSlotW = (F::kSlot + 3) / 4;
   int8_t qB[kD / 64][16][64];  // B operand bytes: [64-dim block][column][dim]
   float qsc[kRows];
   float mlw[kQWaves][kRows][2];
@@ -120,28 +143,34 @@ struct __align__(16) OctLds {
   } u;
 };
 
-__global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(DevFmt f, DecArgs a) {
-  __shared__ OctLds L;
+template <class F>
+__global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f, DecArgs a) {
+  constexpr int kD = F::kD;
+  constexpr int kSlot = F::kSlot;
+  constexpr int kE = kD / kWave;  // query values per lane
+  constexpr int kAcc = F::kAcc;
+  __shared__ OctLds<F> L;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
   const int split = blockIdx.x, kvh = blockIdx.y, gi = blockIdx.z;
   const int q0 = gi * a.n_q;
   // Query row `wave`: its loads go out first, independent of the page table.
-  float qx[2];
+  float qx[kE];
   {
     const int r = wave;
     if (r < a.rows) {
       const int j = r / a.group, g = r % a.group;
       const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
+      for (int e = 0; e < kE; ++e) {
         const int d = kWave * e + lane;
         qx[e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
                         : ((const float*)a.query)[qrow * kD + d];
       }
     } else {
-      qx[0] = qx[1] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) qx[e] = 0.0f;
     }
   }
   const int req = a.q_to_req[q0];
@@ -173,8 +202,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
     const uint8_t* base = a.cache + ((((int64_t)page * a.num_kv_heads + kvh) << ps_shift) +
                                      (t0 & (ps - 1))) * (int64_t)kSlot;
     const uint8_t* slot = base + min(tl, t_end - 1 - t0) * kSlot;
-    x.c0 = *(const uint4*)(slot + 16 * gq);
-    x.c1 = *(const uint4*)(slot + 16 * (4 + gq));
+#pragma unroll
+    for (int i = 0; i < F::kChunks; ++i) x.c[i] = *(const uint4*)(slot + 16 * (4 * i + gq));
+    if constexpr (F::kCompact) x.sw = *(const uint32_t*)(slot + 4 * F::kWScale);
   };
   auto fetch = [&](Tile& x, int k) {
     const int kc = min(k, nt - 1);
@@ -189,15 +219,17 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
   }
   {
     const int r = wave;
-    float x[2];
+    float x[kE];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) x[e] = f.use_signs ? apply_sign(f, qx[e], kWave * e + lane) : qx[e];
-    if (r < a.rows) fwht_strided<2>(x, f.k_block, f.k_norm);
-    float qmax = fmaxf(fabsf(x[0]), fabsf(x[1]));
+    for (int e = 0; e < kE; ++e) x[e] = f.use_signs ? apply_sign(f, qx[e], kWave * e + lane) : qx[e];
+    if (r < a.rows) fwht_strided<kE>(x, f.k_block, f.k_norm);
+    float qmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
     qmax = wave_max(qmax);
     const float inv = qmax > 0.0f ? kQMax / qmax : 0.0f;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < kE; ++e) {
       int qi = (int)rintf(x[e] * inv);
       qi = min(kQMaxI, max(-kQMaxI, qi));
       const int hi = (qi + 128) >> 8;
@@ -231,13 +263,16 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
   const uint32_t gsel_lo = (uint32_t)jb | ((uint32_t)(jb + 4) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
   const uint32_t gsel_hi = 0x0Cu | (0x0Cu << 8) | ((uint32_t)jb << 16) | ((uint32_t)(jb + 4) << 24);
   const int t_lim = min(t_end, kmin);
-  // The bit of code 16 g + 4 i + j of the NoPE segment in the high plane
-  // word: 4 (g & 1) + i of byte j.
+  // 3-bit segments: code 16 m + 4 i + j has its low bits at bits 2 i of byte
+  // j of low-plane word m and its high bit at bit 4 (m & 1) + i of byte j of
+  // high-plane word m >> 1 (vLLM docs, _pack).  For the K operand m = 4 c + g.
   const int hsh = 4 * (g & 1);
+  // For the V operand of the compact layout lane n takes dim 16 m + n: i = n >> 2.
+  const int vi = n >> 2;
 
-  float4_t o[kVGroups][2];
+  float4_t o[kAcc];
 #pragma unroll
-  for (int b = 0; b < kVGroups; ++b) o[b][0] = o[b][1] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b = 0; b < kAcc; ++b) o[b] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
   if (has_work) {
@@ -245,45 +280,67 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
     // to LDS buffer `buf` for the P.V of the unit.
     auto stage_s = [&](const Tile& x, int half, int buf, float (&sc)[4]) {
       uint32_t* tw = &L.u.tt[wave][buf][half][0][tl];
-      tw[(4 * gq + 0) * kTS] = x.c0.x;
-      tw[(4 * gq + 1) * kTS] = x.c0.y;
-      tw[(4 * gq + 2) * kTS] = x.c0.z;
-      tw[(4 * gq + 3) * kTS] = x.c0.w;
-      tw[(16 + 4 * gq + 0) * kTS] = x.c1.x;
-      tw[(16 + 4 * gq + 1) * kTS] = x.c1.y;
-      tw[(16 + 4 * gq + 2) * kTS] = x.c1.z;
-      tw[(16 + 4 * gq + 3) * kTS] = x.c1.w;
+#pragma unroll
+      for (int i = 0; i < F::kChunks; ++i) {
+        tw[(16 * i + 4 * gq + 0) * kTS] = x.c[i].x;
+        tw[(16 * i + 4 * gq + 1) * kTS] = x.c[i].y;
+        tw[(16 * i + 4 * gq + 2) * kTS] = x.c[i].z;
+        tw[(16 * i + 4 * gq + 3) * kTS] = x.c[i].w;
+      }
+      if constexpr (F::kCompact) tw[F::kWScale * kTS] = x.sw;  // lanes of one token store the same word
       wave_sync_lds();
       const uint32_t* tr = &L.u.tt[wave][buf][half][0][0];
-      // RoPE block: words 2g, 2g + 1 of token n (dims 16 g .. 16 g + 15).
-      const uint32_t r0 = tr[(2 * g) * kTS + n], r1 = tr[(2 * g + 1) * kTS + n];
-      int4_t A0;
-      {
-        uint32_t l0, h0, l1, h1;
-        k4_word(r0, l0, h0);
-        k4_word(r1, l1, h1);
-        A0 = (int4_t){(int)l0, (int)h0, (int)l1, (int)h1};
-      }
-      // NoPE block: low-bit plane word g, high-bit plane word g >> 1.
-      const uint32_t lw = tr[(kWNope + g) * kTS + n];
-      const uint32_t hw = tr[(kWNopeHi + (g >> 1)) * kTS + n] >> hsh;
-      int4_t A1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
-        A1[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
-      }
       const int4_t zero4 = {0, 0, 0, 0};
-      const int4_t C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qreg[0], zero4, 0, 0, 0);
-      const int4_t C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qreg[1], zero4, 0, 0, 0);
-      // K scales (RoPE | NoPE << 16) of tokens 4g..4g+3.
-      const uint4 ks = lds_u4(&tr[kWScale * kTS + 4 * g]);
+      // Scales of tokens 4g..4g+3.
+      const uint4 ks = lds_u4(&tr[F::kWScale * kTS + 4 * g]);
       const uint32_t ksw[4] = {ks.x, ks.y, ks.z, ks.w};
+      if constexpr (!F::kCompact) {
+        // RoPE block: words 2g, 2g + 1 of token n (dims 16 g .. 16 g + 15).
+        const uint32_t r0 = tr[(2 * g) * kTS + n], r1 = tr[(2 * g + 1) * kTS + n];
+        int4_t A0;
+        {
+          uint32_t l0, h0, l1, h1;
+          k4_word(r0, l0, h0);
+          k4_word(r1, l1, h1);
+          A0 = (int4_t){(int)l0, (int)h0, (int)l1, (int)h1};
+        }
+        // NoPE block: low-bit plane word g, high-bit plane word g >> 1.
+        const uint32_t lw = tr[(F::kWNope + g) * kTS + n];
+        const uint32_t hw = tr[(F::kWNopeHi + (g >> 1)) * kTS + n] >> hsh;
+        int4_t A1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float acc = fmaf((float)C0[i], h2f((uint16_t)(ksw[i] & 0xffffu)),
-                               (float)C1[i] * h2f((uint16_t)(ksw[i] >> 16)));
-        sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
+          A1[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
+        }
+        const int4_t C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qreg[0], zero4, 0, 0, 0);
+        const int4_t C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qreg[1], zero4, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float acc = fmaf((float)C0[i], h2f((uint16_t)(ksw[i] & 0xffffu)),
+                                 (float)C1[i] * h2f((uint16_t)(ksw[i] >> 16)));
+          sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+        }
+      } else {
+        // Four 64-dim blocks under one scale: the int32 results add up.
+        int4_t C = zero4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t lw = tr[(4 * c + g) * kTS + n];
+          const uint32_t hw = tr[(F::kWKHi + 2 * c + (g >> 1)) * kTS + n] >> hsh;
+          int4_t Ac;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
+            Ac[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
+          }
+          C = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac, qreg[c], C, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float acc = (float)C[i] * h2f((uint16_t)(ksw[i] & 0xffffu));
+          sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+        }
       }
     };
 
@@ -319,62 +376,83 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (4 * g + i) & 7, kWave);
 #pragma unroll
-        for (int b = 0; b < kVGroups; ++b)
+        for (int b = 0; b < kAcc; ++b)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            o[b][0][i] *= al[i];
-            o[b][1][i] *= al[i];
-          }
+          for (int i = 0; i < 4; ++i) o[b][i] *= al[i];
         m_run = m_new;
       }
       const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
-      const uint4 va = lds_u4(&L.u.tt[wave][buf][0][kWScale + 1][4 * g]);
-      const uint4 vb = lds_u4(&L.u.tt[wave][buf][1][kWScale + 1][4 * g]);
+      // V scale: low half of word 31 (k3v4), high half of the scale word (compact).
+      constexpr int kWVs = F::kCompact ? F::kWScale : F::kWScale + 1;
+      constexpr int kVsh = F::kCompact ? 16 : 0;
+      const uint4 va = lds_u4(&L.u.tt[wave][buf][0][kWVs][4 * g]);
+      const uint4 vb = lds_u4(&L.u.tt[wave][buf][1][kWVs][4 * g]);
       const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float p = __builtin_amdgcn_exp2f(s[i] - m_ref - 6.0f);  // p / 64
         l_run += p;
-        const float pv = p * h2f((uint16_t)(vw[i] & 0xffffu));
+        const float pv = p * h2f((uint16_t)((vw[i] >> kVsh) & 0xffffu));
         const _Float16 h = (_Float16)pv;
         A[i] = (_Float16)fmaf((float)h, beta_a, pv * alpha_a);
       }
     };
 
-    // P.V of a unit from LDS buffer `buf`, V word groups [w0, w0 + nw).
+    // P.V of a unit from LDS buffer `buf`, accumulator tiles [w0, w0 + nw)
+    // (k3v4: even and odd tiles are the low and high nibbles of V word group
+    // b >> 1; compact: tile m holds dims 16 m .. 16 m + 15).
     auto stage_p = [&](const half8_t& A, int buf, int w0, int nw) {
       const half8_t c1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
                              (_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
                              (_Float16)-1152.0f, (_Float16)-1152.0f};
       const uint32_t* va = &L.u.tt[wave][buf][0][0][4 * g];
       const uint32_t* vb = &L.u.tt[wave][buf][1][0][4 * g];
+      // Biased codebook bytes of four codes -> fp16 pairs (1024 + byte).
+      auto spread = [&](uint32_t x, uint32_t y) {
+        return (uint4){__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
+                       __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u),
+                       __builtin_amdgcn_perm(0x64646464u, y, 0x04010400u),
+                       __builtin_amdgcn_perm(0x64646464u, y, 0x04030402u)};
+      };
+      // Byte (n & 3) of a word of tokens 4g..4g+3.
+      auto gather = [&](const uint4& W) {
+        return __builtin_amdgcn_perm(W.y, W.x, gsel_lo) | __builtin_amdgcn_perm(W.w, W.z, gsel_hi);
+      };
+      if constexpr (!F::kCompact) {
 #pragma unroll
-      for (int W = w0; W < w0 + nw; ++W) {
-        const int wrd = kWV + 4 * W + (n >> 2);
-        const uint4 Wa = lds_u4(va + wrd * kTS), Wb = lds_u4(vb + wrd * kTS);
-        // Byte (n & 3) of the word of tokens 4g..4g+3 of each tile.
-        const uint32_t ga = __builtin_amdgcn_perm(Wa.y, Wa.x, gsel_lo) |
-                            __builtin_amdgcn_perm(Wa.w, Wa.z, gsel_hi);
-        const uint32_t gb = __builtin_amdgcn_perm(Wb.y, Wb.x, gsel_lo) |
-                            __builtin_amdgcn_perm(Wb.w, Wb.z, gsel_hi);
-        // Biased codebook bytes of the low (dim 8w + j) and high (8w + 4 + j) nibbles.
-        const uint32_t la = lut16(ga & 0x07070707u, byte_sign_mask(ga << 4), kV4[0], kV4[1], kV4[2], kV4[3]);
-        const uint32_t ha = lut16((ga >> 4) & 0x07070707u, byte_sign_mask(ga), kV4[0], kV4[1], kV4[2], kV4[3]);
-        const uint32_t lb = lut16(gb & 0x07070707u, byte_sign_mask(gb << 4), kV4[0], kV4[1], kV4[2], kV4[3]);
-        const uint32_t hb = lut16((gb >> 4) & 0x07070707u, byte_sign_mask(gb), kV4[0], kV4[1], kV4[2], kV4[3]);
-        // Under an 0x64 high byte a biased byte b reads as the fp16 1024 + b.
-        const uint4 lw = {__builtin_amdgcn_perm(0x64646464u, la, 0x04010400u),
-                          __builtin_amdgcn_perm(0x64646464u, la, 0x04030402u),
-                          __builtin_amdgcn_perm(0x64646464u, lb, 0x04010400u),
-                          __builtin_amdgcn_perm(0x64646464u, lb, 0x04030402u)};
-        const uint4 hw = {__builtin_amdgcn_perm(0x64646464u, ha, 0x04010400u),
-                          __builtin_amdgcn_perm(0x64646464u, ha, 0x04030402u),
-                          __builtin_amdgcn_perm(0x64646464u, hb, 0x04010400u),
-                          __builtin_amdgcn_perm(0x64646464u, hb, 0x04030402u)};
-        const half8_t lo = __builtin_bit_cast(half8_t, lw) + c1152;
-        const half8_t hi = __builtin_bit_cast(half8_t, hw) + c1152;
-        o[W][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, lo, o[W][0], 0, 0, 0);
-        o[W][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, hi, o[W][1], 0, 0, 0);
+        for (int W = w0 / 2; W < (w0 + nw) / 2; ++W) {
+          const int wrd = F::kWV + 4 * W + (n >> 2);
+          const uint32_t ga = gather(lds_u4(va + wrd * kTS)), gb = gather(lds_u4(vb + wrd * kTS));
+          // Biased codebook bytes of the low (dim 8w + j) and high (8w + 4 + j) nibbles.
+          const uint32_t la = lut16(ga & 0x07070707u, byte_sign_mask(ga << 4), kV4[0], kV4[1], kV4[2], kV4[3]);
+          const uint32_t ha = lut16((ga >> 4) & 0x07070707u, byte_sign_mask(ga), kV4[0], kV4[1], kV4[2], kV4[3]);
+          const uint32_t lb = lut16(gb & 0x07070707u, byte_sign_mask(gb << 4), kV4[0], kV4[1], kV4[2], kV4[3]);
+          const uint32_t hb = lut16((gb >> 4) & 0x07070707u, byte_sign_mask(gb), kV4[0], kV4[1], kV4[2], kV4[3]);
+          const half8_t lo = __builtin_bit_cast(half8_t, spread(la, lb)) + c1152;
+          const half8_t hi = __builtin_bit_cast(half8_t, spread(ha, hb)) + c1152;
+          o[2 * W] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, lo, o[2 * W], 0, 0, 0);
+          o[2 * W + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, hi, o[2 * W + 1], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int mp = w0 / 2; mp < (w0 + nw) / 2; ++mp) {
+          // High-bit plane word mp serves dims 32 mp .. 32 mp + 31 (tiles 2mp, 2mp+1).
+          const uint32_t gha = gather(lds_u4(va + (F::kWVHi + mp) * kTS));
+          const uint32_t ghb = gather(lds_u4(vb + (F::kWVHi + mp) * kTS));
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int m = 2 * mp + h;
+            const uint32_t gla = gather(lds_u4(va + (F::kWV + m) * kTS));
+            const uint32_t glb = gather(lds_u4(vb + (F::kWV + m) * kTS));
+            const int sh = 4 * h + vi;
+            const uint32_t sa_ = ((gla >> (2 * vi)) & 0x03030303u) | (((gha >> sh) << 2) & 0x04040404u);
+            const uint32_t sb_ = ((glb >> (2 * vi)) & 0x03030303u) | (((ghb >> sh) << 2) & 0x04040404u);
+            const uint32_t la = __builtin_amdgcn_perm(kV3[1], kV3[0], sa_);
+            const uint32_t lb = __builtin_amdgcn_perm(kV3[1], kV3[0], sb_);
+            const half8_t vv = __builtin_bit_cast(half8_t, spread(la, lb)) + c1152;
+            o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, vv, o[m], 0, 0, 0);
+          }
+        }
       }
     };
 
@@ -393,12 +471,12 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
       stage_m(sa, sb, u_cur, buf, A);
       // One basic block: P.V of unit u_cur and the scores of unit u_nxt.
       const int sbuf = buf ^ 1;
-      stage_p(A, buf, 0, 2);
+      stage_p(A, buf, 0, kAcc / 2);
       __builtin_amdgcn_sched_barrier(0);
       stage_s(ta, 0, sbuf, sa);
       fetch(ta, 2 * u_nn);
       __builtin_amdgcn_sched_barrier(0);
-      stage_p(A, buf, 2, 2);
+      stage_p(A, buf, kAcc / 2, kAcc / 2);
       __builtin_amdgcn_sched_barrier(0);
       stage_s(tb, 1, sbuf, sb);
       fetch(tb, 2 * u_nn + 1);
@@ -410,21 +488,19 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
       buf = sbuf;
     }
     stage_m(sa, sb, u_cur, buf, A);
-    stage_p(A, buf, 0, kVGroups);
+    stage_p(A, buf, 0, kAcc);
   }
 
   // Rows 8-15 of the P.V tiles (lanes 32-63) hold the residual part (x 2^12):
   // fold them into rows 0-7 (lanes 0-31).
 #pragma unroll
-  for (int b = 0; b < kVGroups; ++b)
+  for (int b = 0; b < kAcc; ++b)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t u = __float_as_uint(o[b][m][i]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        o[b][m][i] = fmaf(__uint_as_float(sw[1]), 1.0f / 4096.0f, o[b][m][i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = __float_as_uint(o[b][i]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      o[b][i] = fmaf(__uint_as_float(sw[1]), 1.0f / 4096.0f, o[b][i]);
+    }
 
   // ---- merge the waves ----------------------------------------------------
   float lsum = l_run + __shfl_xor(l_run, 16, kWave);
@@ -446,13 +522,11 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
       fw[i] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
     }
 #pragma unroll
-    for (int b = 0; b < kVGroups; ++b)
+    for (int b = 0; b < kAcc; ++b) {
+      const int d = F::kCompact ? 16 * b + n : 32 * (b >> 1) + 8 * (n >> 2) + (n & 3) + 4 * (b & 1);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int d = 32 * b + 8 * (n >> 2) + (n & 3) + 4 * m;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = o[b][m][i] * fw[i];
-      }
+      for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = o[b][i] * fw[i];
+    }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < a.rows * kD; idx += blockDim.x) {
@@ -477,17 +551,25 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_k3v4_kernel(Dev
 
 }  // namespace
 
-bool oct_k3v4_mfma_supported(const DevFmt& f, int rows) {
+bool oct_mfma_supported(const DevFmt& f, int rows) {
   const bool pow2 = (f.page_size & (f.page_size - 1)) == 0;
-  return f.kind == HKV_KIND_OCTAVE && !f.compact && f.D == kD && f.k_wide == kRope &&
-         f.v_bits == 4 && f.slot_bytes == kSlot && f.off_k_nope == 4 * kWNope &&
-         f.off_v == 4 * kWV && f.off_scales == 4 * kWScale && f.num_k_scales == 2 &&
-         f.k_block == 64 && rows <= kRows && f.page_size % kT == 0 && pow2;
+  if (f.kind != HKV_KIND_OCTAVE || rows > kRows || f.page_size % kT != 0 || !pow2) return false;
+  if (!f.compact)
+    return f.D == FmtK3V4::kD && f.k_wide == 64 && f.v_bits == 4 &&
+           f.slot_bytes == FmtK3V4::kSlot && f.off_k_nope == 4 * FmtK3V4::kWNope &&
+           f.off_v == 4 * FmtK3V4::kWV && f.off_scales == 4 * FmtK3V4::kWScale &&
+           f.num_k_scales == 2 && f.k_block == 64;
+  return f.D == FmtK3V3C::kD && f.v_bits == 3 && f.slot_bytes == FmtK3V3C::kSlot &&
+         f.off_v == 4 * FmtK3V3C::kWV && f.off_scales == 4 * FmtK3V3C::kWScale &&
+         f.num_k_scales == 1 && f.k_block == FmtK3V3C::kD;
 }
 
-hipError_t launch_decode_oct_k3v4(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
   if ((a.tokens_per_split + kT - 1) / kT > kMaxSplitTiles) return hipErrorInvalidValue;
-  decode_oct_k3v4_kernel<<<grid, dim3(kQWaves * kWave), 0, s>>>(f, a);
+  if (f.compact)
+    decode_oct_kernel<FmtK3V3C><<<grid, dim3(kQWaves * kWave), 0, s>>>(f, a);
+  else
+    decode_oct_kernel<FmtK3V4><<<grid, dim3(kQWaves * kWave), 0, s>>>(f, a);
   return hipGetLastError();
 }
 
