@@ -386,12 +386,12 @@ hipError_t launch_generic_e(const DevFmt& f, const DecArgs& a, int R, dim3 grid,
 
 bool q4_mfma_supported(const DevFmt& f, int rows);
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
-bool oct_mfma_supported(const DevFmt& f, int rows);
+int oct_mfma_rows(const DevFmt& f, int rows);
 hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
 
 // Decode kernels: 0 the generic VALU kernel (every format), 1 the Q4_0 MFMA
-// kernel (head size 256), 2 the Octave MFMA kernel (k3v4 at head size 128,
-// k3v3 compact at 256).
+// kernel (head size 256, 8 rows), 2 the Octave MFMA kernel (k3v4 at head
+// size 128, k3v3 compact at 256; 8 or 16 rows).
 constexpr int kKernelGeneric = 0, kKernelQ4 = 1, kKernelOctK3v4 = 2;
 
 constexpr int64_t kTargetSplitsWgs = 512;
@@ -407,20 +407,28 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   if (q.rows > 32) return false;
   q.num_groups = num_queries / queries_per_seq;
   auto mfma_kernel = [&](int rows) {
-    return q4_mfma_supported(f, rows)    ? kKernelQ4
-           : oct_mfma_supported(f, rows) ? kKernelOctK3v4
-                                         : kKernelGeneric;
+    return q4_mfma_supported(f, rows)   ? kKernelQ4
+           : oct_mfma_rows(f, rows) > 0 ? kKernelOctK3v4
+                                        : kKernelGeneric;
   };
   q.kernel = mfma_kernel(q.rows);
-  // More rows than the matrix-core kernels take (they hold 8 query rows per
-  // KV head): when one query token's heads fit, every query becomes its own
-  // group (each streams the sequence's K/V through its own workgroups).
-  if (q.kernel == kKernelGeneric && q.n_q > 1 && mfma_kernel(q.group) != kKernelGeneric) {
-    q.n_q = 1;
-    q.rows = q.group;
-    q.num_groups = num_queries;
-    q.kernel = mfma_kernel(q.rows);
+  // More rows than the matrix-core kernels take (8 or 16 query rows per KV
+  // head): the queries of a sequence are split into the largest sub-groups
+  // that fit (each sub-group streams the sequence's K/V through its own
+  // workgroups).
+  if (q.kernel == kKernelGeneric && q.n_q > 1) {
+    for (int nq = q.n_q - 1; nq >= 1; --nq) {
+      if (q.n_q % nq != 0 || mfma_kernel(q.group * nq) == kKernelGeneric) continue;
+      q.num_groups = num_queries / nq;
+      q.n_q = nq;
+      q.rows = q.group * nq;
+      q.kernel = mfma_kernel(q.rows);
+      break;
+    }
   }
+  q.rows_pad = q.kernel == kKernelQ4        ? 8
+               : q.kernel == kKernelOctK3v4 ? oct_mfma_rows(f, q.rows)
+                                            : round_rows(q.rows);
   // Split size: enough splits that (sequence group, KV head, split) fills the
   // chip with one resident round of workgroups (the MFMA kernel: one
   // 8-wave workgroup per CU; the generic kernel: two 4-wave ones), in whole
@@ -437,7 +445,7 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   }
   q.num_splits = max_klen > 0 ? (max_klen + q.tokens_per_split - 1) / q.tokens_per_split : 1;
   q.partial_floats = kPartialHead + (size_t)f.D;
-  const int R = q.kernel != kKernelGeneric ? 8 : round_rows(q.rows);
+  const int R = q.rows_pad;
   q.workspace_bytes = sizeof(float) * q.partial_floats * R * (size_t)q.num_splits *
                       (size_t)q.num_groups * (size_t)num_kv_heads;
   if (q.kernel == kKernelGeneric && generic_lds_bytes(f, R) > 160 * 1024) return false;
@@ -459,7 +467,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   a.group = p.group;
   a.n_q = p.n_q;
   a.rows = p.rows;
-  a.rows_pad = p.kernel != kKernelGeneric ? 8 : round_rows(p.rows);
+  a.rows_pad = p.rows_pad;
   a.num_queries = p.num_groups * p.n_q;
   a.cache = cache;
   a.block_table = block_table;

@@ -25,7 +25,12 @@
 //  * P.V on v_mfma_f32_16x16x32_f16: B = the codebook value as an exact fp16
 //    (the biased byte LUT[c] + 128 under an 0x64 high byte is 1152 + LUT[c]),
 //    so no residual is needed on this side; the token's V scale multiplies p
-//    in the A operand (rows 0-7 fp16(p s), rows 8-15 the residual x 2^12).
+//    in the A operand, fp16(p s) plus its residual x 2^12, in one of two row
+//    modes: with 8 query rows the residual takes A rows 8-15 (one MFMA per 32
+//    tokens); with 16 rows it takes the other half of the K dimension: a
+//    lane's 8 k-slots are its own 4 tokens' fp16(p s) and residuals, against
+//    their values and values x 2^-12 in B (exact, and normal since |LUT| >= 6),
+//    one MFMA per 16 tokens and no data moved between lanes.
 #include "hkv_decode_common.h"
 
 namespace hkv {
@@ -58,7 +63,7 @@ struct FmtK3V3C {           // octave_k3v3_compact, head size 256
   static constexpr int kChunks = 3;   // 12 chunks of 16 bytes per slot: 3 per lane
   static constexpr int kAcc = kD / 16;
 };
-constexpr int kRows = 8;           // query rows per KV head
+constexpr int kRowsMax = 16;       // query rows per KV head (16-row mode)
 constexpr int kT = 16;             // tokens per tile
 constexpr int kTS = kT + 4;        // token stride (words) of the transposed tile
 constexpr int kQMaxI = 32639;      // largest |q| code of the two-plane int8 split
@@ -127,50 +132,55 @@ struct Tile {
   uint32_t sw;
 };
 
-template <class F>
+template <class F, int RM>
 struct __align__(16) OctLds {
   static constexpr int kD = F::kD;
   static constexpr int kSlotW = (F::kSlot + 3) / 4;
-  int8_t qB[kD / 64][16][64];  // B operand bytes: [64-dim block][column][dim]
-  float qsc[kRows];
-  float mlw[kQWaves][kRows][2];
+  // B operand bytes, [64-dim block][column][dim]: 8-row mode column r + 8 plane,
+  // 16-row mode 16 plane + r.
+  int8_t qB[kD / 64][2 * RM][64];
+  float qsc[RM];
+  float mlw[kQWaves][RM][2];
   int pid[kMaxSplitTiles];
   int next_unit;
   int pad_[3];
   union {
     uint32_t tt[kQWaves][2][2][kSlotW][kTS];  // [buf][tile][slot word][token]
-    float ob[kQWaves][kRows][kD];
+    float ob[kQWaves][RM][kD];
   } u;
 };
 
-template <class F>
+template <class F, int RM>
 __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f, DecArgs a) {
   constexpr int kD = F::kD;
   constexpr int kSlot = F::kSlot;
   constexpr int kE = kD / kWave;  // query values per lane
   constexpr int kAcc = F::kAcc;
-  __shared__ OctLds<F> L;
+  constexpr bool kK16 = RM == 16;       // residual of p in the K dimension
+  constexpr int kQR = RM / kQWaves;     // query rows per wave
+  __shared__ OctLds<F, RM> L;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
   const int split = blockIdx.x, kvh = blockIdx.y, gi = blockIdx.z;
   const int q0 = gi * a.n_q;
-  // Query row `wave`: its loads go out first, independent of the page table.
-  float qx[kE];
-  {
-    const int r = wave;
+  // Query rows wave + 8 k: their loads go out first, independent of the page table.
+  float qx[kQR][kE];
+#pragma unroll
+  for (int k = 0; k < kQR; ++k) {
+    const int r = wave + kQWaves * k;
     if (r < a.rows) {
       const int j = r / a.group, g = r % a.group;
       const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
 #pragma unroll
       for (int e = 0; e < kE; ++e) {
         const int d = kWave * e + lane;
-        qx[e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
-                        : ((const float*)a.query)[qrow * kD + d];
+        qx[k][e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
+                           : ((const float*)a.query)[qrow * kD + d];
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < kE; ++e) qx[e] = 0.0f;
+      for (int e = 0; e < kE; ++e) qx[k][e] = 0.0f;
     }
   }
   const int req = a.q_to_req[q0];
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(t_begin + a.tokens_per_split, kmax);
-  float* part = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits + split) * kRows *
+  float* part = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits + split) * RM *
                            a.pstride;
   if (t_begin >= t_end) {
     for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
@@ -217,11 +227,13 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     fetch_pid(ta, k0, bt[(t_begin + kT * k0) >> ps_shift]);
     fetch_pid(tb, k1, bt[(t_begin + kT * k1) >> ps_shift]);
   }
-  {
-    const int r = wave;
+#pragma unroll
+  for (int k = 0; k < kQR; ++k) {
+    const int r = wave + kQWaves * k;
     float x[kE];
 #pragma unroll
-    for (int e = 0; e < kE; ++e) x[e] = f.use_signs ? apply_sign(f, qx[e], kWave * e + lane) : qx[e];
+    for (int e = 0; e < kE; ++e)
+      x[e] = f.use_signs ? apply_sign(f, qx[k][e], kWave * e + lane) : qx[k][e];
     if (r < a.rows) fwht_strided<kE>(x, f.k_block, f.k_norm);
     float qmax = 0.0f;
 #pragma unroll
@@ -235,15 +247,17 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       const int hi = (qi + 128) >> 8;
       const int lo = qi - hi * 256;
       const int d = kWave * e + lane;
-      L.qB[d >> 6][r][d & 63] = (int8_t)hi;
-      L.qB[d >> 6][8 + r][d & 63] = (int8_t)lo;
+      L.qB[d >> 6][kK16 ? r : r][d & 63] = (int8_t)hi;
+      L.qB[d >> 6][kK16 ? 16 + r : 8 + r][d & 63] = (int8_t)lo;
     }
     // 1/64: the codebook scale (LUT_ONE) of the K values.
     if (lane == 0) L.qsc[r] = (qmax / kQMax) * a.q_scale * (1.0f / 64.0f);
   }
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int row = n & 7;
+  // The score row of this lane: 8-row mode row n & 7 (lanes n, n + 8 hold its
+  // hi and lo planes), 16-row mode row n.
+  const int row = kK16 ? n : (n & 7);
   const int klen_row = row < a.rows ? a.q_to_klen[q0 + row / a.group] : 0;
   int kmin = kmax;
   for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
@@ -252,12 +266,17 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   const float qs = L.qsc[row];
   const float w_own = n < 8 ? 256.0f * qs : qs;
   const float w_partner = n < 8 ? qs : 256.0f * qs;
-  int4_t qreg[kD / 64];
+  // 8-row mode: one B operand per block (columns = rows x planes); 16-row
+  // mode: the hi and lo planes of 16 rows.
+  int4_t qreg[kD / 64], qlo[kK16 ? kD / 64 : 1];
 #pragma unroll
-  for (int c = 0; c < kD / 64; ++c) qreg[c] = *(const int4_t*)&L.qB[c][n][16 * g];
+  for (int c = 0; c < kD / 64; ++c) {
+    qreg[c] = *(const int4_t*)&L.qB[c][n][16 * g];
+    if constexpr (kK16) qlo[c] = *(const int4_t*)&L.qB[c][16 + n][16 * g];
+  }
   const bool live_row = row < a.rows;
-  const float alpha_a = live_row ? (n < 8 ? 1.0f : 4096.0f) : 0.0f;
-  const float beta_a = live_row ? (n < 8 ? 0.0f : -4096.0f) : 0.0f;
+  const float alpha_a = live_row ? (kK16 || n < 8 ? 1.0f : 4096.0f) : 0.0f;
+  const float beta_a = live_row ? (kK16 || n < 8 ? 0.0f : -4096.0f) : 0.0f;
   // Gathers byte (n & 3) of a word of tokens t0..t3 into bytes 0..3.
   const int jb = n & 3;
   const uint32_t gsel_lo = (uint32_t)jb | ((uint32_t)(jb + 4) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
@@ -313,17 +332,31 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
           const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
           A1[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
         }
-        const int4_t C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qreg[0], zero4, 0, 0, 0);
-        const int4_t C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qreg[1], zero4, 0, 0, 0);
+        if constexpr (!kK16) {
+          const int4_t C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qreg[0], zero4, 0, 0, 0);
+          const int4_t C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qreg[1], zero4, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float acc = fmaf((float)C0[i], h2f((uint16_t)(ksw[i] & 0xffffu)),
-                                 (float)C1[i] * h2f((uint16_t)(ksw[i] >> 16)));
-          sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+          for (int i = 0; i < 4; ++i) {
+            const float acc = fmaf((float)C0[i], h2f((uint16_t)(ksw[i] & 0xffffu)),
+                                   (float)C1[i] * h2f((uint16_t)(ksw[i] >> 16)));
+            sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+          }
+        } else {
+          // hi and lo planes joined in int32 (exact: |hi| 256 + |lo| < 2^31).
+          const int4_t H0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qreg[0], zero4, 0, 0, 0);
+          const int4_t L0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qlo[0], zero4, 0, 0, 0);
+          const int4_t H1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qreg[1], zero4, 0, 0, 0);
+          const int4_t L1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qlo[1], zero4, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float acc = fmaf((float)(H0[i] * 256 + L0[i]), h2f((uint16_t)(ksw[i] & 0xffffu)),
+                                   (float)(H1[i] * 256 + L1[i]) * h2f((uint16_t)(ksw[i] >> 16)));
+            sc[i] = acc * qs;
+          }
         }
       } else {
         // Four 64-dim blocks under one scale: the int32 results add up.
-        int4_t C = zero4;
+        int4_t C = zero4, Cl = zero4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t lw = tr[(4 * c + g) * kTS + n];
@@ -335,11 +368,16 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
             Ac[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
           }
           C = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac, qreg[c], C, 0, 0, 0);
+          if constexpr (kK16) Cl = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac, qlo[c], Cl, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float acc = (float)C[i] * h2f((uint16_t)(ksw[i] & 0xffffu));
-          sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+          if constexpr (!kK16) {
+            const float acc = (float)C[i] * h2f((uint16_t)(ksw[i] & 0xffffu));
+            sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+          } else {
+            sc[i] = (float)(C[i] * 256 + Cl[i]) * h2f((uint16_t)(ksw[i] & 0xffffu)) * qs;
+          }
         }
       }
     };
@@ -347,7 +385,10 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     // Softmax of unit u (tiles 2u, 2u + 1) and the P.V A operand: p times
     // the token's V scale (the 1/64 of the codebook is taken out of p and
     // put back into l at the end).
-    auto stage_m = [&](const float (&sa)[4], const float (&sb)[4], int u, int buf, half8_t& A) {
+    struct AOps {
+      half8_t a, b;  // 8-row mode: a only (both tiles); 16-row mode: per tile
+    };
+    auto stage_m = [&](const float (&sa)[4], const float (&sb)[4], int u, int buf, AOps& A) {
       float s[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -374,7 +415,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
         l_run *= alpha;
         float al[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (4 * g + i) & 7, kWave);
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, kK16 ? 4 * g + i : (4 * g + i) & 7, kWave);
 #pragma unroll
         for (int b = 0; b < kAcc; ++b)
 #pragma unroll
@@ -394,14 +435,42 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
         l_run += p;
         const float pv = p * h2f((uint16_t)((vw[i] >> kVsh) & 0xffffu));
         const _Float16 h = (_Float16)pv;
-        A[i] = (_Float16)fmaf((float)h, beta_a, pv * alpha_a);
+        if constexpr (!kK16) {
+          A.a[i] = (_Float16)fmaf((float)h, beta_a, pv * alpha_a);
+        } else {
+          // k-slots 0-3: fp16(p s) of the tile's 4 tokens, 4-7: residual x 2^12.
+          half8_t& At = i < 4 ? A.a : A.b;
+          At[i & 3] = (_Float16)(pv * alpha_a);
+          At[4 + (i & 3)] = (_Float16)(fmaf((float)h, -1.0f, pv) * (4096.0f * alpha_a));
+        }
       }
     };
 
     // P.V of a unit from LDS buffer `buf`, accumulator tiles [w0, w0 + nw)
     // (k3v4: even and odd tiles are the low and high nibbles of V word group
     // b >> 1; compact: tile m holds dims 16 m .. 16 m + 15).
-    auto stage_p = [&](const half8_t& A, int buf, int w0, int nw) {
+    // Two tiles' B operands in 16-row mode: values, then values x 2^-12.
+    auto k16_ops = [&](const half8_t& v, half8_t& ba, half8_t& bb) {
+      const _Float16 s12 = (_Float16)(1.0f / 4096.0f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ba[i] = v[i];
+        ba[4 + i] = v[i] * s12;
+        bb[i] = v[4 + i];
+        bb[4 + i] = v[4 + i] * s12;
+      }
+    };
+    auto mma = [&](const AOps& A, const half8_t& v, float4_t& acc) {
+      if constexpr (!kK16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.a, v, acc, 0, 0, 0);
+      } else {
+        half8_t ba, bb;
+        k16_ops(v, ba, bb);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.a, ba, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.b, bb, acc, 0, 0, 0);
+      }
+    };
+    auto stage_p = [&](const AOps& A, int buf, int w0, int nw) {
       const half8_t c1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
                              (_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
                              (_Float16)-1152.0f, (_Float16)-1152.0f};
@@ -430,8 +499,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
           const uint32_t hb = lut16((gb >> 4) & 0x07070707u, byte_sign_mask(gb), kV4[0], kV4[1], kV4[2], kV4[3]);
           const half8_t lo = __builtin_bit_cast(half8_t, spread(la, lb)) + c1152;
           const half8_t hi = __builtin_bit_cast(half8_t, spread(ha, hb)) + c1152;
-          o[2 * W] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, lo, o[2 * W], 0, 0, 0);
-          o[2 * W + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, hi, o[2 * W + 1], 0, 0, 0);
+          mma(A, lo, o[2 * W]);
+          mma(A, hi, o[2 * W + 1]);
         }
       } else {
 #pragma unroll
@@ -450,7 +519,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
             const uint32_t la = __builtin_amdgcn_perm(kV3[1], kV3[0], sa_);
             const uint32_t lb = __builtin_amdgcn_perm(kV3[1], kV3[0], sb_);
             const half8_t vv = __builtin_bit_cast(half8_t, spread(la, lb)) + c1152;
-            o[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, vv, o[m], 0, 0, 0);
+            mma(A, vv, o[m]);
           }
         }
       }
@@ -463,7 +532,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     stage_s(tb, 1, 0, sb);
     fetch(tb, 2 * u_nxt + 1);
     int buf = 0;
-    half8_t A;
+    AOps A;
     while (u_nxt < nu) {
       int u_nn = 0;
       if (lane == 0) u_nn = atomicAdd(&L.next_unit, 1);
@@ -491,26 +560,28 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     stage_p(A, buf, 0, kAcc);
   }
 
-  // Rows 8-15 of the P.V tiles (lanes 32-63) hold the residual part (x 2^12):
-  // fold them into rows 0-7 (lanes 0-31).
+  // 8-row mode: rows 8-15 of the P.V tiles (lanes 32-63) hold the residual
+  // part (x 2^12): fold them into rows 0-7 (lanes 0-31).
+  if constexpr (!kK16) {
 #pragma unroll
-  for (int b = 0; b < kAcc; ++b)
+    for (int b = 0; b < kAcc; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t u = __float_as_uint(o[b][i]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      o[b][i] = fmaf(__uint_as_float(sw[1]), 1.0f / 4096.0f, o[b][i]);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = __float_as_uint(o[b][i]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        o[b][i] = fmaf(__uint_as_float(sw[1]), 1.0f / 4096.0f, o[b][i]);
+      }
+  }
 
   // ---- merge the waves ----------------------------------------------------
   float lsum = l_run + __shfl_xor(l_run, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
-  if (g == 0 && n < kRows) {
+  if (g == 0 && n < RM) {
     L.mlw[wave][n][0] = m_run;
     L.mlw[wave][n][1] = lsum * 64.0f;  // p was kept as p / 64
   }
   __syncthreads();
-  if (g < 2) {
+  if (kK16 || g < 2) {
     float fw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -551,25 +622,37 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 
 }  // namespace
 
-bool oct_mfma_supported(const DevFmt& f, int rows) {
+// Rows the Octave MFMA kernel takes for this format: 8 or 16 (its row
+// mode), or 0 when the format or the row count is not one it handles.
+int oct_mfma_rows(const DevFmt& f, int rows) {
   const bool pow2 = (f.page_size & (f.page_size - 1)) == 0;
-  if (f.kind != HKV_KIND_OCTAVE || rows > kRows || f.page_size % kT != 0 || !pow2) return false;
+  if (f.kind != HKV_KIND_OCTAVE || rows > kRowsMax || f.page_size % kT != 0 || !pow2) return 0;
+  bool ok;
   if (!f.compact)
-    return f.D == FmtK3V4::kD && f.k_wide == 64 && f.v_bits == 4 &&
-           f.slot_bytes == FmtK3V4::kSlot && f.off_k_nope == 4 * FmtK3V4::kWNope &&
-           f.off_v == 4 * FmtK3V4::kWV && f.off_scales == 4 * FmtK3V4::kWScale &&
-           f.num_k_scales == 2 && f.k_block == 64;
-  return f.D == FmtK3V3C::kD && f.v_bits == 3 && f.slot_bytes == FmtK3V3C::kSlot &&
+    ok = f.D == FmtK3V4::kD && f.k_wide == 64 && f.v_bits == 4 &&
+         f.slot_bytes == FmtK3V4::kSlot && f.off_k_nope == 4 * FmtK3V4::kWNope &&
+         f.off_v == 4 * FmtK3V4::kWV && f.off_scales == 4 * FmtK3V4::kWScale &&
+         f.num_k_scales == 2 && f.k_block == 64;
+  else
+    ok = f.D == FmtK3V3C::kD && f.v_bits == 3 && f.slot_bytes == FmtK3V3C::kSlot &&
          f.off_v == 4 * FmtK3V3C::kWV && f.off_scales == 4 * FmtK3V3C::kWScale &&
          f.num_k_scales == 1 && f.k_block == FmtK3V3C::kD;
+  if (!ok) return 0;
+  return rows <= 8 ? 8 : 16;
 }
 
 hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
   if ((a.tokens_per_split + kT - 1) / kT > kMaxSplitTiles) return hipErrorInvalidValue;
-  if (f.compact)
-    decode_oct_kernel<FmtK3V3C><<<grid, dim3(kQWaves * kWave), 0, s>>>(f, a);
-  else
-    decode_oct_kernel<FmtK3V4><<<grid, dim3(kQWaves * kWave), 0, s>>>(f, a);
+  const dim3 block(kQWaves * kWave);
+  if (a.rows_pad == 8) {
+    if (f.compact) decode_oct_kernel<FmtK3V3C, 8><<<grid, block, 0, s>>>(f, a);
+    else decode_oct_kernel<FmtK3V4, 8><<<grid, block, 0, s>>>(f, a);
+  } else if (a.rows_pad == 16) {
+    if (f.compact) decode_oct_kernel<FmtK3V3C, 16><<<grid, block, 0, s>>>(f, a);
+    else decode_oct_kernel<FmtK3V4, 16><<<grid, block, 0, s>>>(f, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ struct DecodePlan {
   int group;            // query heads per KV head
   int n_q;              // queries per sequence group
   int rows;             // group * n_q rows sharing one KV head
+  int rows_pad;         // rows of a partial record block (the kernel's row count)
   int num_groups;       // num_queries / n_q
   int tokens_per_split;
   int num_splits;

@@ -133,6 +133,7 @@ def test_decode_matches_oracle(ci):
                                               ("q4_0", 128, 0, 4, 4),
                                               ("q4_0", 64, 0, 6, 3),
                                               ("octave_k3v4", 128, 64, 32, 8),
+                                              ("octave_k3v4", 128, 64, 32, 4),
                                               ("octave_k3v3", 128, 64, 8, 1),
                                               ("octave_k3v3_compact", 256, 64, 32, 4),
                                               ("octave_k3v4", 192, 64, 4, 2)])
