@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = ("decode-attn packed-KV GB/s (% HBM peak) at 128K ctx; "
           "quantize-append tokens/s")
 INFINITY_CACHE_BYTES = 256 << 20
+WARM_SECONDS = 0.3
 
 
 def parse():
@@ -43,6 +44,9 @@ def parse():
                    help="cache copies rotated between steps (0: enough to exceed the "
                         "256 MB Infinity Cache twice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="replay the step from HIP graphs (one per cache copy) instead of "
+                        "launching it from Python")
     p.add_argument("--cpu-threads", type=int, default=0)
     p.add_argument("--profile", action="store_true",
                    help="short run for a profiler: no CPU baseline")
@@ -183,18 +187,11 @@ def main():
     copies = args.copies or max(2, -(-2 * INFINITY_CACHE_BYTES // cache_bytes))
     caches = [hkv.new_cache(f, w.num_pages, Hkv, dev) for _ in range(copies)]
 
-    # Bulk build of every cache copy (quantize-append of all tokens), timed.
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    # Build every cache copy (quantize-append of all tokens; untimed here).
     for c in caches:
         hkv.quantize_append(f, key, value, slot_mapping, c)
-    e1.record()
     torch.cuda.synchronize()
-    bulk_ms = e0.elapsed_time(e1) / copies
     total_tokens = key.shape[0]
-    del key, value
-    torch.cuda.empty_cache()
 
     def step(i):
         c = caches[i % copies]
@@ -202,35 +199,92 @@ def main():
         hkv.decode_attention(f, query, c, block_table, q_to_req, q_to_klen, w.max_klen, cfg.n_q,
                              scale, out=out, workspace=workspace)
 
+    def decode_call(i):
+        hkv.decode_attention(f, query, caches[i % copies], block_table, q_to_req, q_to_klen,
+                             w.max_klen, cfg.n_q, scale, out=out, workspace=workspace)
+
+    run_step, run_decode = step, decode_call
+    if args.graph:
+        # One HIP graph per cache copy for the step and for the decode call
+        # alone; each replay is checked against the eager call (to the last
+        # bits: the split kernels' wave-level work queue can change how a
+        # split's tokens are grouped between calls).
+        for i in range(copies):
+            step(i)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(copies):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g_step, g_dec = [], []
+        for i in range(copies):
+            for fn, lst in ((step, g_step), (decode_call, g_dec)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn(i)
+                lst.append(g)
+        torch.cuda.synchronize()
+        for i in range(copies):
+            decode_call(i)
+            ref = out.clone()
+            for g in (g_dec[i], g_step[i]):
+                out.fill_(float("nan"))
+                g.replay()
+                torch.cuda.synchronize()
+                err = (out - ref).abs().max().item()
+                if not err <= 1e-4 * (1.0 + ref.abs().max().item()):
+                    raise RuntimeError(f"graph replay differs from the eager call ({err})")
+        run_step = lambda i: g_step[i % copies].replay()
+        run_decode = lambda i: g_dec[i % copies].replay()
+
+    # Clock warm-up: the GPU takes several milliseconds of load to reach its
+    # steady clocks, so untimed steps run for WARM_SECONDS first (not under
+    # --profile, where every dispatch is recorded); then the --warmup steps,
+    # then exactly --steps timed steps.
+    warm = 0.0 if args.profile else WARM_SECONDS
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < warm:
+        for _ in range(10):
+            run_step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i)
+        run_step(i)
     torch.cuda.synchronize()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start.record()
     for i in range(args.steps):
-        step(i)
+        run_step(i)
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # Per-launch durations of the decode call and of the append, on the stream
-    # they run on (torch's current stream), events around each launch.
-    def timed(fn, n):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        for i, (a, b) in enumerate(evs):
-            a.record()
-            fn(i)
-            b.record()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
-
+    # Average duration of one decode call (its split-K kernel and merge
+    # kernel) on the stream it runs on (torch's current stream): one event
+    # pair around back-to-back calls.  The append's device cost is the rest
+    # of the step.
     n_t = max(args.steps, 20)
-    decode_ms = timed(lambda i: hkv.decode_attention(
-        f, query, caches[i % copies], block_table, q_to_req, q_to_klen, w.max_klen, cfg.n_q,
-        scale, out=out, workspace=workspace), n_t)
-    append_ms = timed(lambda i: hkv.quantize_append(f, new_k, new_v, new_sm, caches[i % copies]),
-                      n_t)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for i in range(n_t):
+        run_decode(i)
+    d1.record()
+    torch.cuda.synchronize()
+    decode_ms = d0.elapsed_time(d1) / n_t
+    append_ms = max(ms_per_step - decode_ms, 0.0)
+
+    # Bulk quantize-append of every token into every copy (same bytes again),
+    # timed while the clocks are up.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for c in caches:
+        hkv.quantize_append(f, key, value, slot_mapping, c)
+    e1.record()
+    torch.cuda.synchronize()
+    bulk_ms = e0.elapsed_time(e1) / copies
 
     packed = W.packed_bytes(w, f.slot_bytes)
     value = packed / (ms_per_step * 1e-3) / 1e9
@@ -252,7 +306,8 @@ def main():
         "config": {"workload": cfg.name, "cache_dtype": cfg.cache_dtype, "batch": B,
                    "context": int(w.max_klen), "head_size": D, "q_heads": Hq, "kv_heads": Hkv,
                    "page_size": cfg.page_size, "queries_per_seq": cfg.n_q,
-                   "append_tokens_per_seq": cfg.n_append, "cache_copies_rotated": copies},
+                   "append_tokens_per_seq": cfg.n_append, "cache_copies_rotated": copies,
+                   "launch": "hip_graph" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_call"],
@@ -260,7 +315,8 @@ def main():
                      "bytes_per_call": packed, "us_per_call": round(decode_ms * 1e3, 3)},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "append_us": round(append_ms * 1e3, 3),
-        "append_tokens_per_s": round(len(rows) / (append_ms * 1e-3), 1),
+        "append_tokens_per_s": (round(len(rows) / (append_ms * 1e-3), 1)
+                                if append_ms > 0 else None),
         "bulk_quantize_tokens_per_s": round(total_tokens / (bulk_ms * 1e-3), 1),
         "bulk_quantize_gbps": round((2 * total_tokens * Hkv * D * w.key.itemsize +
                                      total_tokens * Hkv * f.slot_bytes) / (bulk_ms * 1e-3) / 1e9,

@@ -40,8 +40,47 @@ struct DevFmt {
 
 // ---------------------------------------------------------------------------
 // Wave shuffles.
-__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// DPP move of v.  Every pattern used here reads a lane inside the same row,
+// so bound_ctrl (out-of-range lanes read 0) never applies; it lets the
+// compiler fold the move into the consuming add / max / or.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Value of lane l ^ m.  Every caller passes a constant m (unrolled loops),
+// so the switch folds to plain VALU data movement: DPP quad permutations for
+// 1 and 2, a half-row mirror then a quad reversal for 4, a 16-lane rotate for
+// 8, and the lane-swap instructions for 16 and 32 (swapping a value with
+// itself leaves the partner's copy in one of the two results); anything else
+// falls back to the LDS permute.
+__device__ __forceinline__ uint32_t xor_u32(uint32_t u, int m) {
+  switch (m) {
+    case 1:
+      return dpp<0xB1>(u);  // quad_perm [1,0,3,2]
+    case 2:
+      return dpp<0x4E>(u);  // quad_perm [2,3,0,1]
+    case 4:
+      return dpp<0x1B>(dpp<0x141>(u));  // row_half_mirror, then quad_perm [3,2,1,0]
+    case 8:
+      return dpp<0x128>(u);  // row_ror:8
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      return (lane_id() & 16) ? r[0] : r[1];
+    }
+    case 32: {
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      return (lane_id() & 32) ? r[0] : r[1];
+    }
+    default:
+      return (uint32_t)__shfl_xor((int)u, m, kWave);
+  }
+}
+__device__ __forceinline__ float shfl_xor(float v, int m) {
+  return __uint_as_float(xor_u32(__float_as_uint(v), m));
+}
 
 // fp16 bits <-> fp32 (hardware conversions; round to nearest even).
 __device__ __forceinline__ float h2f(uint16_t h) {
@@ -63,6 +102,22 @@ __device__ __forceinline__ float apply_sign(const DevFmt& f, float x, int dim) {
 }
 
 // ---------------------------------------------------------------------------
+// Both lane-swap results of v with itself: of the pair (r[0], r[1]) one is the
+// lane's own value and the other its partner's (lane ^ 16, or lane ^ 32) --
+// r[0] the lower lane's value and r[1] the upper lane's in both lanes.  A
+// sum r[0] + r[1] is then lower + upper in every lane, and
+// fma(r[1], -1, r[0]) is lower - upper.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Orthonormal Walsh-Hadamard transform (vLLM rocm_octave docs, fwht_blocks)
 // of a vector held "strided" across the wave: register e of lane l holds
 // element 64*e + l.  Stages h = 1, 2, 4, ... < block in ascending order; the
@@ -76,11 +131,20 @@ __device__ __forceinline__ void fwht_strided(float (&x)[E], int block, float nor
 #pragma unroll
   for (int h = 1; h < kWave; h <<= 1) {
     if (h < block) {
-      const bool upper = (lane & h) != 0;
+      // lower (bit h clear): mine + partner; upper: partner - mine, as one
+      // fma with an exact +-1 product.
+      const float sgn = (lane & h) ? -1.0f : 1.0f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float p = shfl_xor(x[e], h);
-        x[e] = upper ? (p - x[e]) : (x[e] + p);
+        if (h < 16) {
+          x[e] = fmaf(x[e], sgn, shfl_xor(x[e], h));
+        } else {
+          const uint32_t u = __float_as_uint(x[e]);
+          const auto r = (h == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                                   : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+          // r[0] = lower element, r[1] = upper element, in both lanes.
+          x[e] = fmaf(__uint_as_float(r[1]), sgn, __uint_as_float(r[0]));
+        }
       }
     }
   }
@@ -105,14 +169,17 @@ __device__ __forceinline__ void fwht_strided(float (&x)[E], int block, float nor
 // xor partners every lane ends with the same bits as the sequential tree
 // (a + b == b + a in IEEE arithmetic).
 __device__ __forceinline__ float wave_tree_sum(float v) {
+  v = sum_xor32(v);
+  v = sum_xor16(v);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = v + shfl_xor(v, m);
+  for (int m = 8; m >= 1; m >>= 1) v = v + shfl_xor(v, m);
   return v;
 }
 // Same over 32-lane halves (strides 16..1).
 __device__ __forceinline__ float half_tree_sum(float v) {
+  v = sum_xor16(v);
 #pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) v = v + shfl_xor(v, m);
+  for (int m = 8; m >= 1; m >>= 1) v = v + shfl_xor(v, m);
   return v;
 }
 

@@ -1,10 +1,11 @@
 // hkv_quant.hip -- quantize-append and dequantize kernels.
 //
-// One wave (a 64-thread workgroup) per (token, KV head).  The head vector
-// lives "strided" in registers (register e of lane l = element 64e + l), is
-// sign-flipped and Walsh-Hadamard rotated in registers, quantized with wave
-// reductions, and the slot is assembled in LDS and written with 4-byte
-// stores (consecutive lanes -> consecutive words).
+// Quantize-append: each wave takes (token, KV head) rows in turn and loads
+// the next row while it works on the current one.  A row lives "strided" in
+// registers (register e of lane l = element 64e + l); it is sign-flipped and
+// Walsh-Hadamard rotated in registers, quantized with wave reductions, and
+// its codes are packed into slot words in registers by OR-reductions over the
+// lanes that share a word, then stored straight to the slot.
 //
 // Sources: vLLM API docs "vllm.v1.attention.ops.rocm_octave"
 // (reference_quantize, _quantize_lut, _pack, reference_dequantize) and Strata
@@ -64,10 +65,11 @@ __device__ __forceinline__ float block_tree_sum(float (&t)[E], int e0, int nreg)
 
 // Octave quantizer (_quantize_lut) over registers [e0, e0+nreg) of a strided
 // vector: block RMS, nearest Lloyd-Max code, scale with x . x_hat = |x|^2.
+// The codes land in codes[e0 .. e0+nreg); returns the fp16 bits of the scale
+// (the same in every lane).
 template <int E, int BITS>
-__device__ __forceinline__ uint16_t octave_block(const float (&x)[E], int e0, int nreg,
-                                                 uint8_t* codes_lds) {
-  const int lane = lane_id();
+__device__ __forceinline__ uint32_t octave_block(const float (&x)[E], int e0, int nreg,
+                                                 uint32_t (&codes)[E]) {
   float t[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) t[e] = x[e] * x[e];
@@ -81,8 +83,7 @@ __device__ __forceinline__ uint16_t octave_block(const float (&x)[E], int e0, in
     if (e >= e0 && e < e0 + nreg) {
       const float y = (x[e] / rms) * mult;
       int lv;
-      const int c = bucket<BITS>(y, &lv);
-      codes_lds[kWave * e + lane] = (uint8_t)c;
+      codes[e] = (uint32_t)bucket<BITS>(y, &lv);
       t[e] = x[e] * (float)lv;
     }
   }
@@ -94,153 +95,441 @@ __device__ __forceinline__ uint16_t octave_block(const float (&x)[E], int e0, in
 
 // Q4_0 over one 32-value block = one half-register (lanes 0-31 or 32-63).
 // Max-abs element with the tie-break (larger magnitude; equal magnitudes keep
-// the larger signed value); d = m / -8; code = min(15, trunc(x/d + 8.5)).
-__device__ __forceinline__ uint16_t q4_block(float x, uint8_t* code_lds) {
-  float a = fabsf(x), m = x;
-#pragma unroll
-  for (int s = 16; s >= 1; s >>= 1) {
-    const float a2 = shfl_xor(a, s), m2 = shfl_xor(m, s);
-    if (a2 > a || (a2 == a && m2 > m)) {
-      a = a2;
-      m = m2;
-    }
+// the larger signed value) is the maximum of the key (|x| bits, x >= 0) --
+// the fp32 bits rotated left by one with the sign bit inverted -- reduced
+// over the half with unsigned max.  d = m / -8; code = min(15, trunc(x/d +
+// 8.5)).  Returns the fp16 bits of d (the same in all lanes of the half).
+__device__ __forceinline__ uint32_t q4_block(float x, uint32_t* code) {
+  const uint32_t b = __float_as_uint(x);
+  uint32_t key = (b << 1) | ((~b) >> 31);
+  key = max(key, dpp<0xB1>(key));   // quad [1,0,3,2]
+  key = max(key, dpp<0x4E>(key));   // quad [2,3,0,1]
+  key = max(key, dpp<0x141>(key));  // half-row mirror: quad pairs
+  key = max(key, dpp<0x140>(key));  // row mirror: half-row pairs
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(key, key, false, false);
+    key = max(r[0], r[1]);
   }
-  if (a == 0.0f) m = 0.0f;  // an all-zero block keeps the initial +0 of the scan
+  // an all-zero block keeps the initial +0 of the scan
+  const float m = (key >> 1) == 0 ? 0.0f : __uint_as_float((key >> 1) | ((~key) << 31));
   const float d = m / -8.0f;
   const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
   const float u = x * id + 8.5f;
   int c = (int)u;
   c = c > 15 ? 15 : c;
-  *code_lds = (uint8_t)c;
+  *code = (uint32_t)c;
   return f2h(d);
 }
 
-__device__ __forceinline__ uint32_t pack4_word(const uint8_t* c, int w) {
+// OR of t over the lanes of each quad / 16-lane row / 32-lane half; every
+// lane of the group ends with the result.
+__device__ __forceinline__ uint32_t or_quad(uint32_t t) {
+  t |= dpp<0xB1>(t);
+  t |= dpp<0x4E>(t);
+  return t;
+}
+__device__ __forceinline__ uint32_t or_row(uint32_t t) {
+  t = or_quad(t);
+  t |= dpp<0x141>(t);  // half-row mirror: quad pairs
+  t |= dpp<0x140>(t);  // row mirror: half-row pairs
+  return t;
+}
+__device__ __forceinline__ uint32_t or_half(uint32_t t) {
+  t = or_row(t);
+  const auto r = __builtin_amdgcn_permlane16_swap(t, t, false, false);
+  return r[0] | r[1];
+}
+
+// [OCT] _pack of one register of codes (64 consecutive codes of a segment).
+// 4-bit: word k holds codes 8k .. 8k+7, byte j = code 8k+j | code 8k+4+j << 4;
+// lane 8k ends with word k.
+__device__ __forceinline__ uint32_t pack4_lanes(uint32_t c) {
+  const int lane = lane_id();
+  uint32_t n = c | (xor_u32(c, 4) << 4);
+  n = (lane & 4) ? 0u : n << (8 * (lane & 3));
+  return or_quad(n);
+}
+// 3-bit, low two bits: word k holds codes 16k .. 16k+15, code 16k + 4i + j at
+// bits 8j + 2i; lane 16k ends with word k.
+__device__ __forceinline__ uint32_t pack3_lo_lanes(uint32_t c) {
+  const int lane = lane_id();
+  return or_row((c & 3u) << (2 * ((lane >> 2) & 3) + 8 * (lane & 3)));
+}
+// 3-bit, high bit: word h holds codes 32h .. 32h+31, code 32h + 4i + j at bit
+// 8j + i; lane 32h ends with word h.
+__device__ __forceinline__ uint32_t pack3_hi_lanes(uint32_t c) {
+  const int lane = lane_id();
+  return or_half(((c >> 2) & 1u) << (((lane >> 2) & 7) + 8 * (lane & 3)));
+}
+
+// Q4_0 row: FWHT over the head, 32-value blocks, codes K | V | scales.  The
+// words are formed first and stored at the end (lane 8k holds word k of its
+// register), so the row is one straight-line block.
+template <int E>
+__device__ __forceinline__ void q4_row(const DevFmt& f, float (&k)[E], float (&v)[E],
+                                       uint32_t* dst) {
+  const int lane = lane_id();
+  fwht_strided<E>(k, f.k_block, f.k_norm);
+  fwht_strided<E>(v, f.v_block, f.v_norm);
+  uint32_t wk[E], wv[E];
   uint32_t word = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    word |= (uint32_t)((c[8 * w + j] & 15) | ((c[8 * w + 4 + j] & 15) << 4)) << (8 * j);
-  return word;
-}
-
-// Word at byte offset o of a 3-bit segment of n codes.
-__device__ __forceinline__ uint32_t pack3_word(const uint8_t* c, int n, int o) {
-  uint32_t word = 0;
-  if (o < n / 4) {
-    const int m = o / 4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t b = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) b |= (uint32_t)(c[16 * m + 4 * i + j] & 3) << (2 * i);
-      word |= b << (8 * j);
-    }
-  } else {
-    const int m = (o - n / 4) / 4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t b = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) b |= (uint32_t)((c[32 * m + 4 * i + j] >> 2) & 1) << i;
-      word |= b << (8 * j);
-    }
+  for (int e = 0; e < E; ++e) {
+    uint32_t ck, cv;
+    const uint32_t sk = q4_block(k[e], &ck);
+    const uint32_t sv = q4_block(v[e], &cv);
+    wk[e] = pack4_lanes(ck);
+    wv[e] = pack4_lanes(cv);
+    // Scale word e pairs the blocks of register e (lower half first); K
+    // words then V words; lane q writes word q.
+    const auto rk = __builtin_amdgcn_permlane32_swap(sk, sk, false, false);
+    const auto rv = __builtin_amdgcn_permlane32_swap(sv, sv, false, false);
+    word = (lane == e) ? (rk[0] | (rk[1] << 16)) : word;
+    word = (lane == E + e) ? (rv[0] | (rv[1] << 16)) : word;
   }
-  return word;
-}
-
-template <int E>
-__device__ __forceinline__ void load_row(const void* src, bool f16, int64_t row, float (&x)[E]) {
-  const int lane = lane_id();
-  if (f16) {
-    const uint16_t* p = (const uint16_t*)src + row * (E * kWave);
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = h2f(p[kWave * e + lane]);
-  } else {
-    const float* p = (const float*)src + row * (E * kWave);
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = p[kWave * e + lane];
-  }
-}
-
-template <int E>
-__global__ __launch_bounds__(64) void quantize_append_kernel(DevFmt f, const void* key,
-                                                             const void* value, int in_f16,
-                                                             int num_kv_heads,
-                                                             const int64_t* slot_mapping,
-                                                             uint8_t* cache) {
-  const int64_t row = blockIdx.x;
-  const int64_t t = row / num_kv_heads;
-  const int h = (int)(row % num_kv_heads);
-  const int64_t sm = slot_mapping[t];
-  if (sm < 0) return;
-  const int lane = lane_id();
-  __shared__ uint8_t kc[E * kWave];
-  __shared__ uint8_t vc[E * kWave];
-  __shared__ uint16_t sc[2 * kMaxHead / 32 + 2];
-
-  float k[E], v[E];
-  load_row<E>(key, in_f16 != 0, row, k);
-  load_row<E>(value, in_f16 != 0, row, v);
-  if (f.use_signs) {
+  if ((lane & 7) == 0) {
+    uint32_t* pk = dst + (lane >> 3);
+    uint32_t* pv = dst + f.off_v / 4 + (lane >> 3);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      k[e] = apply_sign(f, k[e], kWave * e + lane);
-      v[e] = apply_sign(f, v[e], kWave * e + lane);
+      pk[8 * e] = wk[e];
+      pv[8 * e] = wv[e];
     }
+  }
+  if (lane < 2 * E) dst[f.off_scales / 4 + lane] = word;
+}
+
+// Octave row: sign flips, FWHT (64-blocks or the whole head), per-block
+// Lloyd-Max codes; K codes (4-bit RoPE registers, then the 3-bit rest), V
+// codes, then the fp16 scales (K scales, V scale, zero padding).  Word
+// layout per register of a segment: 4-bit codes take 8 words (lane 8k holds
+// word k); 3-bit codes 4 low-bit words (lane 16k holds word k) and, after
+// all low words of the segment, 2 high-bit words (lane 32h holds word h).
+template <int E>
+__device__ __forceinline__ void octave_row(const DevFmt& f, float (&k)[E], float (&v)[E],
+                                           uint32_t* dst) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    k[e] = apply_sign(f, k[e], kWave * e + lane);
+    v[e] = apply_sign(f, v[e], kWave * e + lane);
   }
   fwht_strided<E>(k, f.k_block, f.k_norm);
   fwht_strided<E>(v, f.v_block, f.v_norm);
+  uint32_t ck[E], cv[E], ks[E];
+  const int kw = f.k_wide / kWave;  // registers of 4-bit K codes
+  if (f.compact) {
+    ks[0] = octave_block<E, 3>(k, 0, E, ck);
+#pragma unroll
+    for (int e = 1; e < E; ++e) ks[e] = 0;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      ks[e] = (e < kw) ? octave_block<E, 4>(k, e, 1, ck) : octave_block<E, 3>(k, e, 1, ck);
+  }
+  const bool v4 = f.v_bits == 4;
+  const uint32_t vs = v4 ? octave_block<E, 4>(v, 0, E, cv) : octave_block<E, 3>(v, 0, E, cv);
+  // Scale i: K scales first, then the V scale, then zeros; word q holds
+  // scales 2q and 2q+1.
+  const int nks = f.num_k_scales;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i <= E; ++i) {
+    const uint32_t sc = (i < nks) ? ks[i < E ? i : 0] : (i == nks ? vs : 0u);
+    word |= (lane == (i >> 1)) ? (sc << (16 * (i & 1))) : 0u;
+  }
+  // 4-bit words (or 3-bit low words) and 3-bit high words per register.
+  uint32_t k4[E], khi[E], v4w[E], vhi[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    k4[e] = (e < kw) ? pack4_lanes(ck[e]) : pack3_lo_lanes(ck[e]);
+    khi[e] = (e < kw) ? 0u : pack3_hi_lanes(ck[e]);
+    v4w[e] = v4 ? pack4_lanes(cv[e]) : pack3_lo_lanes(cv[e]);
+    vhi[e] = v4 ? 0u : pack3_hi_lanes(cv[e]);
+  }
+  const int wk3 = f.off_k_nope / 4, nk3 = kWave * (E - kw);
+  const int wv0 = f.off_v / 4;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e < kw) {
+      if ((lane & 7) == 0) dst[8 * e + (lane >> 3)] = k4[e];
+    } else {
+      if ((lane & 15) == 0) dst[wk3 + 4 * (e - kw) + (lane >> 4)] = k4[e];
+      if ((lane & 31) == 0) dst[wk3 + nk3 / 16 + 2 * (e - kw) + (lane >> 5)] = khi[e];
+    }
+    if (v4) {
+      if ((lane & 7) == 0) dst[wv0 + 8 * e + (lane >> 3)] = v4w[e];
+    } else {
+      if ((lane & 15) == 0) dst[wv0 + 4 * e + (lane >> 4)] = v4w[e];
+      if ((lane & 31) == 0) dst[wv0 + kWave * E / 16 + 2 * e + (lane >> 5)] = vhi[e];
+    }
+  }
+  if (lane < (f.slot_bytes - f.off_scales) / 4) dst[f.off_scales / 4 + lane] = word;
+}
 
-  if (f.kind == HKV_KIND_Q4_0) {
+template <int E, bool F16>
+__device__ __forceinline__ void fetch_row(const void* key, const void* value, int row,
+                                          uint32_t (&rk)[E], uint32_t (&rv)[E]) {
+  const int lane = lane_id();
+  const int64_t base = (int64_t)row * (E * kWave) + lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (F16) {
+      rk[e] = ((const uint16_t*)key)[base + kWave * e];
+      rv[e] = ((const uint16_t*)value)[base + kWave * e];
+    } else {
+      rk[e] = ((const uint32_t*)key)[base + kWave * e];
+      rv[e] = ((const uint32_t*)value)[base + kWave * e];
+    }
+  }
+}
+
+constexpr int kQuantWaves = 4;        // waves per workgroup
+constexpr int kQuantMaxGroups = 2048; // 8 workgroups per CU on 256 CUs
+
+// rows = num_tokens * num_kv_heads (below 2^31 less one grid stride);
+// row = token * num_kv_heads + head.
+template <int E, bool F16, bool Q4>
+__global__ __launch_bounds__(kQuantWaves * kWave) void quantize_append_kernel(
+    DevFmt f, const void* key, const void* value, int rows, int num_kv_heads,
+    const int64_t* slot_mapping, uint8_t* cache) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int stride = (int)gridDim.x * kQuantWaves;
+  int row = (int)blockIdx.x * kQuantWaves + wave;
+  if (row >= rows) return;
+  uint32_t rk[E], rv[E];
+  fetch_row<E, F16>(key, value, row, rk, rv);
+  int64_t sm = slot_mapping[row / num_kv_heads];
+  for (;;) {
+    float k[E], v[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int blk = 2 * e + (lane >> 5);
-      const uint16_t dk = q4_block(k[e], &kc[kWave * e + lane]);
-      const uint16_t dv = q4_block(v[e], &vc[kWave * e + lane]);
-      if ((lane & 31) == 0) {
-        sc[blk] = dk;
-        sc[2 * E + blk] = dv;
+      k[e] = F16 ? h2f((uint16_t)rk[e]) : __uint_as_float(rk[e]);
+      v[e] = F16 ? h2f((uint16_t)rv[e]) : __uint_as_float(rv[e]);
+    }
+    const int cur = row;
+    const int64_t cur_sm = sm;
+    row += stride;
+    if (row < rows) {  // the next row's loads are in flight during this one
+      fetch_row<E, F16>(key, value, row, rk, rv);
+      sm = slot_mapping[row / num_kv_heads];
+    }
+    if (cur_sm >= 0) {
+      int64_t page;
+      int off;
+      if ((cur_sm >> 32) == 0) {  // 32-bit division when the slot index fits
+        const uint32_t s32 = (uint32_t)cur_sm;
+        page = s32 / (uint32_t)f.page_size;
+        off = (int)(s32 % (uint32_t)f.page_size);
+      } else {
+        page = cur_sm / f.page_size;
+        off = (int)(cur_sm % f.page_size);
       }
+      uint32_t* dst =
+          (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, cur % num_kv_heads);
+      if (Q4) q4_row<E>(f, k, v, dst);
+      else octave_row<E>(f, k, v, dst);
+    }
+    if (row >= rows) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Q4_0 quantize-append for many rows: 16 lanes per row, four rows per wave.
+// Lane l of a 16-lane row holds elements 64q + 4l + i (i = 0..3) of its row
+// for each 64-wide group q, so the element index bits 0-1 live in a
+// register, bits 2-5 in the lane (exchanges stay inside the 16-lane DPP
+// row), bits 6-7 in q.  The butterfly stages still run in ascending stride
+// (1, 2 in registers; 4..32 across lanes; 64, 128 in registers), each as the
+// same (a + b, a - b) pair, so the bytes equal those of the kernel above.
+// A 32-value block is one q of one 8-lane half-row.
+
+template <int Q>
+__device__ __forceinline__ void fwht_rows16(float (&x)[Q][4], float norm) {
+  const int l = lane_id() & 15;
+  // h = 1, 2: registers
+#pragma unroll
+  for (int h = 1; h <= 2; h <<= 1)
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((i & h) == 0) {
+          const float a = x[q][i], b = x[q][i + h];
+          x[q][i] = a + b;
+          x[q][i + h] = a - b;
+        }
+  // h = 4 .. 32: lane strides 1 .. 8 inside the 16-lane row
+#pragma unroll
+  for (int m = 1; m <= 8; m <<= 1) {
+    const float sgn = (l & m) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[q][i] = fmaf(x[q][i], sgn, shfl_xor(x[q][i], m));
+  }
+  // h = 64, 128: register groups
+#pragma unroll
+  for (int hq = 1; hq < Q; hq <<= 1)
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if ((q & hq) == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = x[q][i], b = x[q + hq][i];
+          x[q][i] = a + b;
+          x[q + hq][i] = a - b;
+        }
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * norm;
+}
+
+// One 64-wide group: codes packed into the words of this lane pair and the
+// fp16 scales of its two blocks.  On return `word` (even lanes) is slot word
+// 8q + l/2 of the segment and `scale` (lanes 0-7 of the row) is the scale
+// word of the group (block 2q | block 2q+1 << 16).
+__device__ __forceinline__ void q4_group16(const float (&x)[4], uint32_t* word,
+                                           uint32_t* scale) {
+  uint32_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = __float_as_uint(x[i]);
+    key[i] = (b << 1) | ((~b) >> 31);  // (|x| bits, x >= 0): see q4_block
+  }
+  uint32_t kmax = max(max(key[0], key[1]), max(key[2], key[3]));
+  kmax = max(kmax, dpp<0xB1>(kmax));   // quad [1,0,3,2]
+  kmax = max(kmax, dpp<0x4E>(kmax));   // quad [2,3,0,1]
+  kmax = max(kmax, dpp<0x141>(kmax));  // half-row mirror: the 8 lanes of the block
+  const float m = (kmax >> 1) == 0 ? 0.0f : __uint_as_float((kmax >> 1) | ((~kmax) << 31));
+  const float d = m / -8.0f;
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  uint32_t c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float u = x[i] * id + 8.5f;
+    const int ci = (int)u;
+    c[i] = (uint32_t)(ci > 15 ? 15 : ci);
+  }
+  // bytes of this lane's four codes; the odd lane's go to the high nibbles
+  const uint32_t bytes = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  *word = bytes | (dpp<0xB1>(bytes) << 4);
+  const uint32_t h = f2h(d);
+  *scale = h | (dpp<0x128>(h) << 16);  // row_ror:8 -> the other block's scale
+}
+
+template <int Q, bool F16>
+__device__ __forceinline__ void fetch_rows16(const void* key, const void* value, int row,
+                                             uint32_t (&rk)[Q][F16 ? 2 : 4],
+                                             uint32_t (&rv)[Q][F16 ? 2 : 4]) {
+  const int l = lane_id() & 15;
+  constexpr int D = 64 * Q;
+  if (F16) {
+    const uint2* pk = (const uint2*)((const uint16_t*)key + (int64_t)row * D + 4 * l);
+    const uint2* pv = (const uint2*)((const uint16_t*)value + (int64_t)row * D + 4 * l);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const uint2 a = pk[16 * q], b = pv[16 * q];
+      rk[q][0] = a.x, rk[q][1] = a.y;
+      rv[q][0] = b.x, rv[q][1] = b.y;
     }
   } else {
-    if (f.compact) {
-      const uint16_t s = octave_block<E, 3>(k, 0, E, kc);
-      if (lane == 0) sc[0] = s;
+    const uint4* pk = (const uint4*)((const float*)key + (int64_t)row * D + 4 * l);
+    const uint4* pv = (const uint4*)((const float*)value + (int64_t)row * D + 4 * l);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const uint4 a = pk[16 * q], b = pv[16 * q];
+      rk[q][0] = a.x, rk[q][1] = a.y, rk[q][2] = a.z, rk[q][3] = a.w;
+      rv[q][0] = b.x, rv[q][1] = b.y, rv[q][2] = b.z, rv[q][3] = b.w;
+    }
+  }
+}
+
+template <int Q, bool F16>
+__device__ __forceinline__ void widen16(const uint32_t (&r)[Q][F16 ? 2 : 4], float (&x)[Q][4]) {
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    if (F16) {
+      x[q][0] = h2f((uint16_t)r[q][0]);
+      x[q][1] = h2f((uint16_t)(r[q][0] >> 16));
+      x[q][2] = h2f((uint16_t)r[q][1]);
+      x[q][3] = h2f((uint16_t)(r[q][1] >> 16));
     } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const uint16_t s = (kWave * e < f.k_wide) ? octave_block<E, 4>(k, e, 1, kc)
-                                                   : octave_block<E, 3>(k, e, 1, kc);
-        if (lane == 0) sc[e] = s;
-      }
+      for (int i = 0; i < 4; ++i) x[q][i] = __uint_as_float(r[q][i]);
     }
-    const uint16_t s = (f.v_bits == 4) ? octave_block<E, 4>(v, 0, E, vc)
-                                       : octave_block<E, 3>(v, 0, E, vc);
-    if (lane == 0) sc[f.num_k_scales] = s;
   }
-  __syncthreads();
+}
 
-  const int64_t page = sm / f.page_size;
-  const int off = (int)(sm % f.page_size);
-  uint32_t* dst = (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, h);
-  const int D = E * kWave;
-  for (int w = lane; w < f.slot_bytes / 4; w += kWave) {
-    const int o = 4 * w;
-    uint32_t word;
-    if (o < f.off_k_nope) {
-      word = pack4_word(kc, w);
-    } else if (o < f.off_v) {
-      word = pack3_word(kc + f.k_wide, D - f.k_wide, o - f.off_k_nope);
-    } else if (o < f.off_scales) {
-      word = (f.kind == HKV_KIND_Q4_0 || f.v_bits == 4) ? pack4_word(vc, (o - f.off_v) / 4)
-                                                        : pack3_word(vc, D, o - f.off_v);
-    } else {
-      const int i = (o - f.off_scales) / 2;
-      const uint32_t lo = i < f.num_scales ? sc[i] : 0u;
-      const uint32_t hi = i + 1 < f.num_scales ? sc[i + 1] : 0u;
-      word = lo | (hi << 16);
+constexpr int kRows16MinRows = 4096;  // below this the one-row-per-wave kernel is faster
+
+// rows as for quantize_append_kernel; key/value 8-byte (f16) or 16-byte (f32)
+// aligned.
+template <int Q, bool F16>
+__global__ __launch_bounds__(kQuantWaves * kWave) void quantize_q4_rows16_kernel(
+    DevFmt f, const void* key, const void* value, int rows, int num_kv_heads,
+    const int64_t* slot_mapping, uint8_t* cache) {
+  constexpr int R = F16 ? 2 : 4;
+  const int lane = lane_id();
+  const int l = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int stride = (int)gridDim.x * kQuantWaves * 4;
+  int base = ((int)blockIdx.x * kQuantWaves + wave) * 4;
+  if (base >= rows) return;
+  uint32_t rk[Q][R], rv[Q][R];
+  int row = base + (lane >> 4);
+  fetch_rows16<Q, F16>(key, value, min(row, rows - 1), rk, rv);
+  int64_t sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
+  for (;;) {
+    float k[Q][4], v[Q][4];
+    widen16<Q, F16>(rk, k);
+    widen16<Q, F16>(rv, v);
+    const int cur = row;
+    const int64_t cur_sm = sm;
+    base += stride;
+    row += stride;
+    if (base < rows) {  // the next four rows load during this group
+      fetch_rows16<Q, F16>(key, value, min(row, rows - 1), rk, rv);
+      sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
     }
-    dst[w] = word;
+    fwht_rows16<Q>(k, f.k_norm);
+    fwht_rows16<Q>(v, f.v_norm);
+    uint32_t wk[Q], wv[Q], sk[Q], sv[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      q4_group16(k[q], &wk[q], &sk[q]);
+      q4_group16(v[q], &wv[q], &sv[q]);
+    }
+    // scale words: lanes 0..Q-1 the K words, Q..2Q-1 the V words
+    uint32_t sw = sk[0];
+#pragma unroll
+    for (int q = 1; q < Q; ++q) sw = (l == q) ? sk[q] : sw;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) sw = (l == Q + q) ? sv[q] : sw;
+    if (cur_sm >= 0) {
+      int64_t page;
+      int off;
+      if ((cur_sm >> 32) == 0) {
+        const uint32_t s32 = (uint32_t)cur_sm;
+        page = s32 / (uint32_t)f.page_size;
+        off = (int)(s32 % (uint32_t)f.page_size);
+      } else {
+        page = cur_sm / f.page_size;
+        off = (int)(cur_sm % f.page_size);
+      }
+      uint32_t* dst =
+          (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, cur % num_kv_heads);
+      if ((l & 1) == 0) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          dst[8 * q + (l >> 1)] = wk[q];
+          dst[f.off_v / 4 + 8 * q + (l >> 1)] = wv[q];
+        }
+      }
+      if (l < 2 * Q) dst[f.off_scales / 4 + l] = sw;
+    }
+    if (base >= rows) break;
   }
 }
 
@@ -301,14 +590,54 @@ hipError_t launch_quantize_append(const DevFmt& f, const void* key, const void* 
                                   const int64_t* slot_mapping, uint8_t* cache, hipStream_t s) {
   const int64_t rows = num_tokens * num_kv_heads;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows), block(kWave);
+  // row indices are int; row + grid stride (at most 4 rows per wave) must not overflow
+  if (rows > INT32_MAX - 4 * kQuantMaxGroups * kQuantWaves) return hipErrorInvalidValue;
+  const int64_t groups = (rows + kQuantWaves - 1) / kQuantWaves;
+  const dim3 grid((unsigned)(groups < kQuantMaxGroups ? groups : kQuantMaxGroups));
+  const dim3 block(kQuantWaves * kWave);
+  const int r = (int)rows;
+  const bool q4 = f.kind == HKV_KIND_Q4_0;
+  const uintptr_t align = in_f16 ? 8 : 16;
+  if (q4 && rows >= kRows16MinRows && ((uintptr_t)key % align) == 0 &&
+      ((uintptr_t)value % align) == 0) {
+    const int64_t g16 = (rows + 4 * kQuantWaves - 1) / (4 * kQuantWaves);
+    const dim3 grid16((unsigned)(g16 < kQuantMaxGroups ? g16 : kQuantMaxGroups));
+#define HKV_Q16(Q_)                                                                          \
+  (in_f16 ? (quantize_q4_rows16_kernel<Q_, true><<<grid16, block, 0, s>>>(                   \
+                f, key, value, r, num_kv_heads, slot_mapping, cache))                        \
+          : (quantize_q4_rows16_kernel<Q_, false><<<grid16, block, 0, s>>>(                  \
+                f, key, value, r, num_kv_heads, slot_mapping, cache)))
+    switch (f.D / kWave) {
+      case 1: HKV_Q16(1); break;
+      case 2: HKV_Q16(2); break;
+      case 4: HKV_Q16(4); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef HKV_Q16
+    return hipGetLastError();
+  }
+#define HKV_QA1(E_, F16_, Q4_)                                                         \
+  quantize_append_kernel<E_, F16_, Q4_><<<grid, block, 0, s>>>(f, key, value, r, num_kv_heads, \
+                                                               slot_mapping, cache)
+#define HKV_QA(E_)                               \
+  do {                                           \
+    if (q4) {                                    \
+      if (in_f16) HKV_QA1(E_, true, true);       \
+      else HKV_QA1(E_, false, true);             \
+    } else {                                     \
+      if (in_f16) HKV_QA1(E_, true, false);      \
+      else HKV_QA1(E_, false, false);            \
+    }                                            \
+  } while (0)
   switch (f.D / kWave) {
-    case 1: quantize_append_kernel<1><<<grid, block, 0, s>>>(f, key, value, in_f16, num_kv_heads, slot_mapping, cache); break;
-    case 2: quantize_append_kernel<2><<<grid, block, 0, s>>>(f, key, value, in_f16, num_kv_heads, slot_mapping, cache); break;
-    case 3: quantize_append_kernel<3><<<grid, block, 0, s>>>(f, key, value, in_f16, num_kv_heads, slot_mapping, cache); break;
-    case 4: quantize_append_kernel<4><<<grid, block, 0, s>>>(f, key, value, in_f16, num_kv_heads, slot_mapping, cache); break;
+    case 1: HKV_QA(1); break;
+    case 2: HKV_QA(2); break;
+    case 3: HKV_QA(3); break;
+    case 4: HKV_QA(4); break;
     default: return hipErrorInvalidValue;
   }
+#undef HKV_QA
+#undef HKV_QA1
   return hipGetLastError();
 }
 

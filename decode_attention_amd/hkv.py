@@ -54,6 +54,8 @@ _lib = None
 def lib():
     """Load libhkv.so (raises if it has not been built)."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB_PATH):
@@ -192,9 +194,10 @@ def decode_attention(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
     if out is None:
         out = torch.empty((Q, Hq, D), dtype=torch.float32, device=query.device)
     _need(out, "out", dtype=torch.float32, dims=3)
-    need = decode_workspace_bytes(fmt, Q, Hq, Hkv, max_klen, queries_per_seq)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    if workspace is None:  # a caller's workspace is size-checked by the library
+        need = decode_workspace_bytes(fmt, Q, Hq, Hkv, max_klen, queries_per_seq)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hkv_decode_attention(
         ctypes.byref(fmt), _ptr(query), _dtype_code(query), Q, Hq, Hkv, _ptr(cache),

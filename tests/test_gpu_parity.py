@@ -114,6 +114,50 @@ def test_quantize_and_dequantize_formats(dtype, D, R, in_dtype):
         assert np.all(kd[~keep] == 0) and np.all(vd[~keep] == 0)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("in_dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("misaligned", [False, True])
+def test_quantize_q4_many_rows(D, in_dtype, misaligned):
+    """Row counts that take the many-rows Q4_0 kernel (16 lanes per row, four
+    rows per wave; a ragged last wave, skipped slots); a key/value pointer
+    off its 8/16-byte alignment takes the one-row-per-wave kernel instead.
+    Both must give the oracle's bytes."""
+    rng = np.random.default_rng(7 * D + (3 if misaligned else 0))
+    T, H, P = 1501, 3, 16                              # 4503 rows = 281 waves of 16 + 7
+    k = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
+    v = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
+    k[5] = 0
+    v[9, 2] = 0
+    k[11, 1, :32] = -np.abs(k[11, 1, :32]).max()     # max-abs ties inside one block
+    k[11, 1, 3] = -k[11, 1, 3]
+    f = hkv.format_init("q4_0", D, 0, P)
+    fo = O.format_init("q4_0", D, 0)
+    pages = (T + P - 1) // P + 2
+    sm = rng.permutation(pages * P)[:T].astype(np.int64)
+    sm[[0, 17, T - 1]] = -1
+    cache = hkv.new_cache(f, pages, H, DEV)
+    cache.fill_(0xA5)
+
+    def dev(a):
+        t = torch.from_numpy(a).to(DEV)
+        if not misaligned:
+            return t
+        buf = torch.empty(a.size + 1, dtype=t.dtype, device=DEV)
+        buf[1:] = t.reshape(-1)
+        return buf[1:].view(a.shape)
+    kt, vt = dev(k), dev(v)
+    assert (kt.data_ptr() % 16 != 0) == misaligned
+    hkv.quantize_append(f, kt, vt, torch.from_numpy(sm).to(DEV), cache)
+    got = cache.cpu().numpy()
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    keep = sm >= 0
+    assert np.array_equal(got[sm[keep] // P, :, sm[keep] % P], slots[keep])
+    untouched = np.ones(pages * P, bool)
+    untouched[sm[keep]] = False
+    flat = got.transpose(0, 2, 1, 3).reshape(pages * P, H, -1)
+    assert np.all(flat[untouched] == 0xA5)
+
+
 @pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
 def test_decode_matches_oracle(ci):
     cfg = W.CONFIGS[ci]
