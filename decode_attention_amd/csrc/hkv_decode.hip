@@ -267,12 +267,15 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DevFmt f, DecArgs a
 
 // Merge the split partials of one (query, head) row, normalise, rotate the
 // output back (transform with the V block, then the signs) and store fp32.
-// One workgroup per row; wave w takes splits w, w + kMergeWaves, ...  Only
+// One workgroup per row; wave w takes splits w, w + kMergeWaves, ... in
+// chunks of kMergeChunk, loading the (m, l) pair and o of every split of a
+// chunk together (one memory round trip per chunk), and keeps a running
+// (M, L, acc) in the exp2 domain; the waves then combine through LDS.  Only
 // the splits that start below the row's own klen are visited: each of those
 // holds at least one of the row's tokens, so its whole record was written and
-// is finite, and no split is skipped by a data-dependent branch (which would
-// serialise the loads).
+// is finite.
 constexpr int kMergeWaves = 8;
+constexpr int kMergeChunk = 4;
 
 template <int E>
 __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, DecArgs a,
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   constexpr int D = E * kWave;
   __shared__ float red[kMergeWaves][D + 2];
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t rowid = blockIdx.x;
   const int i = (int)(rowid / a.num_q_heads);
   const int h = (int)(rowid % a.num_q_heads);
@@ -291,44 +294,66 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   const int klen = a.q_to_klen[i];
   const int n_live = klen <= 0 ? 0 : min(a.num_splits, (klen + a.tokens_per_split - 1) /
                                                            a.tokens_per_split);
-  const float* base = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride;
+  const float* base = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride +
+                      (size_t)r * a.pstride;
   const size_t sstride = (size_t)Rp * a.pstride;
-  // Global max of the split maxima.
-  float M = -INFINITY;
-  for (int s = threadIdx.x; s < n_live; s += blockDim.x) M = fmaxf(M, base[s * sstride + r * a.pstride]);
-  M = wave_max(M);
-  if (lane == 0) red[wave][0] = M;
-  __syncthreads();
-  M = red[0][0];
-#pragma unroll
-  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, red[w][0]);
-  __syncthreads();
-  float L = 0.0f, acc[E];
+  float M = -INFINITY, L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  const float* pr = base + (size_t)r * a.pstride + kPartialHead + lane;
-#pragma unroll 4
-  for (int s = wave; s < n_live; s += kMergeWaves) {
-    const float* ps = pr + s * sstride;
-    const float w = exp2f(ps[-kPartialHead - lane] - M);
-    L = fmaf(ps[1 - kPartialHead - lane], w, L);
+  for (int s0 = wave; s0 < n_live; s0 += kMergeWaves * kMergeChunk) {
+    float2 ml[kMergeChunk];
+    float o[kMergeChunk][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = fmaf(ps[kWave * e], w, acc[e]);
+    for (int c = 0; c < kMergeChunk; ++c) {
+      // a split past the end reloads the first one with a zero weight
+      const int s = s0 + kMergeWaves * c;
+      const float* ps = base + (s < n_live ? s : s0) * sstride;
+      ml[c] = *(const float2*)ps;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[c][e] = ps[kPartialHead + kWave * e + lane];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c)
+      if (s0 + kMergeWaves * c < n_live) Mc = fmaxf(Mc, ml[c].x);
+    const float alpha = exp2f(M - Mc);  // M = -inf before the first chunk: 0
+    L *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c) {
+      const float w = s0 + kMergeWaves * c < n_live ? exp2f(ml[c].x - Mc) : 0.0f;
+      L = fmaf(ml[c].y, w, L);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(o[c][e], w, acc[e]);
+    }
+    M = Mc;
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) red[wave][kWave * e + lane] = acc[e];
-  if (lane == 0) red[wave][D] = L;
+  if (lane == 0) {
+    red[wave][D] = M;
+    red[wave][D + 1] = L;
+  }
   __syncthreads();
   if (wave != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, red[w][D]);
+  float fw[kMergeWaves];
   L = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kMergeWaves; ++w) L += red[w][D];
+  for (int w = 0; w < kMergeWaves; ++w) {
+    const float mw = red[w][D];
+    fw[w] = mw == -INFINITY ? 0.0f : exp2f(mw - Mt);
+    L = fmaf(red[w][D + 1], fw[w], L);
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int d = kWave * e + lane;
     float t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) t += red[w][d];
+    for (int w = 0; w < kMergeWaves; ++w) t = fmaf(red[w][d], fw[w], t);
     acc[e] = t;
   }
   const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
