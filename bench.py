@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--cpu-threads", type=int, default=0)
     p.add_argument("--profile", action="store_true",
                    help="short run for a profiler: no CPU baseline")
+    p.add_argument("--op", choices=["decode", "hadamard"], default="decode",
+                   help="decode: the quantize-append + decode step (default); hadamard: the "
+                        "standalone blockwise rotation on an activation-shaped tensor")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of 256 MiB (calibrates the HBM "
                         "byte counters of rocprofv3)")
@@ -146,6 +149,71 @@ def cpu_baseline(cfg, w, threads: int, scale: float, min_seconds: float = 10.0):
                        f"{n_threads} threads (one per sequence)")}
 
 
+HAD_ROWS, HAD_N, HAD_BLOCK = 16384, 4096, 128
+
+
+def hadamard_bench(args):
+    """One step = hkv_hadamard (block 128, sign pattern, rotate) over a
+    (16384, 4096) f16 activation tensor into fp32."""
+    import torch
+    from decode_attention_amd import hkv
+    rng = np.random.default_rng(4242)
+    x = rng.standard_normal((HAD_ROWS, HAD_N), dtype=np.float32).astype(np.float16)
+    bits = rng.integers(-2**31, 2**31, HAD_N // 32, dtype=np.int64).astype(np.int32)
+    dev = torch.device("cuda:0")
+    xt, bt = torch.from_numpy(x).to(dev), torch.from_numpy(bits).to(dev)
+    y = torch.empty((HAD_ROWS, HAD_N), dtype=torch.float32, device=dev)
+    step = lambda: hkv.hadamard(xt, HAD_BLOCK, bt, False, out=y)
+    warm = 0.0 if args.profile else WARM_SECONDS
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warm:
+            break
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    nbytes = HAD_ROWS * HAD_N * (2 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    rec = {"metric": "hadamard rotation GB/s (f16 in + fp32 out)", "value": round(gbs, 3),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"hadamard_b{HAD_BLOCK}_{HAD_ROWS}x{HAD_N}", "rows": HAD_ROWS,
+                      "n": HAD_N, "block": HAD_BLOCK, "in": "f16", "out": "f32", "signs": True},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "hkv_hadamard", "bytes_per_call": nbytes,
+                        "us_per_call": round(ms * 1e3, 3)}}
+    if not args.no_cpu_baseline and not args.profile:
+        import oracle as O
+        n_rows, reps = 256, 0
+        xs = x[:n_rows].astype(np.float32)
+        s = (1 - 2 * ((bits.view(np.uint32)[np.arange(HAD_N) // 32] >> (np.arange(HAD_N) % 32)) & 1)
+             ).astype(np.float32)
+        t0 = time.perf_counter()
+        while True:
+            O.fwht(xs * s, HAD_BLOCK)
+            reps += 1
+            if time.perf_counter() - t0 >= 10.0:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        rec["cpu_baseline"] = {"value": round(n_rows * HAD_N * 6 / dt / 1e9, 6), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{n_rows} of the {HAD_ROWS} rows, {reps} passes, "
+                                         f"{dt * 1e3:.1f} ms per pass, one thread"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -153,8 +221,12 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md, not built).", file=sys.stderr)
+              "(the multi-GPU sharding is a design note, not built).", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "hadamard":
+        hadamard_bench(args)
+        return
 
     import torch
 

@@ -219,6 +219,36 @@ hkv_status hkv_dequantize(const hkv_format* f, const uint8_t* cache, int32_t num
   return e == hipSuccess ? HKV_OK : hip_fail(e, "dequantize launch");
 }
 
+hkv_status hkv_hadamard(const void* x, hkv_dtype in_dtype, float* y, int64_t rows, int32_t n,
+                        int32_t block, const uint32_t* sign_bits, int32_t inverse,
+                        void* stream) {
+  if (in_dtype != HKV_F32 && in_dtype != HKV_F16)
+    return fail(HKV_ERR_INVALID_ARG, "hadamard: bad input dtype %d", (int)in_dtype);
+  if (block != 64 && block != 128 && block != 256)
+    return fail(HKV_ERR_INVALID_ARG, "hadamard: block must be 64, 128 or 256, got %d", block);
+  if (rows < 0 || n <= 0 || n % block)
+    return fail(HKV_ERR_INVALID_ARG, "hadamard: rows=%lld n=%d (n a positive multiple of %d)",
+                (long long)rows, n, block);
+  if (rows == 0) return HKV_OK;
+  if (!x || !y) return fail(HKV_ERR_INVALID_ARG, "hadamard: NULL pointer");
+  if (!aligned(x, in_dtype == HKV_F16 ? 8 : 16) || !aligned(y, 16))
+    return fail(HKV_ERR_INVALID_ARG, "hadamard: x must be %d-byte and y 16-byte aligned",
+                in_dtype == HKV_F16 ? 8 : 16);
+  if (sign_bits && !aligned(sign_bits, 4))
+    return fail(HKV_ERR_INVALID_ARG, "hadamard: sign_bits must be 4-byte aligned");
+  const size_t esz = in_dtype == HKV_F16 ? 2 : 4;
+  const uintptr_t xb = (uintptr_t)x, xe = xb + (size_t)rows * n * esz;
+  const uintptr_t yb = (uintptr_t)y, ye = yb + (size_t)rows * n * 4;
+  const bool same = xb == yb && in_dtype == HKV_F32;
+  if (!same && xb < ye && yb < xe)
+    return fail(HKV_ERR_INVALID_ARG, "hadamard: x and y overlap (only y == x with f32 input)");
+  if (rows * (int64_t)(n / block) > ((int64_t)1 << 40))
+    return fail(HKV_ERR_UNSUPPORTED, "hadamard: too many blocks");
+  const hipError_t e = hkv::launch_hadamard(x, in_dtype == HKV_F16, y, rows, n, block, sign_bits,
+                                            inverse != 0, (hipStream_t)stream);
+  return e == hipSuccess ? HKV_OK : hip_fail(e, "hadamard launch");
+}
+
 size_t hkv_decode_workspace_bytes(const hkv_format* f, int32_t num_queries, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t max_klen,
                                   int32_t queries_per_seq) {

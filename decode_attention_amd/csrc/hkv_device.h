@@ -165,6 +165,55 @@ __device__ __forceinline__ void fwht_strided(float (&x)[E], int block, float nor
   for (int e = 0; e < E; ++e) x[e] = x[e] * norm;
 }
 
+// The same transform, for a block of 64Q values held 16 lanes to a block:
+// lane l of a 16-lane row holds elements 64q + 4l + i (i = 0..3), so index
+// bits 0-1 are in a register, bits 2-5 in the lane (exchanges stay inside the
+// 16-lane DPP row), bits 6-7 in q.  The stages still run in ascending stride
+// (1, 2 in registers; 4..32 across lanes; 64, 128 in registers), each as the
+// same (a + b, a - b) pair, so the values are bitwise those of fwht_strided.
+template <int Q>
+__device__ __forceinline__ void fwht_rows16(float (&x)[Q][4], float norm) {
+  const int l = lane_id() & 15;
+  // h = 1, 2: registers
+#pragma unroll
+  for (int h = 1; h <= 2; h <<= 1)
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((i & h) == 0) {
+          const float a = x[q][i], b = x[q][i + h];
+          x[q][i] = a + b;
+          x[q][i + h] = a - b;
+        }
+  // h = 4 .. 32: lane strides 1 .. 8 inside the 16-lane row
+#pragma unroll
+  for (int m = 1; m <= 8; m <<= 1) {
+    const float sgn = (l & m) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[q][i] = fmaf(x[q][i], sgn, shfl_xor(x[q][i], m));
+  }
+  // h = 64, 128: register groups
+#pragma unroll
+  for (int hq = 1; hq < Q; hq <<= 1)
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if ((q & hq) == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = x[q][i], b = x[q + hq][i];
+          x[q][i] = a + b;
+          x[q + hq][i] = a - b;
+        }
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * norm;
+}
+
+
 // Sum over the 64 lanes as a pairwise tree (strides 32, 16, ..., 1).  With
 // xor partners every lane ends with the same bits as the sequential tree
 // (a + b == b + a in IEEE arithmetic).

@@ -17,6 +17,9 @@ hipError_t launch_quantize_append(const DevFmt& f, const void* key, const void* 
                                   bool in_f16, int64_t num_tokens, int num_kv_heads,
                                   const int64_t* slot_mapping, uint8_t* cache, hipStream_t s);
 
+hipError_t launch_hadamard(const void* x, bool in_f16, float* y, int64_t rows, int n, int block,
+                           const uint32_t* sign_bits, bool inverse, hipStream_t s);
+
 hipError_t launch_dequantize(const DevFmt& f, const uint8_t* cache, int num_kv_heads,
                              const int64_t* slot_ids, int64_t num_tokens, bool rotated,
                              float* k_out, float* v_out, hipStream_t s);

@@ -344,48 +344,6 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_append_kernel(
 // same (a + b, a - b) pair, so the bytes equal those of the kernel above.
 // A 32-value block is one q of one 8-lane half-row.
 
-template <int Q>
-__device__ __forceinline__ void fwht_rows16(float (&x)[Q][4], float norm) {
-  const int l = lane_id() & 15;
-  // h = 1, 2: registers
-#pragma unroll
-  for (int h = 1; h <= 2; h <<= 1)
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if ((i & h) == 0) {
-          const float a = x[q][i], b = x[q][i + h];
-          x[q][i] = a + b;
-          x[q][i + h] = a - b;
-        }
-  // h = 4 .. 32: lane strides 1 .. 8 inside the 16-lane row
-#pragma unroll
-  for (int m = 1; m <= 8; m <<= 1) {
-    const float sgn = (l & m) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[q][i] = fmaf(x[q][i], sgn, shfl_xor(x[q][i], m));
-  }
-  // h = 64, 128: register groups
-#pragma unroll
-  for (int hq = 1; hq < Q; hq <<= 1)
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-      if ((q & hq) == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = x[q][i], b = x[q + hq][i];
-          x[q][i] = a + b;
-          x[q + hq][i] = a - b;
-        }
-#pragma unroll
-  for (int q = 0; q < Q; ++q)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * norm;
-}
-
 // One 64-wide group: codes packed into the words of this lane pair and the
 // fp16 scales of its two blocks.  On return `word` (even lanes) is slot word
 // 8q + l/2 of the segment and `scale` (lanes 0-7 of the row) is the scale

@@ -24,8 +24,8 @@ HKV_MAX_HEAD = 256
 
 # Names of the exported entry points (include/hkv.h).
 EXPORTS = ("hkv_format_init", "hkv_quantize_append", "hkv_dequantize",
-           "hkv_decode_workspace_bytes", "hkv_decode_attention", "hkv_last_error",
-           "hkv_version")
+           "hkv_decode_workspace_bytes", "hkv_decode_attention", "hkv_hadamard",
+           "hkv_last_error", "hkv_version")
 
 
 class HkvError(RuntimeError):
@@ -76,6 +76,8 @@ def lib():
                                                vp, i32, vp, vp, i32, i32, ctypes.c_float, vp, vp,
                                                ctypes.c_size_t, vp]
             L.hkv_decode_attention.restype = ctypes.c_int
+            L.hkv_hadamard.argtypes = [vp, ctypes.c_int, vp, i64, i32, i32, vp, i32, vp]
+            L.hkv_hadamard.restype = ctypes.c_int
             L.hkv_last_error.restype = ctypes.c_char_p
             L.hkv_version.restype = ctypes.c_char_p
             _lib = L
@@ -204,6 +206,30 @@ def decode_attention(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
         _ptr(block_table), block_table.shape[1], _ptr(q_to_req), _ptr(q_to_klen), int(max_klen),
         int(queries_per_seq), float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return out
+
+
+def hadamard(x: torch.Tensor, block: int = 128, sign_bits: Optional[torch.Tensor] = None,
+             inverse: bool = False, out: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """Blockwise orthonormal Walsh-Hadamard rotation over the last dim of x
+    (f32 or f16), fp32 result; sign_bits: None or an int32 device tensor of
+    n/32 words (bit set = element negated), applied before the transform, or
+    after it when inverse.  out may be x itself for f32 input."""
+    _need(x, "x")
+    n = x.shape[-1] if x.dim() else 0
+    rows = x.numel() // n if n else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _need(out, "out", dtype=torch.float32)
+    if tuple(out.shape) != tuple(x.shape):
+        raise ValueError("hadamard: out must have the shape of x")
+    if sign_bits is not None:
+        _need(sign_bits, "sign_bits", dtype=torch.int32, dims=1)
+        if sign_bits.numel() * 32 < n:
+            raise ValueError("hadamard: sign_bits needs n/32 words")
+    _check(lib().hkv_hadamard(_ptr(x), _dtype_code(x), _ptr(out), rows, n, int(block),
+                              _ptr(sign_bits), int(bool(inverse)), _stream(stream)))
     return out
 
 

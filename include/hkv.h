@@ -168,6 +168,29 @@ hkv_status hkv_decode_attention(const hkv_format* f /*host*/, const void* query,
                                 int32_t queries_per_seq, float sm_scale, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * hkv_hadamard -- blockwise orthonormal Walsh-Hadamard rotation of rows, the
+ * rotation of the cache formats as an operation of its own ([OCT]
+ * fwht_blocks, signs / sign_bits; the block-128 activation rotation of
+ * Strata pull request #928, "What's in it").
+ *   x:          (rows, n), in_dtype f32 or f16; 16-byte (f32) or 8-byte (f16)
+ *               aligned.  n is a positive multiple of block.
+ *   y:          (rows, n) fp32, 16-byte aligned.  y may be x itself (in place)
+ *               when in_dtype is f32; any other overlap is an error.
+ *   block:      64, 128 or 256.
+ *   sign_bits:  NULL (no signs) or (n/32,) uint32 words, 4-byte aligned: bit
+ *               i of word k set negates element 32k + i of every row.
+ *   inverse:    0 rotates, y = FWHT_block(x * s); non-zero unrotates,
+ *               y = FWHT_block(x) * s.
+ * FWHT_block runs the butterfly stages h = 1, 2, ..., block/2 on pairs
+ * (a + b, a - b) and multiplies once by fp32(1/sqrt(block)), the order the
+ * cache rotation uses, so the values are bitwise those of the formats'
+ * rotation.  The transform is its own inverse up to rounding.
+ */
+hkv_status hkv_hadamard(const void* x, hkv_dtype in_dtype, float* y, int64_t rows, int32_t n,
+                        int32_t block, const uint32_t* sign_bits, int32_t inverse,
+                        void* stream);
+
 /* Message for the last non-OK status returned on this thread (host). */
 const char* hkv_last_error(void);
 

@@ -131,3 +131,21 @@ def test_decode_host_errors_and_workspace():
     assert call(ws=FAKE + 4) == hkv.HKV_ERR_INVALID_ARG
     assert call(cache=FAKE + 2) == hkv.HKV_ERR_INVALID_ARG
     assert call(Hq=64, Hkv=1) == hkv.HKV_ERR_UNSUPPORTED      # 64 rows per KV head
+
+
+def test_hadamard_host_errors():
+    L = hkv.lib()
+    h = lambda **kw: L.hkv_hadamard(kw.get("x", FAKE), kw.get("dt", 0), kw.get("y", FAKE + (1 << 24)),
+                                    kw.get("rows", 4), kw.get("n", 256), kw.get("block", 128),
+                                    kw.get("sb", None), 0, None)
+    assert h(rows=0) == hkv.HKV_OK
+    assert h(block=96) == hkv.HKV_ERR_INVALID_ARG
+    assert h(n=192) == hkv.HKV_ERR_INVALID_ARG                  # not a multiple of 128
+    assert h(n=0) == hkv.HKV_ERR_INVALID_ARG
+    assert h(x=None) == hkv.HKV_ERR_INVALID_ARG
+    assert h(dt=5) == hkv.HKV_ERR_INVALID_ARG
+    assert h(x=FAKE + 8) == hkv.HKV_ERR_INVALID_ARG             # f32 input not 16-byte aligned
+    assert h(y=FAKE + (1 << 24) + 4) == hkv.HKV_ERR_INVALID_ARG
+    assert h(sb=FAKE + 2) == hkv.HKV_ERR_INVALID_ARG
+    assert h(y=FAKE + 1024) == hkv.HKV_ERR_INVALID_ARG          # partial overlap
+    assert h(dt=1, y=FAKE) == hkv.HKV_ERR_INVALID_ARG           # f16 input cannot be in place
