@@ -273,9 +273,9 @@ hkv_status hkv_decode_attention(const hkv_format* f, const void* query, hkv_dtyp
     return fail(HKV_ERR_INVALID_ARG,
                 "decode: need num_q_heads a positive multiple of num_kv_heads (%d, %d), "
                 "num_queries >= 0 (%d)", num_q_heads, num_kv_heads, num_queries);
-  if (queries_per_seq < 1 || queries_per_seq > 8 || num_queries % queries_per_seq)
+  if (queries_per_seq < 1 || queries_per_seq > 16 || num_queries % queries_per_seq)
     return fail(HKV_ERR_INVALID_ARG,
-                "decode: queries_per_seq must be in [1, 8] and divide num_queries (%d, %d)",
+                "decode: queries_per_seq must be in [1, 16] and divide num_queries (%d, %d)",
                 queries_per_seq, num_queries);
   if (q_dtype != HKV_F32 && q_dtype != HKV_F16)
     return fail(HKV_ERR_INVALID_ARG, "decode: bad query dtype %d", (int)q_dtype);

@@ -420,16 +420,19 @@ hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipSt
 constexpr int kKernelGeneric = 0, kKernelQ4 = 1, kKernelOctK3v4 = 2;
 
 constexpr int64_t kTargetSplitsWgs = 512;
+constexpr int kMaxRows = 32;          // query rows per KV head in one pass
+constexpr int kMaxQueriesPerSeq = 16;
 
 bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_heads,
                  int max_klen, int queries_per_seq, DecodePlan* p) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return false;
-  if (queries_per_seq < 1 || queries_per_seq > 8 || num_queries % queries_per_seq) return false;
+  if (queries_per_seq < 1 || queries_per_seq > kMaxQueriesPerSeq ||
+      num_queries % queries_per_seq)
+    return false;
   DecodePlan q;
   q.group = num_q_heads / num_kv_heads;
   q.n_q = queries_per_seq;
   q.rows = q.group * q.n_q;
-  if (q.rows > 32) return false;
   q.num_groups = num_queries / queries_per_seq;
   auto mfma_kernel = [&](int rows) {
     return q4_mfma_supported(f, rows)   ? kKernelQ4
@@ -437,20 +440,25 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
                                         : kKernelGeneric;
   };
   q.kernel = mfma_kernel(q.rows);
-  // More rows than the matrix-core kernels take (8 or 16 query rows per KV
-  // head): the queries of a sequence are split into the largest sub-groups
-  // that fit (each sub-group streams the sequence's K/V through its own
-  // workgroups).
-  if (q.kernel == kKernelGeneric && q.n_q > 1) {
-    for (int nq = q.n_q - 1; nq >= 1; --nq) {
-      if (q.n_q % nq != 0 || mfma_kernel(q.group * nq) == kKernelGeneric) continue;
-      q.num_groups = num_queries / nq;
-      q.n_q = nq;
-      q.rows = q.group * nq;
+  // More rows than one kernel pass takes (the matrix-core kernels: 8 or 16
+  // query rows per KV head; the generic kernel: 32): the queries of a
+  // sequence are split into the largest sub-groups that fit, preferring a
+  // matrix-core kernel; each sub-group streams the sequence's K/V through its
+  // own workgroups.
+  if ((q.kernel == kKernelGeneric || q.rows > kMaxRows) && q.n_q > 1) {
+    int best = 0;
+    for (int nq = q.n_q - 1; nq >= 1 && !best; --nq)
+      if (q.n_q % nq == 0 && mfma_kernel(q.group * nq) != kKernelGeneric) best = nq;
+    for (int nq = q.n_q; nq >= 1 && !best; --nq)
+      if (q.n_q % nq == 0 && q.group * nq <= kMaxRows) best = nq;
+    if (best) {
+      q.num_groups = num_queries / best;
+      q.n_q = best;
+      q.rows = q.group * best;
       q.kernel = mfma_kernel(q.rows);
-      break;
     }
   }
+  if (q.rows > kMaxRows) return false;
   q.rows_pad = q.kernel == kKernelQ4        ? 8
                : q.kernel == kKernelOctK3v4 ? oct_mfma_rows(f, q.rows)
                                             : round_rows(q.rows);

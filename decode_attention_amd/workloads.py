@@ -61,6 +61,13 @@ CONFIGS = {
     4: Config(4, "octave_k3v4_32k", "octave_k3v4", 128, 64, 32, 32768, 32, 8, "f16"),
     5: Config(5, "octave_k3v3_compact_verify", "octave_k3v3_compact", 256, 64, 64, 32768,
               32, 4, "f16", n_q=4, min_len=1024, n_append=4),
+    # Shapes beyond the five above, for the widened paths: a verify window of
+    # 8 query tokens (64 query rows per KV head), the non-compact 3-bit V
+    # format, and a head size that is not a power of two.
+    6: Config(6, "q4_0_window8_32k", "q4_0", 256, 0, 16, 32768, 16, 2, "f16", n_q=8,
+              outlier_frac=0.01),
+    7: Config(7, "octave_k3v3_32k", "octave_k3v3", 128, 64, 32, 32768, 32, 8, "f16"),
+    8: Config(8, "octave_k3v4_d192_32k", "octave_k3v4", 192, 64, 16, 32768, 16, 4, "f16"),
 }
 
 

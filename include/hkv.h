@@ -152,8 +152,11 @@ size_t hkv_decode_workspace_bytes(const hkv_format* f /*host*/, int32_t num_quer
  *                 q_to_klen[i] tokens of its sequence; <= 0 gives a zero row.
  *   max_klen:     host upper bound of q_to_klen (sizes the split-K grid).
  *   queries_per_seq: the queries come in consecutive groups of this many
- *                 that share one sequence (1..8; the kernel reads the cache
- *                 once per group).  num_queries must be a multiple.
+ *                 that share one sequence (1..16; a group's query rows --
+ *                 num_q_heads / num_kv_heads per query -- read the cache
+ *                 once per pass; more rows than a pass takes are split into
+ *                 sub-groups of whole queries, each reading the cache).
+ *                 num_queries must be a multiple.
  *   sm_scale:     softmax scale applied to q.k.
  *   out:          (num_queries, num_q_heads, D) fp32, unrotated space.
  *   workspace:    >= hkv_decode_workspace_bytes(...) bytes, 16-byte aligned.

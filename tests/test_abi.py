@@ -121,7 +121,7 @@ def test_decode_host_errors_and_workspace():
     assert call(Q=0) == hkv.HKV_OK
     assert call(Hkv=3) == hkv.HKV_ERR_INVALID_ARG
     assert call(nq=3) == hkv.HKV_ERR_INVALID_ARG
-    assert call(nq=9, Q=9) == hkv.HKV_ERR_INVALID_ARG
+    assert call(nq=17, Q=17) == hkv.HKV_ERR_INVALID_ARG
     assert call(q=None) == hkv.HKV_ERR_INVALID_ARG
     assert call(out=None) == hkv.HKV_ERR_INVALID_ARG
     assert call(mk=-1) == hkv.HKV_ERR_INVALID_ARG

@@ -173,6 +173,30 @@ def test_decode_matches_oracle(ci):
     _assert_close(got, ref, f"config {ci}")
 
 
+@pytest.mark.parametrize("dtype,D,R,Hq,Hkv,n_q", [("q4_0", 256, 0, 16, 2, 8),
+                                                  ("q4_0", 256, 0, 16, 2, 16),
+                                                  ("octave_k3v3_compact", 256, 64, 32, 4, 8),
+                                                  ("octave_k3v4", 128, 64, 32, 8, 16),
+                                                  ("octave_k3v4", 128, 64, 32, 8, 6),
+                                                  ("q4_0", 128, 0, 32, 1, 4),
+                                                  ("octave_k3v3", 128, 64, 8, 1, 12)])
+def test_decode_long_query_windows(dtype, D, R, Hq, Hkv, n_q):
+    """Query windows beyond 4 tokens (verify / multi-token prediction): more
+    query rows per KV head than one kernel pass takes, so the window's
+    queries run as sub-groups; causal among the window's tokens."""
+    cfg = W.Config(90, "window", dtype, D, R, 3, 900, Hq, Hkv, "f16", n_q=n_q, min_len=300)
+    w = W.make_workload(cfg)
+    f = hkv.format_init(dtype, D, R, cfg.page_size)
+    fo = O.format_init(dtype, D, R)
+    cache = _gpu_cache(f, w)
+    ref_cache, _ = _oracle_cache(fo, w, tuple(cache.shape))
+    scale = W.default_sm_scale(D)
+    got = _decode(f, w, cache, scale).cpu().numpy()
+    ref = O.attention(fo, w.query.astype(np.float32), ref_cache, w.block_table, w.q_to_req,
+                      w.q_to_klen, scale)
+    _assert_close(got, ref, f"{dtype} D={D} G={Hq // Hkv} n_q={n_q}")
+
+
 @pytest.mark.parametrize("dtype,D,R,Hq,Hkv", [("q4_0", 256, 0, 16, 2), ("q4_0", 256, 0, 8, 2),
                                               ("q4_0", 128, 0, 4, 4),
                                               ("q4_0", 64, 0, 6, 3),
