@@ -61,6 +61,7 @@ def lib():
             L.orc_bucket.restype = i32
             L.orc_quantize_lut.argtypes = [P(f32), i32, i32, P(ctypes.c_uint8), P(f32)]
             L.orc_q4_0_block.argtypes = [P(f32), P(ctypes.c_uint8), P(ctypes.c_uint16)]
+            L.orc_q8_0_block.argtypes = [P(f32), P(ctypes.c_int8), P(ctypes.c_uint16)]
             L.orc_pack.argtypes = [P(ctypes.c_uint8), i32, i32, P(ctypes.c_uint8)]
             L.orc_unpack.argtypes = [P(ctypes.c_uint8), i32, i32, P(ctypes.c_uint8)]
             L.orc_quantize.argtypes = [P(Format), P(f32), P(f32), i64, i32, P(ctypes.c_uint8)]
@@ -157,6 +158,16 @@ def q4_0_block(x: np.ndarray):
     lib().orc_q4_0_block(_p(x, ctypes.c_float), _p(codes, ctypes.c_uint8), ctypes.byref(d16))
     return codes, int(d16.value)
 
+
+
+def q8_0_block(x: np.ndarray):
+    """Q8_0 block (READING, the GGML block type): int8 codes and fp16 bits of d."""
+    x = np.ascontiguousarray(x, np.float32)
+    assert x.shape == (32,)
+    codes = np.empty(32, np.int8)
+    d16 = ctypes.c_uint16()
+    lib().orc_q8_0_block(_p(x, ctypes.c_float), _p(codes, ctypes.c_int8), ctypes.byref(d16))
+    return codes, int(d16.value)
 
 def pack(codes: np.ndarray, bits: int) -> np.ndarray:
     c = np.ascontiguousarray(codes, np.uint8)

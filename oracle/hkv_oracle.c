@@ -59,6 +59,30 @@ int orc_format_init(orc_format* f, const char* cache_dtype, int32_t head_size,
     f->kernel_code = 0;
     return ORC_OK;
   }
+  if (strcmp(cache_dtype, "q8_0") == 0) {
+    /* READING of the int8 mode that [Q4] compares against (its footprint
+     * note: the Q4_0 cache is half of Q8_0's; the merge note: int8 stays the
+     * default) and that [M5] row 5 measures with FWHT: the same rotation as
+     * Q4_0 (FWHT over the head, no signs) followed by the Q8_0 block type of
+     * the GGML family, 32 int8 codes and one fp16 scale per block. */
+    if (!is_pow2(d) || d < 32 || d > ORC_MAX_HEAD) return ORC_EINVAL;
+    f->kind = ORC_KIND_Q8_0;
+    f->head_size = d;
+    f->rope_dim = 0;
+    f->v_bits = 8;
+    f->k_block = d;
+    f->v_block = d;
+    f->use_signs = 0;
+    f->k_wide_dim = 0;
+    f->off_k_nope = d; /* no NoPE part: equals off_v */
+    f->off_v = d;
+    f->off_scales = 2 * d;
+    f->num_k_scales = d / 32;
+    f->num_scales = d / 16;
+    f->slot_bytes = 2 * d + 2 * (d / 16);
+    f->kernel_code = 8;
+    return ORC_OK;
+  }
   int32_t v_bits, compact;
   if (strcmp(cache_dtype, "octave_k3v4") == 0) {
     v_bits = 4;
@@ -376,6 +400,25 @@ void orc_q4_0_block(const float* x, uint8_t* codes, uint16_t* d16) {
   }
 }
 
+/* READING: the Q8_0 block type of the GGML family.  d = amax / 127 with
+ * amax the largest magnitude, id = d != 0 ? 1/d : 0, code = round(x * id)
+ * with halves away from zero (C roundf), so the largest-magnitude element
+ * maps to +-127; the fp16 of d is stored. */
+void orc_q8_0_block(const float* x, int8_t* codes, uint16_t* d16) {
+  float amax = 0.0f;
+  for (int32_t j = 0; j < 32; ++j) {
+    const float a = fabsf(x[j]);
+    if (a > amax) amax = a;
+  }
+  const float d = amax / 127.0f;
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  *d16 = orc_f32_to_f16(d);
+  for (int32_t j = 0; j < 32; ++j) {
+    const float t = x[j] * id;
+    codes[j] = (int8_t)roundf(t);
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* [OCT] _pack.  4-bit: every 8 codes form one little-endian word; byte j    */
 /* holds code j in its low nibble and code j+4 in its high nibble.  3-bit: a */
@@ -461,6 +504,16 @@ static void quantize_one(const orc_format* f, const float* sgn, const float* key
   memcpy(vbuf, value, sizeof(float) * (size_t)d);
   rotate_f32(f, sgn, kbuf, f->k_block);
   rotate_f32(f, sgn, vbuf, f->v_block);
+  if (f->kind == ORC_KIND_Q8_0) {
+    uint16_t h16;
+    for (int32_t b = 0; b < d / 32; ++b) {
+      orc_q8_0_block(kbuf + 32 * b, (int8_t*)(slot + 32 * b), &h16);
+      put_f16(slot + f->off_scales + 2 * b, h16);
+      orc_q8_0_block(vbuf + 32 * b, (int8_t*)(slot + f->off_v + 32 * b), &h16);
+      put_f16(slot + f->off_scales + 2 * (d / 32 + b), h16);
+    }
+    return;
+  }
   if (f->kind == ORC_KIND_Q4_0) {
     uint16_t h16;
     for (int32_t b = 0; b < d / 32; ++b) {
@@ -517,10 +570,16 @@ void orc_quantize(const orc_format* f, const float* key, const float* value,
 }
 
 /* Rotated-space dequantization of one slot ([OCT] reference_dequantize with
- * rotated=True): code value times (fp16 scale / LUT_ONE) for Octave, and
- * (code - 8) times the fp16 scale for Q4_0.  Both are exact in fp32. */
+ * rotated=True): code value times (fp16 scale / LUT_ONE) for Octave,
+ * (code - 8) times the fp16 scale for Q4_0, and the int8 code times the fp16
+ * scale for Q8_0.  All are exact in fp32. */
 static void dequant_k_rot(const orc_format* f, const uint8_t* slot, float* k, uint8_t* codes) {
   const int32_t d = f->head_size;
+  if (f->kind == ORC_KIND_Q8_0) {
+    for (int32_t i = 0; i < d; ++i)
+      k[i] = (float)(int8_t)slot[i] * orc_f16_to_f32(get_f16(slot + f->off_scales + 2 * (i / 32)));
+    return;
+  }
   if (f->kind == ORC_KIND_Q4_0) {
     orc_unpack(slot, d, 4, codes);
     for (int32_t i = 0; i < d; ++i)
@@ -548,6 +607,12 @@ static void dequant_k_rot(const orc_format* f, const uint8_t* slot, float* k, ui
 
 static void dequant_v_rot(const orc_format* f, const uint8_t* slot, float* v, uint8_t* codes) {
   const int32_t d = f->head_size;
+  if (f->kind == ORC_KIND_Q8_0) {
+    for (int32_t i = 0; i < d; ++i)
+      v[i] = (float)(int8_t)slot[f->off_v + i] *
+             orc_f16_to_f32(get_f16(slot + f->off_scales + 2 * (d / 32 + i / 32)));
+    return;
+  }
   if (f->kind == ORC_KIND_Q4_0) {
     orc_unpack(slot + f->off_v, d, 4, codes);
     for (int32_t i = 0; i < d; ++i)

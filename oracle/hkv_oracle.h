@@ -37,12 +37,13 @@
 extern "C" {
 #endif
 
-enum { ORC_KIND_Q4_0 = 0, ORC_KIND_OCTAVE = 1 };
+enum { ORC_KIND_Q4_0 = 0, ORC_KIND_OCTAVE = 1, ORC_KIND_Q8_0 = 2 };
 enum { ORC_OK = 0, ORC_EINVAL = 1 };
 
 /* Format descriptor; field meanings follow [OCT] OctaveFormat.  For Q4_0 the
  * slot is READING: [K nibbles D/2][V nibbles D/2][K fp16 scales D/32]
- * [V fp16 scales D/32]. */
+ * [V fp16 scales D/32].  For Q8_0 (READING, below) it is [K int8 D][V int8 D]
+ * [K fp16 scales D/32][V fp16 scales D/32]. */
 typedef struct {
   int32_t kind;
   int32_t head_size;
@@ -62,7 +63,7 @@ typedef struct {
   int32_t kernel_code;
 } orc_format;
 
-/* "q4_0", "octave_k3v4", "octave_k3v3", "octave_k3v3_compact". */
+/* "q4_0", "q8_0", "octave_k3v4", "octave_k3v3", "octave_k3v3_compact". */
 int orc_format_init(orc_format* f, const char* cache_dtype, int32_t head_size,
                     int32_t rope_dim);
 
@@ -94,6 +95,8 @@ int32_t orc_bucket(float y, int32_t bits);
 void orc_quantize_lut(const float* x, int32_t n, int32_t bits, uint8_t* codes,
                       float* scale);
 void orc_q4_0_block(const float* x, uint8_t* codes, uint16_t* d16);
+/* Q8_0 block of 32 values: int8 codes in [-127, 127] and the fp16 scale. */
+void orc_q8_0_block(const float* x, int8_t* codes, uint16_t* d16);
 
 /* Bit packing of [OCT] _pack (4- and 3-bit) and its inverse. */
 void orc_pack(const uint8_t* codes, int32_t n, int32_t bits, uint8_t* out);

@@ -13,7 +13,7 @@ import torch
 import oracle as O
 
 FORMATS = [("q4_0", 256, 0), ("octave_k3v4", 128, 64), ("octave_k3v3_compact", 256, 64),
-           ("octave_k3v3", 128, 64), ("octave_k3v4", 192, 64)]
+           ("octave_k3v3", 128, 64), ("octave_k3v4", 192, 64), ("q8_0", 128, 0)]
 
 
 def _setup(dtype, D, R, lens, Hq, Hkv, page=16, seed=0, shuffle=True):
