@@ -45,10 +45,13 @@ void make_sign_bits(int n, uint32_t* words) {
 // descriptor is refused before anything is enqueued.
 hkv_status check_format(const hkv_format* f) {
   if (!f) return fail(HKV_ERR_INVALID_ARG, "format is NULL");
-  static const char* names[] = {"q4_0", "octave_k3v4", "octave_k3v3", "octave_k3v3_compact"};
+  static const char* names[] = {"q4_0", "octave_k3v4", "octave_k3v3", "octave_k3v3_compact",
+                                "q8_0"};
   const char* name = nullptr;
   if (f->kind == HKV_KIND_Q4_0) {
     name = names[0];
+  } else if (f->kind == HKV_KIND_Q8_0) {
+    name = names[4];
   } else if (f->kind == HKV_KIND_OCTAVE) {
     name = f->compact ? names[3] : (f->v_bits == 4 ? names[1] : names[2]);
   } else {
@@ -131,6 +134,27 @@ hkv_status hkv_format_init(hkv_format* f, const char* cache_dtype, int32_t head_
     g.num_scales = d / 16;
     g.slot_bytes = d + d / 8;
     g.kernel_code = 0;
+    *f = g;
+    return HKV_OK;
+  }
+  if (std::strcmp(cache_dtype, "q8_0") == 0) {
+    // The int8 mode [Q4] compares against, after the same rotation (FWHT
+    // over the head, no signs): 32 int8 codes and one fp16 scale per block.
+    if (d != 64 && d != 128 && d != 256)
+      return fail(HKV_ERR_INVALID_ARG, "q8_0 needs head_size 64, 128 or 256, got %d", d);
+    g.kind = HKV_KIND_Q8_0;
+    g.rope_dim = 0;
+    g.v_bits = 8;
+    g.k_block = d;
+    g.v_block = d;
+    g.k_wide_dim = 0;
+    g.off_k_nope = d;
+    g.off_v = d;
+    g.off_scales = 2 * d;
+    g.num_k_scales = d / 32;
+    g.num_scales = d / 16;
+    g.slot_bytes = 2 * d + d / 8;
+    g.kernel_code = 8;
     *f = g;
     return HKV_OK;
   }

@@ -35,6 +35,16 @@ __device__ __forceinline__ uint32_t lds_word(const uint32_t* p, int byte_off) {
 __device__ __forceinline__ void k_chunk(const DevFmt& f, const uint32_t* s, int d0,
                                         float (&cv)[32], float& sc) {
   const uint8_t* sb = (const uint8_t*)s;
+  if (f.kind == HKV_KIND_Q8_0) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t word = lds_word(s, d0 + 4 * w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cv[4 * w + j] = (float)(int8_t)(uint8_t)(word >> (8 * j));
+    }
+    sc = h2f(rd16(sb + f.off_scales + 2 * (d0 >> 5)));
+    return;
+  }
   if (f.kind == HKV_KIND_Q4_0) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -446,11 +456,15 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   // matrix-core kernel; each sub-group streams the sequence's K/V through its
   // own workgroups.
   if ((q.kernel == kKernelGeneric || q.rows > kMaxRows) && q.n_q > 1) {
+    // (the generic kernel stages a tile of slots per wave in LDS, so large
+    // slots bound its rows too)
     int best = 0;
     for (int nq = q.n_q - 1; nq >= 1 && !best; --nq)
       if (q.n_q % nq == 0 && mfma_kernel(q.group * nq) != kKernelGeneric) best = nq;
     for (int nq = q.n_q; nq >= 1 && !best; --nq)
-      if (q.n_q % nq == 0 && q.group * nq <= kMaxRows) best = nq;
+      if (q.n_q % nq == 0 && q.group * nq <= kMaxRows &&
+          generic_lds_bytes(f, round_rows(q.group * nq)) <= 160 * 1024)
+        best = nq;
     if (best) {
       q.num_groups = num_queries / best;
       q.n_q = best;

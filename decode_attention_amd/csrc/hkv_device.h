@@ -280,8 +280,11 @@ __device__ __forceinline__ uint16_t rd16(const uint8_t* p) {
 }
 
 // Rotated-space value of K dim d of a slot: (code - 8) * fp16 scale for
-// Q4_0, LUT[code] * (fp16 scale / 64) for Octave.  Exact in fp32.
+// Q4_0, the int8 code * fp16 scale for Q8_0, LUT[code] * (fp16 scale / 64)
+// for Octave.  Exact in fp32.
 __device__ __forceinline__ float k_value(const DevFmt& f, const uint8_t* slot, int d) {
+  if (f.kind == HKV_KIND_Q8_0)
+    return (float)(int8_t)slot[d] * h2f(rd16(slot + f.off_scales + 2 * (d >> 5)));
   if (f.kind == HKV_KIND_Q4_0) {
     const int c = code4(slot, d);
     return (float)(c - 8) * h2f(rd16(slot + f.off_scales + 2 * (d >> 5)));
@@ -306,6 +309,8 @@ __device__ __forceinline__ float k_value(const DevFmt& f, const uint8_t* slot, i
 
 __device__ __forceinline__ float v_value(const DevFmt& f, const uint8_t* slot, int d) {
   const uint8_t* seg = slot + f.off_v;
+  if (f.kind == HKV_KIND_Q8_0)
+    return (float)(int8_t)seg[d] * h2f(rd16(slot + f.off_scales + 2 * (f.D / 32 + (d >> 5))));
   if (f.kind == HKV_KIND_Q4_0) {
     const int c = code4(seg, d);
     return (float)(c - 8) * h2f(rd16(slot + f.off_scales + 2 * (f.D / 32 + (d >> 5))));

@@ -199,6 +199,62 @@ __device__ __forceinline__ void q4_row(const DevFmt& f, float (&k)[E], float (&v
   if (lane < 2 * E) dst[f.off_scales / 4 + lane] = word;
 }
 
+// Q8_0 over one 32-value block = one half-register: d = max|x| / 127,
+// code = round(x * (1/d)), halves away from zero, as int8.  The magnitudes
+// are reduced as fp32 bit patterns (non-negative floats order like their
+// bits).  Returns the fp16 bits of d (the same in all lanes of the half).
+__device__ __forceinline__ uint32_t q8_block(float x, uint32_t* code) {
+  uint32_t a = __float_as_uint(x) & 0x7FFFFFFFu;
+  a = max(a, dpp<0xB1>(a));
+  a = max(a, dpp<0x4E>(a));
+  a = max(a, dpp<0x141>(a));
+  a = max(a, dpp<0x140>(a));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    a = max(r[0], r[1]);
+  }
+  const float d = __uint_as_float(a) / 127.0f;
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const float t = x * id;
+  *code = (uint32_t)(int)roundf(t) & 0xFFu;
+  return f2h(d);
+}
+
+// Q8_0 row: FWHT over the head, 32-value blocks, int8 codes K | V, then the
+// scales as for Q4_0.  Slot word k of register e is the codes of lanes
+// 4k .. 4k+3; lane 4k ends with it.
+template <int E>
+__device__ __forceinline__ void q8_row(const DevFmt& f, float (&k)[E], float (&v)[E],
+                                       uint32_t* dst) {
+  const int lane = lane_id();
+  fwht_strided<E>(k, f.k_block, f.k_norm);
+  fwht_strided<E>(v, f.v_block, f.v_norm);
+  uint32_t wk[E], wv[E];
+  uint32_t word = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint32_t ck, cv;
+    const uint32_t sk = q8_block(k[e], &ck);
+    const uint32_t sv = q8_block(v[e], &cv);
+    wk[e] = or_quad(ck << (8 * (lane & 3)));
+    wv[e] = or_quad(cv << (8 * (lane & 3)));
+    const auto rk = __builtin_amdgcn_permlane32_swap(sk, sk, false, false);
+    const auto rv = __builtin_amdgcn_permlane32_swap(sv, sv, false, false);
+    word = (lane == e) ? (rk[0] | (rk[1] << 16)) : word;
+    word = (lane == E + e) ? (rv[0] | (rv[1] << 16)) : word;
+  }
+  if ((lane & 3) == 0) {
+    uint32_t* pk = dst + (lane >> 2);
+    uint32_t* pv = dst + f.off_v / 4 + (lane >> 2);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      pk[16 * e] = wk[e];
+      pv[16 * e] = wv[e];
+    }
+  }
+  if (lane < 2 * E) dst[f.off_scales / 4 + lane] = word;
+}
+
 // Octave row: sign flips, FWHT (64-blocks or the whole head), per-block
 // Lloyd-Max codes; K codes (4-bit RoPE registers, then the 3-bit rest), V
 // codes, then the fp16 scales (K scales, V scale, zero padding).  Word
@@ -289,7 +345,7 @@ constexpr int kQuantMaxGroups = 2048; // 8 workgroups per CU on 256 CUs
 
 // rows = num_tokens * num_kv_heads (below 2^31 less one grid stride);
 // row = token * num_kv_heads + head.
-template <int E, bool F16, bool Q4>
+template <int E, bool F16, int KIND>
 __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_append_kernel(
     DevFmt f, const void* key, const void* value, int rows, int num_kv_heads,
     const int64_t* slot_mapping, uint8_t* cache) {
@@ -327,7 +383,8 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_append_kernel(
       }
       uint32_t* dst =
           (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, cur % num_kv_heads);
-      if (Q4) q4_row<E>(f, k, v, dst);
+      if (KIND == HKV_KIND_Q4_0) q4_row<E>(f, k, v, dst);
+      else if (KIND == HKV_KIND_Q8_0) q8_row<E>(f, k, v, dst);
       else octave_row<E>(f, k, v, dst);
     }
     if (row >= rows) break;
@@ -335,7 +392,8 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_append_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Q4_0 quantize-append for many rows: 16 lanes per row, four rows per wave.
+// Q4_0 and Q8_0 quantize-append for many rows: 16 lanes per row, four rows
+// per wave.
 // Lane l of a 16-lane row holds elements 64q + 4l + i (i = 0..3) of its row
 // for each 64-wide group q, so the element index bits 0-1 live in a
 // register, bits 2-5 in the lane (exchanges stay inside the 16-lane DPP
@@ -375,6 +433,26 @@ __device__ __forceinline__ void q4_group16(const float (&x)[4], uint32_t* word,
   *word = bytes | (dpp<0xB1>(bytes) << 4);
   const uint32_t h = f2h(d);
   *scale = h | (dpp<0x128>(h) << 16);  // row_ror:8 -> the other block's scale
+}
+
+// Q8_0 over one 64-wide group in the 16-lane layout: `word` is slot word
+// 16q + l (this lane's four int8 codes), `scale` (lanes 0-7) the scale word
+// of the group, as for Q4_0.
+__device__ __forceinline__ void q8_group16(const float (&x)[4], uint32_t* word,
+                                           uint32_t* scale) {
+  uint32_t a = max(max(__float_as_uint(x[0]) & 0x7FFFFFFFu, __float_as_uint(x[1]) & 0x7FFFFFFFu),
+                   max(__float_as_uint(x[2]) & 0x7FFFFFFFu, __float_as_uint(x[3]) & 0x7FFFFFFFu));
+  a = max(a, dpp<0xB1>(a));   // quad [1,0,3,2]
+  a = max(a, dpp<0x4E>(a));   // quad [2,3,0,1]
+  a = max(a, dpp<0x141>(a));  // half-row mirror: the 8 lanes of the block
+  const float d = __uint_as_float(a) / 127.0f;
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w |= ((uint32_t)(int)roundf(x[i] * id) & 0xFFu) << (8 * i);
+  *word = w;
+  const uint32_t h = f2h(d);
+  *scale = h | (dpp<0x128>(h) << 16);
 }
 
 template <int Q, bool F16>
@@ -424,8 +502,8 @@ constexpr int kRows16MinRows = 4096;  // below this the one-row-per-wave kernel 
 
 // rows as for quantize_append_kernel; key/value 8-byte (f16) or 16-byte (f32)
 // aligned.
-template <int Q, bool F16>
-__global__ __launch_bounds__(kQuantWaves * kWave) void quantize_q4_rows16_kernel(
+template <int Q, bool F16, int KIND>
+__global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
     DevFmt f, const void* key, const void* value, int rows, int num_kv_heads,
     const int64_t* slot_mapping, uint8_t* cache) {
   constexpr int R = F16 ? 2 : 4;
@@ -456,8 +534,13 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_q4_rows16_kernel
     uint32_t wk[Q], wv[Q], sk[Q], sv[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-      q4_group16(k[q], &wk[q], &sk[q]);
-      q4_group16(v[q], &wv[q], &sv[q]);
+      if (KIND == HKV_KIND_Q8_0) {
+        q8_group16(k[q], &wk[q], &sk[q]);
+        q8_group16(v[q], &wv[q], &sv[q]);
+      } else {
+        q4_group16(k[q], &wk[q], &sk[q]);
+        q4_group16(v[q], &wv[q], &sv[q]);
+      }
     }
     // scale words: lanes 0..Q-1 the K words, Q..2Q-1 the V words
     uint32_t sw = sk[0];
@@ -478,7 +561,13 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_q4_rows16_kernel
       }
       uint32_t* dst =
           (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, cur % num_kv_heads);
-      if ((l & 1) == 0) {
+      if (KIND == HKV_KIND_Q8_0) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          dst[16 * q + l] = wk[q];
+          dst[f.off_v / 4 + 16 * q + l] = wv[q];
+        }
+      } else if ((l & 1) == 0) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
           dst[8 * q + (l >> 1)] = wk[q];
@@ -554,17 +643,18 @@ hipError_t launch_quantize_append(const DevFmt& f, const void* key, const void* 
   const dim3 grid((unsigned)(groups < kQuantMaxGroups ? groups : kQuantMaxGroups));
   const dim3 block(kQuantWaves * kWave);
   const int r = (int)rows;
-  const bool q4 = f.kind == HKV_KIND_Q4_0;
+  const bool q4 = f.kind == HKV_KIND_Q4_0, q8 = f.kind == HKV_KIND_Q8_0;
   const uintptr_t align = in_f16 ? 8 : 16;
-  if (q4 && rows >= kRows16MinRows && ((uintptr_t)key % align) == 0 &&
+  if ((q4 || q8) && rows >= kRows16MinRows && ((uintptr_t)key % align) == 0 &&
       ((uintptr_t)value % align) == 0) {
     const int64_t g16 = (rows + 4 * kQuantWaves - 1) / (4 * kQuantWaves);
     const dim3 grid16((unsigned)(g16 < kQuantMaxGroups ? g16 : kQuantMaxGroups));
-#define HKV_Q16(Q_)                                                                          \
-  (in_f16 ? (quantize_q4_rows16_kernel<Q_, true><<<grid16, block, 0, s>>>(                   \
+#define HKV_Q16K(Q_, K_)                                                                     \
+  (in_f16 ? (quantize_rows16_kernel<Q_, true, K_><<<grid16, block, 0, s>>>(                  \
                 f, key, value, r, num_kv_heads, slot_mapping, cache))                        \
-          : (quantize_q4_rows16_kernel<Q_, false><<<grid16, block, 0, s>>>(                  \
+          : (quantize_rows16_kernel<Q_, false, K_><<<grid16, block, 0, s>>>(                 \
                 f, key, value, r, num_kv_heads, slot_mapping, cache)))
+#define HKV_Q16(Q_) (q8 ? HKV_Q16K(Q_, HKV_KIND_Q8_0) : HKV_Q16K(Q_, HKV_KIND_Q4_0))
     switch (f.D / kWave) {
       case 1: HKV_Q16(1); break;
       case 2: HKV_Q16(2); break;
@@ -572,20 +662,24 @@ hipError_t launch_quantize_append(const DevFmt& f, const void* key, const void* 
       default: return hipErrorInvalidValue;
     }
 #undef HKV_Q16
+#undef HKV_Q16K
     return hipGetLastError();
   }
 #define HKV_QA1(E_, F16_, Q4_)                                                         \
   quantize_append_kernel<E_, F16_, Q4_><<<grid, block, 0, s>>>(f, key, value, r, num_kv_heads, \
                                                                slot_mapping, cache)
-#define HKV_QA(E_)                               \
-  do {                                           \
-    if (q4) {                                    \
-      if (in_f16) HKV_QA1(E_, true, true);       \
-      else HKV_QA1(E_, false, true);             \
-    } else {                                     \
-      if (in_f16) HKV_QA1(E_, true, false);      \
-      else HKV_QA1(E_, false, false);            \
-    }                                            \
+#define HKV_QA(E_)                                                        \
+  do {                                                                    \
+    if (q4) {                                                             \
+      if (in_f16) HKV_QA1(E_, true, HKV_KIND_Q4_0);                       \
+      else HKV_QA1(E_, false, HKV_KIND_Q4_0);                             \
+    } else if (q8) {                                                      \
+      if (in_f16) HKV_QA1(E_, true, HKV_KIND_Q8_0);                       \
+      else HKV_QA1(E_, false, HKV_KIND_Q8_0);                             \
+    } else {                                                              \
+      if (in_f16) HKV_QA1(E_, true, HKV_KIND_OCTAVE);                     \
+      else HKV_QA1(E_, false, HKV_KIND_OCTAVE);                           \
+    }                                                                     \
   } while (0)
   switch (f.D / kWave) {
     case 1: HKV_QA(1); break;

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libhkv.so")
 
 HKV_OK, HKV_ERR_INVALID_ARG, HKV_ERR_UNSUPPORTED, HKV_ERR_WORKSPACE, HKV_ERR_HIP = range(5)
 HKV_F32, HKV_F16 = 0, 1
-HKV_KIND_Q4_0, HKV_KIND_OCTAVE = 0, 1
+HKV_KIND_Q4_0, HKV_KIND_OCTAVE, HKV_KIND_Q8_0 = 0, 1, 2
 HKV_MAX_HEAD = 256
 
 # Names of the exported entry points (include/hkv.h).

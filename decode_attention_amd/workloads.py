@@ -29,7 +29,7 @@ import numpy as np
 class Config:
     index: int
     name: str
-    cache_dtype: str          # "q4_0" | "octave_k3v4" | "octave_k3v3" | "octave_k3v3_compact"
+    cache_dtype: str          # "q4_0" | "q8_0" | "octave_k3v4" | "octave_k3v3" | "octave_k3v3_compact"
     head_size: int
     rope_dim: int
     batch: int
@@ -68,6 +68,9 @@ CONFIGS = {
               outlier_frac=0.01),
     7: Config(7, "octave_k3v3_32k", "octave_k3v3", 128, 64, 32, 32768, 32, 8, "f16"),
     8: Config(8, "octave_k3v4_d192_32k", "octave_k3v4", 192, 64, 16, 32768, 16, 4, "f16"),
+    # the shape of config 3 in the int8 (Q8_0) mode
+    9: Config(9, "q8_0_long_128k", "q8_0", 256, 0, 4, 131072, 16, 2, "f16",
+              outlier_frac=0.01, n_append=4),
 }
 
 

@@ -47,7 +47,7 @@ typedef enum {
 
 typedef enum { HKV_F32 = 0, HKV_F16 = 1 } hkv_dtype;
 
-typedef enum { HKV_KIND_Q4_0 = 0, HKV_KIND_OCTAVE = 1 } hkv_kind;
+typedef enum { HKV_KIND_Q4_0 = 0, HKV_KIND_OCTAVE = 1, HKV_KIND_Q8_0 = 2 } hkv_kind;
 
 /* Largest head size the GPU kernels take. */
 #define HKV_MAX_HEAD 256
@@ -64,6 +64,10 @@ typedef enum { HKV_KIND_Q4_0 = 0, HKV_KIND_OCTAVE = 1 } hkv_kind;
  *   Q4_0:   [K nibbles D/2][V nibbles D/2][K fp16 scales D/32][V fp16
  *           scales D/32]; nibbles in the 4-bit order of [OCT] _pack; one
  *           scale per 32 values ([Q4] "How" item 2).
+ *   Q8_0:   [K int8 D][V int8 D][K fp16 scales D/32][V fp16 scales D/32]:
+ *           the int8 mode [Q4] compares its footprint against, after the
+ *           same rotation; codes round(x / d) with d = max|x| / 127 per 32
+ *           values, halves away from zero.
  * sign_bits: the fixed +-1 pattern applied before the Hadamard transform
  *   ([OCT] signs / sign_bits), bit i of the words set where the sign is -1;
  *   all zero for Q4_0, which has no sign flips ([Q4] "How" item 1).
@@ -72,7 +76,7 @@ typedef struct {
   int32_t kind;         /* hkv_kind                                        */
   int32_t head_size;    /* D                                               */
   int32_t rope_dim;     /* leading K dims that take 4-bit codes (Octave)   */
-  int32_t v_bits;       /* 3 or 4                                          */
+  int32_t v_bits;       /* 3 or 4 (8 for Q8_0)                             */
   int32_t compact;      /* Octave compact K (one full-head rotation)       */
   int32_t page_size;    /* tokens per cache page                           */
   int32_t k_block;      /* FWHT block of K and of the query                */
@@ -84,17 +88,17 @@ typedef struct {
   int32_t num_k_scales;
   int32_t num_scales;
   int32_t slot_bytes;
-  int32_t kernel_code;  /* [OCT] kernel_code: v_bits + 16*compact; 0 = Q4_0 */
+  int32_t kernel_code;  /* [OCT] kernel_code: v_bits + 16*compact; 0 = Q4_0, 8 = Q8_0 */
   uint32_t sign_bits[HKV_MAX_HEAD / 32];
 } hkv_format;
 
 /*
  * hkv_format_init -- fill *f for a cache dtype.
- *   cache_dtype (host): "q4_0", "octave_k3v4", "octave_k3v3",
+ *   cache_dtype (host): "q4_0", "q8_0", "octave_k3v4", "octave_k3v3",
  *                       "octave_k3v3_compact" ([OCT] from_cache_dtype).
  *   head_size: Octave: multiple of 64, <= 256 (compact: a power of two);
- *              Q4_0: 64, 128 or 256.
- *   rope_dim:  Octave: multiple of 64, <= head_size; ignored for Q4_0.
+ *              Q4_0 and Q8_0: 64, 128 or 256.
+ *   rope_dim:  Octave: multiple of 64, <= head_size; ignored for Q4_0/Q8_0.
  *   page_size: tokens per page, 1..1024.
  * Errors mirror [OCT] OctaveFormat validation: HKV_ERR_INVALID_ARG.
  * Enqueues nothing.

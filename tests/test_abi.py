@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol():
 @pytest.mark.parametrize("dtype,D,R", [("q4_0", 256, 0), ("q4_0", 128, 0), ("q4_0", 64, 0),
                                        ("octave_k3v4", 128, 64), ("octave_k3v3", 128, 64),
                                        ("octave_k3v3_compact", 256, 64), ("octave_k3v4", 192, 64),
-                                       ("octave_k3v4", 256, 128), ("octave_k3v3_compact", 64, 0)])
+                                       ("octave_k3v4", 256, 128), ("octave_k3v3_compact", 64, 0),
+                                       ("q8_0", 256, 0), ("q8_0", 64, 0)])
 def test_format_matches_oracle(dtype, D, R):
     f = hkv.format_init(dtype, D, R, 16)
     g = O.format_init(dtype, D, R)
@@ -50,7 +51,8 @@ def test_format_matches_oracle(dtype, D, R):
 @pytest.mark.parametrize("args", [("octave_k3v3_compact", 192, 64, 16), ("octave_k3v4", 128, 32, 16),
                                   ("octave_k3v4", 96, 0, 16), ("octave_k3v4", 128, 192, 16),
                                   ("octave_k5v5", 128, 64, 16), ("q4_0", 96, 0, 16),
-                                  ("q4_0", 256, 0, 0), ("q4_0", 256, 0, 2048)])
+                                  ("q4_0", 256, 0, 0), ("q4_0", 256, 0, 2048), ("q8_0", 96, 0, 16),
+                                  ("q8_0", 512, 0, 16)])
 def test_format_validation(args):
     with pytest.raises(hkv.HkvError) as e:
         hkv.format_init(*args)

@@ -78,7 +78,8 @@ def test_quantize_append_bit_exact(ci):
                                        ("octave_k3v4", 128, 64), ("octave_k3v3", 128, 64),
                                        ("octave_k3v3_compact", 256, 64), ("octave_k3v4", 192, 64),
                                        ("octave_k3v4", 256, 128), ("octave_k3v3_compact", 64, 0),
-                                       ("octave_k3v4", 128, 0), ("octave_k3v4", 128, 128)])
+                                       ("octave_k3v4", 128, 0), ("octave_k3v4", 128, 128),
+                                       ("q8_0", 256, 0), ("q8_0", 128, 0), ("q8_0", 64, 0)])
 @pytest.mark.parametrize("in_dtype", [np.float32, np.float16])
 def test_quantize_and_dequantize_formats(dtype, D, R, in_dtype):
     rng = np.random.default_rng(D + R)
@@ -114,15 +115,16 @@ def test_quantize_and_dequantize_formats(dtype, D, R, in_dtype):
         assert np.all(kd[~keep] == 0) and np.all(vd[~keep] == 0)
 
 
+@pytest.mark.parametrize("dtype", ["q4_0", "q8_0"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("in_dtype", [np.float32, np.float16])
 @pytest.mark.parametrize("misaligned", [False, True])
-def test_quantize_q4_many_rows(D, in_dtype, misaligned):
-    """Row counts that take the many-rows Q4_0 kernel (16 lanes per row, four
-    rows per wave; a ragged last wave, skipped slots); a key/value pointer
-    off its 8/16-byte alignment takes the one-row-per-wave kernel instead.
-    Both must give the oracle's bytes."""
-    rng = np.random.default_rng(7 * D + (3 if misaligned else 0))
+def test_quantize_many_rows(dtype, D, in_dtype, misaligned):
+    """Row counts that take the many-rows Q4_0 / Q8_0 kernel (16 lanes per
+    row, four rows per wave; a ragged last wave, skipped slots); a key/value
+    pointer off its 8/16-byte alignment takes the one-row-per-wave kernel
+    instead.  Both must give the oracle's bytes."""
+    rng = np.random.default_rng(7 * D + (3 if misaligned else 0) + (1 if dtype == "q8_0" else 0))
     T, H, P = 1501, 3, 16                              # 4503 rows = 281 waves of 16 + 7
     k = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
     v = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
@@ -130,8 +132,8 @@ def test_quantize_q4_many_rows(D, in_dtype, misaligned):
     v[9, 2] = 0
     k[11, 1, :32] = -np.abs(k[11, 1, :32]).max()     # max-abs ties inside one block
     k[11, 1, 3] = -k[11, 1, 3]
-    f = hkv.format_init("q4_0", D, 0, P)
-    fo = O.format_init("q4_0", D, 0)
+    f = hkv.format_init(dtype, D, 0, P)
+    fo = O.format_init(dtype, D, 0)
     pages = (T + P - 1) // P + 2
     sm = rng.permutation(pages * P)[:T].astype(np.int64)
     sm[[0, 17, T - 1]] = -1
@@ -179,7 +181,8 @@ def test_decode_matches_oracle(ci):
                                                   ("octave_k3v4", 128, 64, 32, 8, 16),
                                                   ("octave_k3v4", 128, 64, 32, 8, 6),
                                                   ("q4_0", 128, 0, 32, 1, 4),
-                                                  ("octave_k3v3", 128, 64, 8, 1, 12)])
+                                                  ("octave_k3v3", 128, 64, 8, 1, 12),
+                                                  ("q8_0", 256, 0, 16, 2, 4)])
 def test_decode_long_query_windows(dtype, D, R, Hq, Hkv, n_q):
     """Query windows beyond 4 tokens (verify / multi-token prediction): more
     query rows per KV head than one kernel pass takes, so the window's
@@ -204,7 +207,9 @@ def test_decode_long_query_windows(dtype, D, R, Hq, Hkv, n_q):
                                               ("octave_k3v4", 128, 64, 32, 4),
                                               ("octave_k3v3", 128, 64, 8, 1),
                                               ("octave_k3v3_compact", 256, 64, 32, 4),
-                                              ("octave_k3v4", 192, 64, 4, 2)])
+                                              ("octave_k3v4", 192, 64, 4, 2),
+                                              ("q8_0", 256, 0, 16, 2), ("q8_0", 128, 0, 4, 4),
+                                              ("q8_0", 64, 0, 6, 3)])
 def test_decode_edge_lengths(dtype, D, R, Hq, Hkv):
     # klen 0, 1, one page, page +- 1, 1024 and 2048 +- 1 (split boundaries for
     # the split sizes these shapes get: multiples of 64 that divide them) and a
