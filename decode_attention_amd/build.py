@@ -12,6 +12,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhkv.so")
+# Measurement aid for the benchmark (a streaming-read probe), not the library.
+PROBE_LIB = os.path.join(HERE, "libhkv_probe.so")
 ARCH = os.environ.get("HKV_OFFLOAD_ARCH", "gfx950")
 
 
@@ -30,6 +32,13 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    probe = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-o", PROBE_LIB + ".tmp", os.path.join(HERE, "probe", "hkv_probe.hip")]
+    if verbose:
+        print(" ".join(probe))
+    subprocess.run(probe, check=True)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 

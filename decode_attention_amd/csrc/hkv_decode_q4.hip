@@ -73,9 +73,6 @@ __device__ __forceinline__ float max_xor16_32(float v) {
 __device__ __forceinline__ float f16lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float f16hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& c, int i) {
-  return i == 0 ? c.x : i == 1 ? c.y : i == 2 ? c.z : c.w;
-}
 
 struct Tile {
   uint4 k0, k1, v0, v1, sc;
@@ -107,15 +104,20 @@ struct __align__(16) Q4Lds {
     struct {
       uint32_t kt[kQWaves][2][kT][kKStride];           // [tile of unit][token][word * 8 + block]
       uint32_t vt[kQWaves][2][2][kNB][4][kVStride];    // [buf][tile][block][word][token]
-      uint32_t st[kQWaves][2][2][2][4][kT];            // [buf][tile][K|V][scale word][token]
-      uint32_t st_dup[kQWaves][4][2 * kT];             // stores of lanes 32-63 (never read)
+      // fp16 block scales, block-major: [buf][K|V][block][token group g][tile][token
+      // 4g..4g+3], so one lane's eight V scales of a block (both tiles) are 16
+      // contiguous bytes and its four K scales of a block and tile are 8
+      uint16_t sh[kQWaves][2][2][kNB][4][2][4];
+      uint16_t sh_dup[kQWaves][kNB][32];               // stores of lanes 32-63 (never read)
     } s;
     float ob[kQWaves][kRows][kD];  // wave merge, after the stream
   } u;
 };
 
-static_assert(sizeof(Q4Lds::u.s.st[0][0][0]) == 2 * 4 * kT * sizeof(uint32_t),
-              "scale tile stride");
+static_assert(sizeof(Q4Lds::u.s.sh[0][0][0][0]) == 4 * 2 * 4 * sizeof(uint16_t),
+              "scale block stride");
+static_assert(sizeof(Q4Lds::u.s.sh_dup[0][0]) == sizeof(Q4Lds::u.s.sh[0][0][0][0]),
+              "dummy scale rows share the block stride");
 static_assert(sizeof(Q4Lds::u.s.vt[0][0][0]) == kNB * 4 * kVStride * sizeof(uint32_t),
               "V tile stride");
 
@@ -282,14 +284,18 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
       vw[((4 + gq) * 4 + 1) * kVStride] = x.v1.y;
       vw[((4 + gq) * 4 + 2) * kVStride] = x.v1.z;
       vw[((4 + gq) * 4 + 3) * kVStride] = x.v1.w;
-      {  // lanes 32-63 hold copies of lanes 0-31's chunks: they store to a dummy row
-        uint32_t* sw = lane < 32 ? &L.u.s.st[wave][buf][half][scale_kind][0][tl]
-                                 : &L.u.s.st_dup[wave][0][lane - 32];
-        const int ss = lane < 32 ? kT : 2 * kT;
-        sw[0 * ss] = x.sc.x;
-        sw[1 * ss] = x.sc.y;
-        sw[2 * ss] = x.sc.z;
-        sw[3 * ss] = x.sc.w;
+      {  // lanes 32-63 hold copies of lanes 0-31's chunks: they store to dummy rows
+        uint16_t* sw = lane < 32 ? &L.u.s.sh[wave][buf][scale_kind][0][tl >> 2][half][tl & 3]
+                                 : &L.u.s.sh_dup[wave][0][lane - 32];
+        constexpr int sb = 4 * 2 * 4;  // halves per block, real and dummy rows alike
+        sw[0 * sb] = (uint16_t)x.sc.x;
+        sw[1 * sb] = (uint16_t)(x.sc.x >> 16);
+        sw[2 * sb] = (uint16_t)x.sc.y;
+        sw[3 * sb] = (uint16_t)(x.sc.y >> 16);
+        sw[4 * sb] = (uint16_t)x.sc.z;
+        sw[5 * sb] = (uint16_t)(x.sc.z >> 16);
+        sw[6 * sb] = (uint16_t)x.sc.w;
+        sw[7 * sb] = (uint16_t)(x.sc.w >> 16);
       }
       wave_sync_lds();
       // Word g of every block of token n: the A operand of 8 score MFMAs.
@@ -310,8 +316,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
       const int4_t zero4 = {0, 0, 0, 0};
 #pragma unroll
       for (int bp = bp0; bp < bp0 + 2; ++bp) {
-        // K scale words of blocks 2bp, 2bp + 1 for tokens 4g..4g+3.
-        const uint4 kw4 = lds_u4(&L.u.s.st[wave][buf][half][0][bp][4 * g]);
+        // K scales of blocks 2bp, 2bp + 1 for tokens 4g..4g+3 of this tile.
+        const uint2 ks[2] = {*(const uint2*)&L.u.s.sh[wave][buf][0][2 * bp][g][half][0],
+                             *(const uint2*)&L.u.s.sh[wave][buf][0][2 * bp + 1][g][half][0]};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int b = 2 * bp + h;
@@ -323,8 +330,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
                                                                  qreg[b], zero4, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const uint32_t w = word_of(kw4, i);
-            st.acc[i] = fmaf((float)C[i], h ? f16hi(w) : f16lo(w), st.acc[i]);
+            const uint32_t w = i < 2 ? ks[h].x : ks[h].y;
+            st.acc[i] = fmaf((float)C[i], (i & 1) ? f16hi(w) : f16lo(w), st.acc[i]);
           }
         }
       }
@@ -409,17 +416,13 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
       const half8_t c72 = {(_Float16)-72.0f, (_Float16)-72.0f, (_Float16)-72.0f,
                            (_Float16)-72.0f, (_Float16)-72.0f, (_Float16)-72.0f,
                            (_Float16)-72.0f, (_Float16)-72.0f};
-      constexpr uint32_t kSel[2] = {0x05040100u, 0x07060302u};
       // Per-lane bases: tile 0 of the unit; tile 1 and the blocks are constant offsets.
       const uint32_t* vbase = &L.u.s.vt[wave][buf][0][0][n >> 2][4 * g];
-      const uint32_t* sbase = &L.u.s.st[wave][buf][0][1][0][4 * g];
-      constexpr int kStTile = 2 * 4 * kT;         // st: dwords per tile
+      const uint16_t* sbase = &L.u.s.sh[wave][buf][1][0][g][0][0];
+      constexpr int kShBlock = 4 * 2 * 4;          // sh: halves per block
       constexpr int kVtTile = kNB * 4 * kVStride;  // vt: dwords per tile
 #pragma unroll
       for (int bp = bp0; bp < bp0 + nbp; ++bp) {
-        // V scale words of blocks 2bp, 2bp + 1 for tokens 4g..4g+3 of both tiles.
-        const uint4 sa = lds_u4(sbase + bp * kT);
-        const uint4 sb = lds_u4(sbase + bp * kT + kStTile);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int b = 2 * bp + h;
@@ -436,11 +439,10 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
                             (x2 & mf0) | 0x64006400u, (x3 & mf0) | 0x64006400u};
           const half8_t lo = __builtin_bit_cast(half8_t, lw) + c1032;
           const half8_t hi = __builtin_elementwise_fma(__builtin_bit_cast(half8_t, hw), c16, c72);
+          // V scales of block b for tokens 4g..4g+3 of both tiles, in the k order
+          // of the A operand.
           const half8_t dv = __builtin_bit_cast(
-              half8_t, (uint4){__builtin_amdgcn_perm(sa.y, sa.x, kSel[h]),
-                               __builtin_amdgcn_perm(sa.w, sa.z, kSel[h]),
-                               __builtin_amdgcn_perm(sb.y, sb.x, kSel[h]),
-                               __builtin_amdgcn_perm(sb.w, sb.z, kSel[h])});
+              half8_t, lds_u4((const uint32_t*)(sbase + (2 * bp + h) * kShBlock)));
           const half8_t loh = lo * dv, hih = hi * dv;
           const half8_t lol = __builtin_elementwise_fma(lo, dv, -loh);
           const half8_t hil = __builtin_elementwise_fma(hi, dv, -hih);

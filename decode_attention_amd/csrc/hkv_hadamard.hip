@@ -11,7 +11,8 @@
 //
 // Blocks are independent and contiguous, so the kernel walks a flat array of
 // blocks, 16 lanes to a block and four blocks per wave (the layout of
-// fwht_rows16), loading the next four while it transforms the current ones.
+// fwht_rows16), with the loads of the next two groups of four in flight
+// while it transforms the current one.
 // Each lane loads and stores 16 contiguous bytes per 64-wide group.
 #include <cmath>
 
@@ -59,62 +60,88 @@ __device__ __forceinline__ void had_signs(const uint32_t* sign_bits, int pos, ui
   }
 }
 
-// nblk = rows * n / B blocks; block b is row b / bpr, position b % bpr.
+// Rotates the four blocks whose raw words are in r (this lane-row's block
+// `cur`) and stores them.
+template <int Q, bool F16, bool SIGNS, bool INV>
+__device__ __forceinline__ void had_block(const uint32_t (&r)[Q][F16 ? 2 : 4], int64_t cur,
+                                          int64_t nblk, int bpr, float norm,
+                                          const uint32_t* sign_bits, float* y) {
+  const int l = lane_id() & 15;
+  float v[Q][4];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    if (F16) {
+      v[q][0] = h2f((uint16_t)r[q][0]);
+      v[q][1] = h2f((uint16_t)(r[q][0] >> 16));
+      v[q][2] = h2f((uint16_t)r[q][1]);
+      v[q][3] = h2f((uint16_t)(r[q][1] >> 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[q][i] = __uint_as_float(r[q][i]);
+    }
+  }
+  uint32_t sm[Q][4];
+  if (SIGNS) {
+    const int64_t c = min(cur, nblk - 1);
+    const int pos = (c >> 31) == 0 ? (int)((uint32_t)c % (uint32_t)bpr) : (int)(c % bpr);
+    had_signs<Q>(sign_bits, pos, sm);
+  }
+  if (SIGNS && !INV) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[q][i] = __uint_as_float(__float_as_uint(v[q][i]) ^ sm[q][i]);
+  }
+  fwht_rows16<Q>(v, norm);
+  if (SIGNS && INV) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[q][i] = __uint_as_float(__float_as_uint(v[q][i]) ^ sm[q][i]);
+  }
+  if (cur < nblk) {
+    float4* p = (float4*)(y + cur * (64 * Q) + 4 * l);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) p[16 * q] = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
+  }
+}
+
+// nblk = rows * n / B blocks; block b is row b / bpr, position b % bpr.  Each
+// wave keeps two groups of four blocks in flight: while it rotates one, the
+// loads of the next two are outstanding.
 template <int Q, bool F16, bool SIGNS, bool INV>
 __global__ __launch_bounds__(kHadWaves * kWave) void hadamard_kernel(
     const void* x, float* y, int64_t nblk, int bpr, float norm, const uint32_t* sign_bits) {
   constexpr int R = F16 ? 2 : 4;
   const int lane = lane_id();
-  const int l = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t stride = (int64_t)gridDim.x * kHadWaves * 4;
   int64_t base = ((int64_t)blockIdx.x * kHadWaves + wave) * 4;
   if (base >= nblk) return;
   int64_t blk = base + (lane >> 4);
-  uint32_t r[Q][R];
-  had_load<Q, F16>(x, min(blk, nblk - 1), r);
+  uint32_t ra[Q][R], rb[Q][R];
+  had_load<Q, F16>(x, min(blk, nblk - 1), ra);
+  if (base + stride < nblk) had_load<Q, F16>(x, min(blk + stride, nblk - 1), rb);
   for (;;) {
-    float v[Q][4];
+    // group at `base` is in ra, group at base + stride (if any) in rb
+    uint32_t cur[Q][R];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      if (F16) {
-        v[q][0] = h2f((uint16_t)r[q][0]);
-        v[q][1] = h2f((uint16_t)(r[q][0] >> 16));
-        v[q][2] = h2f((uint16_t)r[q][1]);
-        v[q][3] = h2f((uint16_t)(r[q][1] >> 16));
-      } else {
+    for (int q = 0; q < Q; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[q][i] = __uint_as_float(r[q][i]);
-      }
-    }
-    const int64_t cur = blk;
+      for (int i = 0; i < R; ++i) cur[q][i] = ra[q][i];
+    if (base + 2 * stride < nblk) had_load<Q, F16>(x, min(blk + 2 * stride, nblk - 1), ra);
+    had_block<Q, F16, SIGNS, INV>(cur, blk, nblk, bpr, norm, sign_bits, y);
     base += stride;
     blk += stride;
-    if (base < nblk) had_load<Q, F16>(x, min(blk, nblk - 1), r);  // next four blocks in flight
-    uint32_t sm[Q][4];
-    if (SIGNS) {
-      const int64_t c = min(cur, nblk - 1);
-      const int pos = (c >> 31) == 0 ? (int)((uint32_t)c % (uint32_t)bpr) : (int)(c % bpr);
-      had_signs<Q>(sign_bits, pos, sm);
-    }
-    if (SIGNS && !INV) {
+    if (base >= nblk) break;
 #pragma unroll
-      for (int q = 0; q < Q; ++q)
+    for (int q = 0; q < Q; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[q][i] = __uint_as_float(__float_as_uint(v[q][i]) ^ sm[q][i]);
-    }
-    fwht_rows16<Q>(v, norm);
-    if (SIGNS && INV) {
-#pragma unroll
-      for (int q = 0; q < Q; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[q][i] = __uint_as_float(__float_as_uint(v[q][i]) ^ sm[q][i]);
-    }
-    if (cur < nblk) {
-      float4* p = (float4*)(y + cur * (64 * Q) + 4 * l);
-#pragma unroll
-      for (int q = 0; q < Q; ++q) p[16 * q] = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
-    }
+      for (int i = 0; i < R; ++i) cur[q][i] = rb[q][i];
+    if (base + 2 * stride < nblk) had_load<Q, F16>(x, min(blk + 2 * stride, nblk - 1), rb);
+    had_block<Q, F16, SIGNS, INV>(cur, blk, nblk, bpr, norm, sign_bits, y);
+    base += stride;
+    blk += stride;
     if (base >= nblk) break;
   }
 }

@@ -68,3 +68,17 @@ def test_hadamard_is_the_cache_rotation():
     got = hkv.hadamard(torch.from_numpy(np.ascontiguousarray(kr.reshape(40, 128))).to(DEV), 64,
                        bits, True)
     assert np.array_equal(got.cpu().numpy().view(np.uint32), ku.reshape(40, 128).view(np.uint32))
+
+
+@pytest.mark.parametrize("in_dtype", [np.float32, np.float16])
+def test_hadamard_many_blocks(in_dtype):
+    """More blocks than one grid pass (2048 workgroups x 16 blocks): every
+    wave runs several loop iterations with two groups of loads in flight,
+    and the last group is ragged."""
+    rng = np.random.default_rng(77)
+    rows, n, block = 40001, 128, 64                   # 80002 blocks
+    x = rng.standard_normal((rows, n)).astype(in_dtype)
+    bits = rng.integers(-2**31, 2**31, n // 32, dtype=np.int64).astype(np.int32)
+    y = hkv.hadamard(torch.from_numpy(x).to(DEV), block, torch.from_numpy(bits).to(DEV), False)
+    ref = _ref(x.astype(np.float32), block, bits, False)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))

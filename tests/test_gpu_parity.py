@@ -160,6 +160,27 @@ def test_quantize_many_rows(dtype, D, in_dtype, misaligned):
     assert np.all(flat[untouched] == 0xA5)
 
 
+@pytest.mark.parametrize("dtype", ["q4_0", "q8_0"])
+def test_quantize_many_rows_several_passes(dtype):
+    """More rows than one grid pass of the 16-lanes-per-row kernel (2048
+    workgroups x 16 rows): waves loop, loading the next rows during the
+    current ones; ragged end."""
+    rng = np.random.default_rng(88)
+    T, H, P, D = 17003, 2, 16, 256                     # 34006 rows
+    k = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(np.float16)
+    v = rng.standard_normal((T, H, D)).astype(np.float16)
+    f = hkv.format_init(dtype, D, 0, P)
+    fo = O.format_init(dtype, D, 0)
+    pages = (T + P - 1) // P
+    sm = rng.permutation(pages * P)[:T].astype(np.int64)
+    cache = hkv.new_cache(f, pages, H, DEV)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    got = cache.cpu().numpy()
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    assert np.array_equal(got[sm // P, :, sm % P], slots)
+
+
 @pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
 def test_decode_matches_oracle(ci):
     cfg = W.CONFIGS[ci]
