@@ -580,6 +580,310 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Octave quantize-append for many rows, in the 16-lanes-per-row layout of the
+// kernel above (lane l of a 16-lane row holds elements 64q + 4l + i).
+//
+// Division.  The oracle's y = (x / rms) * mult needs the correctly rounded
+// x / rms for every element.  With y_r = RN(1/rms), q0 = RN(x * y_r) and the
+// exact remainder fma(-rms, q0, x), q = fma(remainder, y_r, q0) is that
+// quotient (Markstein's theorem for round to nearest, which assumes no
+// underflow); a quotient below 2^-100 is recomputed with the division.
+//
+// Codes.  The code is #{k : mid_k < y} with mid_k = (LUT[k] + LUT[k+1]) / 2,
+// i.e. #{k : T_k < 2y} for the integers T_k = LUT[k] + LUT[k+1], which is
+// #{k : T_k <= n} for the integer n = ceil(2y) - 1.  A table indexed by n
+// (clamped to [-256, 255], which holds every T_k) gives the code in its low
+// byte and LUT[code] in its high byte.  2y = RN(q * 2 mult) exactly, since
+// doubling commutes with rounding.
+
+struct OctTables {
+  uint16_t t3[512];
+  uint16_t t4[512];
+};
+
+__device__ void oct_tables_fill(OctTables& T) {
+  for (int e = threadIdx.x; e < 1024; e += blockDim.x) {
+    const int n = (e & 511) - 256;
+    int c = 0, lv;
+    if (e < 512) {
+#pragma unroll
+      for (int k = 0; k < 7; ++k) c += (kLut3[k] + kLut3[k + 1] <= n) ? 1 : 0;
+      lv = kLut3[c];
+      T.t3[e] = (uint16_t)(c | ((lv & 0xFF) << 8));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 15; ++k) c += (kLut4[k] + kLut4[k + 1] <= n) ? 1 : 0;
+      lv = kLut4[c];
+      T.t4[e - 512] = (uint16_t)(c | ((lv & 0xFF) << 8));
+    }
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t oct_code(const OctTables& T, float z, float* lv) {
+  int n = (int)ceilf(z) - 1;
+  n = min(max(n, -256), 255);
+  const uint32_t e = (BITS == 3 ? T.t3 : T.t4)[n + 256];
+  *lv = (float)(int)(int8_t)(uint8_t)(e >> 8);
+  return e & 0xFFu;
+}
+
+// fwht_rows16 for a transform block of 64 or 64Q values (the group stages
+// run only below the block).
+template <int Q>
+__device__ __forceinline__ void fwht_rows16b(float (&x)[Q][4], int block, float norm) {
+  const int l = lane_id() & 15;
+#pragma unroll
+  for (int h = 1; h <= 2; h <<= 1)
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((i & h) == 0) {
+          const float a = x[q][i], b = x[q][i + h];
+          x[q][i] = a + b;
+          x[q][i + h] = a - b;
+        }
+#pragma unroll
+  for (int m = 1; m <= 8; m <<= 1) {
+    const float sgn = (l & m) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[q][i] = fmaf(x[q][i], sgn, shfl_xor(x[q][i], m));
+  }
+#pragma unroll
+  for (int hq = 1; hq < Q; hq <<= 1) {
+    if (64 * hq < block) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if ((q & hq) == 0 && q + hq < Q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = x[q][i], b = x[q + hq][i];
+            x[q][i] = a + b;
+            x[q + hq][i] = a - b;
+          }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * norm;
+}
+
+// Sum of t over groups [q0, q0 + NQ) of one 16-lane row in the oracle's
+// tree order: groups first (halving when NQ is a power of two, else left to
+// right), then element strides 32, 16, 8, 4 (lanes 8, 4, 2, 1), then 2, 1
+// (registers).  Every lane of the row ends with the sum.
+template <int Q, int NQ>
+__device__ __forceinline__ float tree16(const float (&t)[Q][4], int q0) {
+  float u[4];
+  if constexpr ((NQ & (NQ - 1)) == 0) {
+    float w[NQ][4];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[q][i] = t[q0 + q][i];
+#pragma unroll
+    for (int h = NQ / 2; h >= 1; h >>= 1)
+#pragma unroll
+      for (int q = 0; q < h; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[q][i] = w[q][i] + w[q + h][i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = w[0][i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u[i] = t[q0][i];
+#pragma unroll
+      for (int q = 1; q < NQ; ++q) u[i] = u[i] + t[q0 + q][i];
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = u[i] + shfl_xor(u[i], m);
+  const float a = u[0] + u[2], b = u[1] + u[3];
+  return a + b;
+}
+
+// [OCT] _quantize_lut over groups [q0, q0 + NQ) of a row; codes into
+// codes[q0 ..]; returns the fp16 bits of the scale (the same in the row).
+template <int Q, int NQ, int BITS>
+__device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float (&x)[Q][4], int q0,
+                                                uint32_t (&codes)[Q][4]) {
+  float t[Q][4];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[q][i] = x[q][i] * x[q][i];
+  const float ss = tree16<Q, NQ>(t, q0);
+  float rms = sqrtf(ss / (float)(NQ * kWave));
+  rms = rms < 1e-12f ? 1e-12f : rms;
+  const float ry = 1.0f / rms;
+  float qv[NQ][4];
+  bool tiny = false;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float xv = x[q0 + q][i];
+      const float q0v = xv * ry;
+      const float r = fmaf(-rms, q0v, xv);
+      qv[q][i] = fmaf(r, ry, q0v);
+      tiny |= xv != 0.0f && fabsf(qv[q][i]) < 0x1p-100f;
+    }
+  if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xv = x[q0 + q][i];
+        if (xv != 0.0f && fabsf(qv[q][i]) < 0x1p-100f) qv[q][i] = xv / rms;
+      }
+  }
+  const float m2 = (float)(2 * (BITS == 3 ? kLutMult3 : kLutMult4));
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float lv;
+      codes[q0 + q][i] = oct_code<BITS>(T, qv[q][i] * m2, &lv);
+      t[q0 + q][i] = x[q0 + q][i] * lv;
+    }
+  const float dot = tree16<Q, NQ>(t, q0);
+  float sc = 0.0f;
+  if (dot > 0.0f) sc = ss / (dot > 1e-30f ? dot : 1e-30f);
+  return f2h(sc * (float)kLutOne);
+}
+
+// Slot words of one group's codes (segment-relative group qq, segment of n
+// codes starting at word w0), stored by the lanes that hold them.
+__device__ __forceinline__ void store4_16(uint32_t* dst, int w0, int qq, const uint32_t (&c)[4]) {
+  const int l = lane_id() & 15;
+  const uint32_t bytes = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  const uint32_t w = bytes | (dpp<0xB1>(bytes) << 4);  // odd lane: the high nibbles
+  if ((l & 1) == 0) dst[w0 + 8 * qq + (l >> 1)] = w;
+}
+__device__ __forceinline__ void store3_16(uint32_t* dst, int w0, int n, int qq,
+                                          const uint32_t (&c)[4]) {
+  const int l = lane_id() & 15;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo |= (c[j] & 3u) << (8 * j);
+    hi |= ((c[j] >> 2) & 1u) << (8 * j);
+  }
+  lo = or_quad(lo << (2 * (l & 3)));                    // low plane: 4 lanes a word
+  hi <<= (l & 7);
+  hi = or_quad(hi);
+  hi |= dpp<0x141>(hi);                                 // high plane: 8 lanes a word
+  if ((l & 3) == 0) dst[w0 + 4 * qq + (l >> 2)] = lo;
+  if ((l & 7) == 0) dst[w0 + n / 16 + 2 * qq + (l >> 3)] = hi;
+}
+
+// rows as for quantize_append_kernel; key/value 8-byte (f16) or 16-byte (f32)
+// aligned; D = 64Q.
+template <int Q, bool F16>
+__global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kernel(
+    DevFmt f, const void* key, const void* value, int rows, int num_kv_heads,
+    const int64_t* slot_mapping, uint8_t* cache) {
+  __shared__ OctTables T;
+  oct_tables_fill(T);
+  __syncthreads();
+  constexpr int R = F16 ? 2 : 4;
+  const int lane = lane_id();
+  const int l = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int stride = (int)gridDim.x * kQuantWaves * 4;
+  int base = ((int)blockIdx.x * kQuantWaves + wave) * 4;
+  if (base >= rows) return;
+  // sign masks of this lane's elements (the same in every row)
+  uint32_t smk[Q][4];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 64 * q + 4 * l + i;
+      smk[q][i] = ((f.sign_bits[d >> 5] >> (d & 31)) & 1u) << 31;
+    }
+  const int kw = f.k_wide / kWave;  // groups of 4-bit K codes
+  const int nks = f.num_k_scales;
+  const int nsw = (f.slot_bytes - f.off_scales) / 4;
+  uint32_t rk[Q][R], rv[Q][R];
+  int row = base + (lane >> 4);
+  fetch_rows16<Q, F16>(key, value, min(row, rows - 1), rk, rv);
+  int64_t sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
+  for (;;) {
+    float k[Q][4], v[Q][4];
+    widen16<Q, F16>(rk, k);
+    widen16<Q, F16>(rv, v);
+    const int cur = row;
+    const int64_t cur_sm = sm;
+    base += stride;
+    row += stride;
+    if (base < rows) {  // the next four rows load during this group
+      fetch_rows16<Q, F16>(key, value, min(row, rows - 1), rk, rv);
+      sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        k[q][i] = __uint_as_float(__float_as_uint(k[q][i]) ^ smk[q][i]);
+        v[q][i] = __uint_as_float(__float_as_uint(v[q][i]) ^ smk[q][i]);
+      }
+    fwht_rows16b<Q>(k, f.k_block, f.k_norm);
+    fwht_rows16b<Q>(v, f.v_block, f.v_norm);
+    uint32_t ck[Q][4], cv[Q][4], ks[Q];
+    if (f.compact) {
+      ks[0] = oct_block16<Q, Q, 3>(T, k, 0, ck);
+#pragma unroll
+      for (int q = 1; q < Q; ++q) ks[q] = 0;
+    } else {
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        ks[q] = (q < kw) ? oct_block16<Q, 1, 4>(T, k, q, ck) : oct_block16<Q, 1, 3>(T, k, q, ck);
+    }
+    const bool v4 = f.v_bits == 4;
+    const uint32_t vs = v4 ? oct_block16<Q, Q, 4>(T, v, 0, cv) : oct_block16<Q, Q, 3>(T, v, 0, cv);
+    // scale word w holds scales 2w and 2w + 1: K scales, the V scale, zeros
+    uint32_t sw = 0;
+#pragma unroll
+    for (int i = 0; i <= Q; ++i) {
+      const uint32_t sc = (i < nks) ? ks[i < Q ? i : 0] : (i == nks ? vs : 0u);
+      sw |= (l == (i >> 1)) ? (sc << (16 * (i & 1))) : 0u;
+    }
+    if (cur_sm >= 0) {
+      int64_t page;
+      int off;
+      if ((cur_sm >> 32) == 0) {
+        const uint32_t s32 = (uint32_t)cur_sm;
+        page = s32 / (uint32_t)f.page_size;
+        off = (int)(s32 % (uint32_t)f.page_size);
+      } else {
+        page = cur_sm / f.page_size;
+        off = (int)(cur_sm % f.page_size);
+      }
+      uint32_t* dst =
+          (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, cur % num_kv_heads);
+      const int wk3 = f.off_k_nope / 4, nk3 = kWave * (Q - kw), wv0 = f.off_v / 4;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        if (q < kw) store4_16(dst, 0, q, ck[q]);
+        else store3_16(dst, wk3, nk3, q - kw, ck[q]);
+        if (v4) store4_16(dst, wv0, q, cv[q]);
+        else store3_16(dst, wv0, kWave * Q, q, cv[q]);
+      }
+      if (l < nsw) dst[f.off_scales / 4 + l] = sw;
+    }
+    if (base >= rows) break;
+  }
+}
+
 template <int E>
 __global__ __launch_bounds__(64) void dequantize_kernel(DevFmt f, const uint8_t* cache,
                                                         int num_kv_heads,
@@ -663,6 +967,25 @@ hipError_t launch_quantize_append(const DevFmt& f, const void* key, const void* 
     }
 #undef HKV_Q16
 #undef HKV_Q16K
+    return hipGetLastError();
+  }
+  if (!q4 && !q8 && rows >= kRows16MinRows && ((uintptr_t)key % align) == 0 &&
+      ((uintptr_t)value % align) == 0) {
+    const int64_t g16 = (rows + 4 * kQuantWaves - 1) / (4 * kQuantWaves);
+    const dim3 grid16((unsigned)(g16 < kQuantMaxGroups ? g16 : kQuantMaxGroups));
+#define HKV_O16(Q_)                                                                           \
+  (in_f16 ? (quantize_oct_rows16_kernel<Q_, true><<<grid16, block, 0, s>>>(                   \
+                f, key, value, r, num_kv_heads, slot_mapping, cache))                         \
+          : (quantize_oct_rows16_kernel<Q_, false><<<grid16, block, 0, s>>>(                  \
+                f, key, value, r, num_kv_heads, slot_mapping, cache)))
+    switch (f.D / kWave) {
+      case 1: HKV_O16(1); break;
+      case 2: HKV_O16(2); break;
+      case 3: HKV_O16(3); break;
+      case 4: HKV_O16(4); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef HKV_O16
     return hipGetLastError();
   }
 #define HKV_QA1(E_, F16_, Q4_)                                                         \

@@ -115,16 +115,23 @@ def test_quantize_and_dequantize_formats(dtype, D, R, in_dtype):
         assert np.all(kd[~keep] == 0) and np.all(vd[~keep] == 0)
 
 
-@pytest.mark.parametrize("dtype", ["q4_0", "q8_0"])
-@pytest.mark.parametrize("D", [64, 128, 256])
+MANY_ROW_FORMATS = [("q4_0", 64, 0), ("q4_0", 128, 0), ("q4_0", 256, 0),
+                    ("q8_0", 64, 0), ("q8_0", 128, 0), ("q8_0", 256, 0),
+                    ("octave_k3v4", 128, 64), ("octave_k3v3", 128, 64),
+                    ("octave_k3v3_compact", 256, 64), ("octave_k3v3_compact", 64, 0),
+                    ("octave_k3v4", 192, 64), ("octave_k3v4", 256, 128),
+                    ("octave_k3v4", 128, 0), ("octave_k3v4", 128, 128)]
+
+
+@pytest.mark.parametrize("dtype,D,R", MANY_ROW_FORMATS)
 @pytest.mark.parametrize("in_dtype", [np.float32, np.float16])
 @pytest.mark.parametrize("misaligned", [False, True])
-def test_quantize_many_rows(dtype, D, in_dtype, misaligned):
-    """Row counts that take the many-rows Q4_0 / Q8_0 kernel (16 lanes per
-    row, four rows per wave; a ragged last wave, skipped slots); a key/value
-    pointer off its 8/16-byte alignment takes the one-row-per-wave kernel
-    instead.  Both must give the oracle's bytes."""
-    rng = np.random.default_rng(7 * D + (3 if misaligned else 0) + (1 if dtype == "q8_0" else 0))
+def test_quantize_many_rows(dtype, D, R, in_dtype, misaligned):
+    """Row counts that take the many-rows kernels (16 lanes per row, four
+    rows per wave; a ragged last wave, skipped slots); a key/value pointer
+    off its 8/16-byte alignment takes the one-row-per-wave kernel instead.
+    Both must give the oracle's bytes."""
+    rng = np.random.default_rng(7 * D + R + (3 if misaligned else 0) + len(dtype))
     T, H, P = 1501, 3, 16                              # 4503 rows = 281 waves of 16 + 7
     k = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
     v = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
@@ -132,8 +139,8 @@ def test_quantize_many_rows(dtype, D, in_dtype, misaligned):
     v[9, 2] = 0
     k[11, 1, :32] = -np.abs(k[11, 1, :32]).max()     # max-abs ties inside one block
     k[11, 1, 3] = -k[11, 1, 3]
-    f = hkv.format_init(dtype, D, 0, P)
-    fo = O.format_init(dtype, D, 0)
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
     pages = (T + P - 1) // P + 2
     sm = rng.permutation(pages * P)[:T].astype(np.int64)
     sm[[0, 17, T - 1]] = -1
@@ -160,8 +167,9 @@ def test_quantize_many_rows(dtype, D, in_dtype, misaligned):
     assert np.all(flat[untouched] == 0xA5)
 
 
-@pytest.mark.parametrize("dtype", ["q4_0", "q8_0"])
-def test_quantize_many_rows_several_passes(dtype):
+@pytest.mark.parametrize("dtype,R", [("q4_0", 0), ("q8_0", 0), ("octave_k3v3_compact", 64),
+                                     ("octave_k3v4", 128)])
+def test_quantize_many_rows_several_passes(dtype, R):
     """More rows than one grid pass of the 16-lanes-per-row kernel (2048
     workgroups x 16 rows): waves loop, loading the next rows during the
     current ones; ragged end."""
@@ -169,8 +177,8 @@ def test_quantize_many_rows_several_passes(dtype):
     T, H, P, D = 17003, 2, 16, 256                     # 34006 rows
     k = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(np.float16)
     v = rng.standard_normal((T, H, D)).astype(np.float16)
-    f = hkv.format_init(dtype, D, 0, P)
-    fo = O.format_init(dtype, D, 0)
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
     pages = (T + P - 1) // P
     sm = rng.permutation(pages * P)[:T].astype(np.int64)
     cache = hkv.new_cache(f, pages, H, DEV)
