@@ -22,6 +22,7 @@
 #include "hkv_decode_common.h"
 
 #include <algorithm>
+#include <cstdint>
 
 namespace hkv {
 namespace {
@@ -101,14 +102,15 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DevFmt f, DecArgs a
 
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int split = blockIdx.x, kvh = blockIdx.y, gi = blockIdx.z;
+  int split, kvh, gi;
+  if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
   const int req = a.q_to_req[q0];
   int kmax = 0;
   for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(t_begin + a.tokens_per_split, kmax);
-  float* part = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits + split) * R * a.pstride;
+  float* part = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits + split) * R * a.pstride;
 
   if (t_begin >= t_end) {  // nothing to attend to in this split
     for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   const int klen = a.q_to_klen[i];
   const int n_live = klen <= 0 ? 0 : min(a.num_splits, (klen + a.tokens_per_split - 1) /
                                                            a.tokens_per_split);
-  const float* base = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride +
+  const float* base = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride +
                       (size_t)r * a.pstride;
   const size_t sstride = (size_t)Rp * a.pstride;
   float M = -INFINITY, L = 0.0f, acc[E];
@@ -444,6 +446,7 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   q.n_q = queries_per_seq;
   q.rows = q.group * q.n_q;
   q.num_groups = num_queries / queries_per_seq;
+  q.nsub = 1;
   auto mfma_kernel = [&](int rows) {
     return q4_mfma_supported(f, rows)   ? kKernelQ4
            : oct_mfma_rows(f, rows) > 0 ? kKernelOctK3v4
@@ -466,6 +469,7 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
           generic_lds_bytes(f, round_rows(q.group * nq)) <= 160 * 1024)
         best = nq;
     if (best) {
+      q.nsub = q.n_q / best;
       q.num_groups = num_queries / best;
       q.n_q = best;
       q.rows = q.group * best;
@@ -491,6 +495,12 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
     q.tokens_per_split = (int)std::min<int64_t>(cap, std::max<int64_t>(64, tps));
   }
   q.num_splits = max_klen > 0 ? (max_klen + q.tokens_per_split - 1) / q.tokens_per_split : 1;
+  // Grid sizes in work-items are 32-bit (512-lane workgroups at most).
+  const int64_t wgs = decode_wgs(q.num_groups, q.nsub, num_kv_heads, q.num_splits);
+  const int64_t merge_rows = (int64_t)q.num_groups * q.n_q * num_q_heads;
+  if (wgs * 512 > (int64_t)UINT32_MAX || merge_rows * kMergeWaves * kWave > (int64_t)UINT32_MAX)
+    return false;
+  q.num_wgs = wgs;
   q.partial_floats = kPartialHead + (size_t)f.D;
   const int R = q.rows_pad;
   q.workspace_bytes = sizeof(float) * q.partial_floats * R * (size_t)q.num_splits *
@@ -516,6 +526,8 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   a.rows = p.rows;
   a.rows_pad = p.rows_pad;
   a.num_queries = p.num_groups * p.n_q;
+  a.num_groups = p.num_groups;
+  a.nsub = p.nsub;
   a.cache = cache;
   a.block_table = block_table;
   a.max_pages = max_pages_per_req;
@@ -527,7 +539,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   a.ws = (float*)workspace;
   a.pstride = (int)p.partial_floats;
   const int R = round_rows(p.rows);
-  const dim3 grid(p.num_splits, num_kv_heads, p.num_groups);
+  const dim3 grid((unsigned)p.num_wgs);
   hipError_t e;
   if (p.kernel == kKernelQ4) {
     e = launch_decode_q4_mfma(f, a, grid, s);

@@ -20,6 +20,8 @@ struct DecArgs {
   int rows;
   int rows_pad;     // rows rounded up to the kernel's row count (partial records per split)
   int num_queries;
+  int num_groups;   // query groups of n_q queries (num_queries / n_q)
+  int nsub;         // groups per request when its queries are split into sub-groups, else 1
   const uint8_t* cache;
   const int32_t* block_table;
   int max_pages;
@@ -44,6 +46,41 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+
+// The (split, KV head, query group) of this workgroup; false for the few ids
+// past the last one.  Workgroup ids are dealt round-robin to the chip's 8
+// XCDs (id mod 8), so the id order decides which XCD streams what:
+//  * item w enumerates (request group, KV head) within a split, splits
+//    slowest, so every XCD takes every split of an even share of the
+//    requests (with the split index fastest, as in a (split, head, group)
+//    grid, an XCD would take one split of every request: with ragged
+//    lengths the XCD of split 0 does the most work and the late splits'
+//    XCDs sit idle);
+//  * id = 8 (nsub (w / 8) + s) + w % 8 gives the nsub sub-groups s of one
+//    request's queries, which read the same K/V, one XCD and consecutive
+//    dispatches there, so the second read of a tile can hit that XCD's L2.
+__device__ __forceinline__ bool wg_item(const DecArgs& a, int& split, int& kvh, int& gi) {
+  const uint32_t id = blockIdx.x;
+  const uint32_t hi = id >> 3;
+  const uint32_t nsub = (uint32_t)a.nsub;
+  const uint32_t s = hi % nsub;
+  const uint32_t w = 8u * (hi / nsub) + (id & 7u);
+  const uint32_t per_split = (uint32_t)(a.num_groups / a.nsub) * (uint32_t)a.num_kv_heads;
+  const uint32_t sp = w / per_split;
+  if (sp >= (uint32_t)a.num_splits) return false;
+  const uint32_t r = w - sp * per_split;
+  const uint32_t rg = r / (uint32_t)a.num_kv_heads;
+  split = (int)sp;
+  kvh = (int)(r - rg * (uint32_t)a.num_kv_heads);
+  gi = (int)(rg * nsub + s);
+  return true;
+}
+
+// Workgroups of a decode launch (see wg_item).
+inline int64_t decode_wgs(int num_groups, int nsub, int num_kv_heads, int num_splits) {
+  const int64_t items = (int64_t)(num_groups / nsub) * num_kv_heads * num_splits;
+  return 8 * (int64_t)nsub * ((items + 7) / 8);
+}
 
 // Partial record of one (query row, split): m, l, two pad words, o[D].
 constexpr int kPartialHead = 4;

@@ -162,7 +162,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
-  const int split = blockIdx.x, kvh = blockIdx.y, gi = blockIdx.z;
+  int split, kvh, gi;
+  if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
   // Query rows wave + 8 k: their loads go out first, independent of the page table.
   float qx[kQR][kE];
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(t_begin + a.tokens_per_split, kmax);
-  float* part = a.ws + ((size_t)(gi * a.num_kv_heads + kvh) * a.num_splits + split) * RM *
+  float* part = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits + split) * RM *
                            a.pstride;
   if (t_begin >= t_end) {
     for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {

@@ -30,6 +30,8 @@ struct DecodePlan {
   int rows;             // group * n_q rows sharing one KV head
   int rows_pad;         // rows of a partial record block (the kernel's row count)
   int num_groups;       // num_queries / n_q
+  int nsub;             // query groups per request (queries_per_seq / n_q)
+  int64_t num_wgs;      // workgroups of the decode kernel
   int tokens_per_split;
   int num_splits;
   size_t partial_floats;  // floats per (row, split) partial record
