@@ -39,6 +39,8 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // Slot layouts (slot words; vLLM docs, module text and OctaveFormat).
 struct FmtK3V4 {            // octave_k3v4, head size 128, rope 64
@@ -621,13 +623,377 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   }
 }
 
+
+// ---- 32 query rows per KV head (k3v3 compact, head size 256), one pass ----
+//
+// The rows of a sequence group sharing a KV head (up to 32) take every tile
+// once, so the codebook lookups of K and V are paid once for all of them.
+// Both products run on the 32 x 32 matrix-core shapes:
+//  * scores on v_mfma_i32_32x32x32_i8: A = the int8 codebook values of 32
+//    tokens x 32 dims (a lane: token l % 32, dims 16 (l / 32) .. + 15 of the
+//    block, which are one low-plane word of the token), B = one plane of the
+//    rotated query (32 dims x 32 rows), two planes into two accumulators.
+//    A lane ends with the scores of its row l % 32 for tokens
+//    8 j + 4 (l / 32) + i, j, i < 4: the very k-slots that lane supplies as
+//    the B operand of P.V, so p never moves between lanes.
+//  * P.V on v_mfma_f32_32x32x16_f16 as O^T = V^T P^T (rows = dims, columns =
+//    query rows), 8 tokens per step: a lane's k-slots are its 4 tokens'
+//    fp16(p s) and their residuals x 2^12, against the tokens' values and
+//    values x 2^-12.  The values enter biased, as the fp16 1024 + (LUT[c] +
+//    128) (and that x 2^-12, the same byte under an exponent 2^-2), so each
+//    takes one v_perm_b32; the bias is removed at the end with the running
+//    sum of p s per row.
+//  * V dims: tile (b, i) of 32 dims has row a = 4 m' + j holding dim
+//    16 (8 b + m') + 4 i + j; a lane gathers byte j of low-plane word 8 b + m'
+//    of its 4 tokens once and takes the codes of all four i from it.
+constexpr int kR32 = 32;
+constexpr int kOB = 65;  // row stride (floats) of the cross-wave sum: 64 values + pad
+
+struct __align__(16) Oct32Lds {
+  static constexpr int kWords = 48;  // code words of a compact slot (the scale word is staged as floats)
+  int8_t qB[2][8][kR32][32];         // [plane][32-dim block][row][dim in block]
+  float qsc[kR32];
+  float mlw[kQWaves][kR32][2];
+  int pid[kMaxSplitTiles];
+  int next_unit;
+  int pad_[3];
+  union {
+    struct {
+      uint32_t tt[kQWaves][2][kWords][kTS];  // [tile][slot word][token], one unit per wave
+      float sc[kQWaves][2][2][kT];           // [tile][K | V][token] scales as fp32
+    } s;
+    float ob[kQWaves][2][kR32][kOB];         // [wave][l / 32][row][value] for one half of the dims
+  } u;
+};
+
+__global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt f, DecArgs a) {
+  using F = FmtK3V3C;
+  constexpr int kD = F::kD;
+  constexpr int kSlot = F::kSlot;
+  constexpr int kE = kD / kWave;
+  constexpr int kQR = kR32 / kQWaves;  // query rows set up per wave
+  __shared__ Oct32Lds L;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  int split, kvh, gi;
+  if (!wg_item(a, split, kvh, gi)) return;
+  const int q0 = gi * a.n_q;
+  float qx[kQR][kE];
+#pragma unroll
+  for (int k = 0; k < kQR; ++k) {
+    const int r = wave + kQWaves * k;
+    if (r < a.rows) {
+      const int j = r / a.group, g = r % a.group;
+      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        const int d = kWave * e + lane;
+        qx[k][e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
+                           : ((const float*)a.query)[qrow * kD + d];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kE; ++e) qx[k][e] = 0.0f;
+    }
+  }
+  const int req = a.q_to_req[q0];
+  int kmax = 0, kmin = INT32_MAX;
+  for (int j = 0; j < a.n_q; ++j) {
+    kmax = max(kmax, a.q_to_klen[q0 + j]);
+    kmin = min(kmin, a.q_to_klen[q0 + j]);
+  }
+  const int t_begin = split * a.tokens_per_split;
+  const int t_end = min(t_begin + a.tokens_per_split, kmax);
+  float* part = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits + split) * kR32 *
+                           a.pstride;
+  if (t_begin >= t_end) {
+    for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
+      part[r * a.pstride + 0] = -INFINITY;
+      part[r * a.pstride + 1] = 0.0f;
+    }
+    return;
+  }
+
+  // ---- page ids, first unit, query planes ---------------------------------
+  const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
+  const int ps = f.page_size;
+  const int ps_shift = 31 - __builtin_clz(ps);
+  const int nt = (t_end - t_begin + kT - 1) / kT;
+  const int nu = (nt + 1) >> 1;
+  for (int t = threadIdx.x; t < nt; t += blockDim.x) L.pid[t] = bt[(t_begin + kT * t) >> ps_shift];
+  if (threadIdx.x == 0) L.next_unit = kQWaves;
+  const int tl = lane & 15, gq = lane >> 4;
+  auto fetch_pid = [&](Tile& x, int kc, int page) {
+    const int t0 = t_begin + kT * kc;
+    const uint8_t* base = a.cache + ((((int64_t)page * a.num_kv_heads + kvh) << ps_shift) +
+                                     (t0 & (ps - 1))) * (int64_t)kSlot;
+    const uint8_t* slot = base + min(tl, t_end - 1 - t0) * kSlot;
+#pragma unroll
+    for (int i = 0; i < F::kChunks; ++i) x.c[i] = *(const uint4*)(slot + 16 * (4 * i + gq));
+    x.sw = *(const uint32_t*)(slot + 4 * F::kWScale);
+  };
+  auto fetch = [&](Tile& x, int k) {
+    const int kc = min(k, nt - 1);
+    fetch_pid(x, kc, __builtin_amdgcn_readfirstlane(L.pid[kc]));
+  };
+  Tile ta, tb;
+  const bool has_work = wave < nu;
+  if (has_work) {
+    const int k0 = 2 * wave, k1 = min(2 * wave + 1, nt - 1);
+    fetch_pid(ta, k0, bt[(t_begin + kT * k0) >> ps_shift]);
+    fetch_pid(tb, k1, bt[(t_begin + kT * k1) >> ps_shift]);
+  }
+#pragma unroll
+  for (int k = 0; k < kQR; ++k) {
+    const int r = wave + kQWaves * k;
+    float x[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+      x[e] = f.use_signs ? apply_sign(f, qx[k][e], kWave * e + lane) : qx[k][e];
+    if (r < a.rows) fwht_strided<kE>(x, f.k_block, f.k_norm);
+    float qmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
+    qmax = wave_max(qmax);
+    const float inv = qmax > 0.0f ? kQMax / qmax : 0.0f;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      int qi = (int)rintf(x[e] * inv);
+      qi = min(kQMaxI, max(-kQMaxI, qi));
+      const int hi = (qi + 128) >> 8;
+      const int lo = qi - hi * 256;
+      const int d = kWave * e + lane;
+      L.qB[0][d >> 5][r][d & 31] = (int8_t)hi;
+      L.qB[1][d >> 5][r][d & 31] = (int8_t)lo;
+    }
+    // 1/64: the codebook scale (LUT_ONE) of the K values.
+    if (lane == 0) L.qsc[r] = (qmax / kQMax) * a.q_scale * (1.0f / 64.0f);
+  }
+  const int n = lane & 31;  // this lane's query row (scores, P.V columns) and token (K operand)
+  const int h = lane >> 5;
+  const int klen_row = n < a.rows ? a.q_to_klen[q0 + n / a.group] : 0;
+  const int t_lim = min(t_end, kmin);
+  // V operand rows: dim 16 (8 b + m') + 4 i + j for row n = 4 m' + j.
+  const int vm = n >> 2, vj = n & 3;
+  const uint32_t gsel_lo = (uint32_t)vj | ((uint32_t)(vj + 4) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
+  const uint32_t gsel_hi = 0x0Cu | (0x0Cu << 8) | ((uint32_t)vj << 16) | ((uint32_t)(vj + 4) << 24);
+  const int vsh = 4 * (vm & 1);
+  __syncthreads();
+  const float qs = L.qsc[n];
+
+  f32x16 o[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[b][i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f, sps = 0.0f;
+
+  if (has_work) {
+    uint32_t* const tw = &L.u.s.tt[wave][0][0][0];
+    int u_cur = wave;
+    for (;;) {
+      // ---- stage the unit's two tiles (registers -> LDS, transposed) ----
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const Tile& x = hb ? tb : ta;
+        uint32_t* w = tw + hb * (Oct32Lds::kWords * kTS) + tl;
+#pragma unroll
+        for (int i = 0; i < F::kChunks; ++i) {
+          w[(16 * i + 4 * gq + 0) * kTS] = x.c[i].x;
+          w[(16 * i + 4 * gq + 1) * kTS] = x.c[i].y;
+          w[(16 * i + 4 * gq + 2) * kTS] = x.c[i].z;
+          w[(16 * i + 4 * gq + 3) * kTS] = x.c[i].w;
+        }
+        if (gq == 0) {
+          L.u.s.sc[wave][hb][0][tl] = h2f((uint16_t)(x.sw & 0xffffu));
+          L.u.s.sc[wave][hb][1][tl] = h2f((uint16_t)(x.sw >> 16));
+        }
+      }
+      wave_sync_lds();
+      int u_nxt = 0;
+      if (lane == 0) u_nxt = atomicAdd(&L.next_unit, 1);
+      u_nxt = __builtin_amdgcn_readfirstlane(u_nxt);
+      if (u_nxt < nu) {
+        fetch(ta, 2 * u_nxt);
+        fetch(tb, 2 * u_nxt + 1);
+      }
+
+      // ---- scores: 32 tokens x 32 rows ----
+      i32x16 chi = {}, clo = {};
+      {
+        const uint32_t* tk = tw + (n >> 4) * (Oct32Lds::kWords * kTS) + (n & 15);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t lw = tk[(2 * c + h) * kTS];
+          const uint32_t hw = tk[(F::kWKHi + c) * kTS] >> (4 * h);
+          int4_t A;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
+            A[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
+          }
+          const int4_t bh = *(const int4_t*)&L.qB[0][c][n][16 * h];
+          const int4_t bl = *(const int4_t*)&L.qB[1][c][n][16 * h];
+          chi = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, bh, chi, 0, 0, 0);
+          clo = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, bl, clo, 0, 0, 0);
+        }
+      }
+      // score k = 4 j + i: token 8 j + 4 h + i of the unit (tile j >> 1)
+      float s[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 ks = *(const float4*)&L.u.s.sc[wave][j >> 1][0][8 * (j & 1) + 4 * h];
+        const float kk[4] = {ks.x, ks.y, ks.z, ks.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[4 * j + i] = (float)(chi[4 * j + i] * 256 + clo[4 * j + i]) * kk[i] * qs;
+      }
+      const int t0 = t_begin + 2 * kT * u_cur;
+      if (!(t0 + 2 * kT <= t_lim)) {
+        asm volatile("" ::: "memory");  // keep this a branch: only edge units mask
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 8 * j + 4 * h + i;
+            s[4 * j + i] = (t < t_end && t < klen_row) ? s[4 * j + i] : -INFINITY;
+          }
+      }
+      float mt = s[0];
+#pragma unroll
+      for (int k = 1; k < 16; ++k) mt = fmaxf(mt, s[k]);
+      {
+        const uint32_t u = __float_as_uint(mt);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+        l_run *= alpha;
+        sps *= alpha;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+      // P operands: step j, k-slots 0-3 fp16(p s) of tokens 8 j + 4 h + i, 4-7 residuals x 2^12
+      half8_t P[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 vs = *(const float4*)&L.u.s.sc[wave][j >> 1][1][8 * (j & 1) + 4 * h];
+        const float vv[4] = {vs.x, vs.y, vs.z, vs.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(s[4 * j + i] - m_ref - 6.0f);  // p / 64
+          l_run += p;
+          const float pv = p * vv[i];
+          sps += pv;
+          const _Float16 hp = (_Float16)pv;
+          P[j][i] = hp;
+          P[j][4 + i] = (_Float16)(fmaf((float)hp, -1.0f, pv) * 4096.0f);
+        }
+      }
+
+      // ---- P.V: 8 accumulator tiles of 32 dims ----
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t* vt = tw + (j >> 1) * (Oct32Lds::kWords * kTS) + 8 * (j & 1) + 4 * h;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint4 wl = lds_u4(vt + (F::kWV + 8 * b + vm) * kTS);
+          const uint4 wh = lds_u4(vt + (F::kWVHi + 4 * b + (vm >> 1)) * kTS);
+          const uint32_t gl = __builtin_amdgcn_perm(wl.y, wl.x, gsel_lo) |
+                              __builtin_amdgcn_perm(wl.w, wl.z, gsel_hi);
+          const uint32_t gh = (__builtin_amdgcn_perm(wh.y, wh.x, gsel_lo) |
+                               __builtin_amdgcn_perm(wh.w, wh.z, gsel_hi)) >> vsh;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t sel = ((gl >> (2 * i)) & 0x03030303u) | (((gh >> i) << 2) & 0x04040404u);
+            const uint32_t x = __builtin_amdgcn_perm(kV3[1], kV3[0], sel);
+            const uint4 A = {__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
+                             __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u),
+                             __builtin_amdgcn_perm(0x34343434u, x, 0x04010400u),
+                             __builtin_amdgcn_perm(0x34343434u, x, 0x04030402u)};
+            o[4 * b + i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(half8_t, A), P[j], o[4 * b + i], 0, 0, 0);
+          }
+        }
+      }
+      if (u_nxt >= nu) break;
+      u_cur = u_nxt;
+    }
+  }
+
+  // ---- merge the waves ----------------------------------------------------
+  // This lane: row n, values of dims 16 (8 b + m') + 4 i + j for tile 4 b + i,
+  // register 4 jj + ii, with 4 m' + j = 8 jj + 4 h + ii.
+  float lsum, psum;
+  {
+    const uint32_t lu = __float_as_uint(l_run), pu = __float_as_uint(sps);
+    const auto ls = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
+    const auto pss = __builtin_amdgcn_permlane32_swap(pu, pu, false, false);
+    lsum = __uint_as_float(ls[0]) + __uint_as_float(ls[1]);
+    psum = __uint_as_float(pss[0]) + __uint_as_float(pss[1]);
+  }
+  if (h == 0) {
+    L.mlw[wave][n][0] = m_run;
+    L.mlw[wave][n][1] = lsum * 64.0f;  // p was kept as p / 64
+  }
+  __syncthreads();
+  float fw;
+  {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][n][0]);
+    fw = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
+  }
+  const float bias = 1152.0f * psum;  // the values entered as 1152 + LUT[c]
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if (b) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) L.u.ob[wave][h][n][16 * i + k] = (o[4 * b + i][k] - bias) * fw;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < a.rows * 128; idx += blockDim.x) {
+      const int r = idx >> 7, dd = idx & 127;
+      // dd = 16 m' + 4 i + j -> lane half (m' & 1), register 4 (m' >> 1) + j of tile i
+      const int mp = dd >> 4, i = (dd >> 2) & 3, j = dd & 3;
+      const int hh = mp & 1, k = 4 * (mp >> 1) + j;
+      float acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kQWaves; ++w) acc += L.u.ob[w][hh][r][16 * i + k];
+      part[r * a.pstride + kPartialHead + 128 * b + dd] = acc;
+    }
+  }
+  if (threadIdx.x < a.rows) {
+    const int r = threadIdx.x;
+    float M = -INFINITY, L_ = 0.0f;
+    for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
+    for (int w = 0; w < kQWaves; ++w) {
+      const float mw = L.mlw[w][r][0];
+      if (mw != -INFINITY) L_ += L.mlw[w][r][1] * exp2f(mw - M);
+    }
+    part[r * a.pstride + 0] = M;
+    part[r * a.pstride + 1] = L_;
+  }
+}
+
 }  // namespace
 
-// Rows the Octave MFMA kernel takes for this format: 8 or 16 (its row
-// mode), or 0 when the format or the row count is not one it handles.
+// Rows the Octave MFMA kernels take for this format: 8 or 16 (the row
+// mode), 32 (the compact layout's one-pass kernel), or 0 when the format
+// or the row count is not one they handle.
 int oct_mfma_rows(const DevFmt& f, int rows) {
   const bool pow2 = (f.page_size & (f.page_size - 1)) == 0;
-  if (f.kind != HKV_KIND_OCTAVE || rows > kRowsMax || f.page_size % kT != 0 || !pow2) return 0;
+  if (f.kind != HKV_KIND_OCTAVE || rows > (f.compact ? kR32 : kRowsMax) || f.page_size % kT != 0 ||
+      !pow2)
+    return 0;
   bool ok;
   if (!f.compact)
     ok = f.D == FmtK3V4::kD && f.k_wide == 64 && f.v_bits == 4 &&
@@ -639,7 +1005,7 @@ int oct_mfma_rows(const DevFmt& f, int rows) {
          f.off_v == 4 * FmtK3V3C::kWV && f.off_scales == 4 * FmtK3V3C::kWScale &&
          f.num_k_scales == 1 && f.k_block == FmtK3V3C::kD;
   if (!ok) return 0;
-  return rows <= 8 ? 8 : 16;
+  return rows <= 8 ? 8 : rows <= 16 ? 16 : 32;
 }
 
 hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
@@ -651,6 +1017,8 @@ hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipSt
   } else if (a.rows_pad == 16) {
     if (f.compact) decode_oct_kernel<FmtK3V3C, 16><<<grid, block, 0, s>>>(f, a);
     else decode_oct_kernel<FmtK3V4, 16><<<grid, block, 0, s>>>(f, a);
+  } else if (a.rows_pad == kR32 && f.compact) {
+    decode_oct32_kernel<<<grid, block, 0, s>>>(f, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -207,6 +207,9 @@ def test_decode_matches_oracle(ci):
 @pytest.mark.parametrize("dtype,D,R,Hq,Hkv,n_q", [("q4_0", 256, 0, 16, 2, 8),
                                                   ("q4_0", 256, 0, 16, 2, 16),
                                                   ("octave_k3v3_compact", 256, 64, 32, 4, 8),
+                                                  ("octave_k3v3_compact", 256, 64, 32, 4, 3),
+                                                  ("octave_k3v3_compact", 256, 64, 34, 2, 1),
+                                                  ("octave_k3v3_compact", 256, 64, 32, 2, 2),
                                                   ("octave_k3v4", 128, 64, 32, 8, 16),
                                                   ("octave_k3v4", 128, 64, 32, 8, 6),
                                                   ("q4_0", 128, 0, 32, 1, 4),
@@ -284,6 +287,57 @@ def test_decode_edge_lengths(dtype, D, R, Hq, Hkv):
         ref = O.attention(fo, q, ref_cache, bt, q_to_req, q_to_klen, scale)
         _assert_close(got, ref, f"{dtype} qps={qps}")
         assert np.all(got[1] == 0) and np.all(got[-1] == 0)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 4), (24, 4), (17, 1)])
+def test_decode_compact_one_pass_edge_lengths(Hq, Hkv):
+    """The one-pass kernel for 17-32 query rows per KV head (Octave k3v3
+    compact): four queries per sequence (causal: klen L-3 .. L), so with
+    queries_per_seq 4 a pass holds 4 G rows (G = 8: all 32 rows live; G = 6:
+    24 rows and 8 padding rows); lengths at the tile, page and split edges;
+    a query with no tokens and one with a negative length give zero rows."""
+    D, R, P = 256, 64, 16
+    lens = [4, 5, 16, 19, 20, 35, 1027, 2051, 2500, 7]
+    rng = np.random.default_rng(Hq * 7 + Hkv)
+    T = sum(lens)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    pages = [(L + P - 1) // P for L in lens]
+    perm = rng.permutation(sum(pages))
+    bt = np.zeros((len(lens), max(pages)), np.int32)
+    sm = np.empty(T, np.int64)
+    off = t0 = 0
+    for b, L in enumerate(lens):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+        pos = np.arange(L)
+        sm[t0:t0 + L] = bt[b, pos // P].astype(np.int64) * P + pos % P
+        t0 += L
+    f = hkv.format_init("octave_k3v3_compact", D, R, P)
+    fo = O.format_init("octave_k3v3_compact", D, R)
+    cache = hkv.new_cache(f, sum(pages), Hkv, DEV)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    ref_cache = np.zeros(tuple(cache.shape), np.uint8)
+    ref_cache[sm // P, :, sm % P] = slots
+    q_to_req = np.arange(len(lens), dtype=np.int32).repeat(4)
+    q_to_klen = np.array([[L - 3, L - 2, L - 1, L] for L in lens], np.int32).reshape(-1)
+    q_to_klen[2] = 0                 # klen 0 -> zero row
+    q_to_klen[-4] = -5               # negative -> zero row
+    # small and large query magnitudes in one pass (per-row query planes; the
+    # largest gives logits of a few tens, within the range where the query's
+    # 15-bit planes keep the scores inside the tolerance)
+    q = (rng.standard_normal((len(q_to_req), Hq, D)) *
+         rng.choice([0.01, 1.0, 4.0], size=(len(q_to_req), Hq, 1))).astype(np.float32)
+    scale = W.default_sm_scale(D)
+    got = hkv.decode_attention(f, torch.from_numpy(q).to(DEV), cache,
+                               torch.from_numpy(bt).to(DEV), torch.from_numpy(q_to_req).to(DEV),
+                               torch.from_numpy(q_to_klen).to(DEV), int(q_to_klen.max()), 4,
+                               scale).cpu().numpy()
+    ref = O.attention(fo, q, ref_cache, bt, q_to_req, q_to_klen, scale)
+    _assert_close(got, ref, f"compact Hq={Hq} Hkv={Hkv}")
+    assert np.all(got[2] == 0) and np.all(got[-4] == 0)
 
 
 def test_decode_is_deterministic_and_page_relabel_invariant():
