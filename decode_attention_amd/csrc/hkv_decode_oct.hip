@@ -40,6 +40,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // Slot layouts (slot words; vLLM docs, module text and OctaveFormat).
@@ -780,7 +781,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
   const uint32_t gsel_hi = 0x0Cu | (0x0Cu << 8) | ((uint32_t)vj << 16) | ((uint32_t)(vj + 4) << 24);
   const int vsh = 4 * (vm & 1);
   __syncthreads();
-  const float qs = L.qsc[n];
+  // (kept positive so that a masked score, -inf, stays -inf through the fma)
+  const float qs = fmaxf(L.qsc[n], 0x1p-126f);
 
   f32x16 o[8];
 #pragma unroll
@@ -839,7 +841,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
           clo = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, bl, clo, 0, 0, 0);
         }
       }
-      // score k = 4 j + i: token 8 j + 4 h + i of the unit (tile j >> 1)
+      // score k = 4 j + i: token 8 j + 4 h + i of the unit (tile j >> 1),
+      // held as s / qs until the exponent
       float s[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -847,7 +850,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
         const float kk[4] = {ks.x, ks.y, ks.z, ks.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          s[4 * j + i] = (float)(chi[4 * j + i] * 256 + clo[4 * j + i]) * kk[i] * qs;
+          s[4 * j + i] = (float)(chi[4 * j + i] * 256 + clo[4 * j + i]) * kk[i];
       }
       const int t0 = t_begin + 2 * kT * u_cur;
       if (!(t0 + 2 * kT <= t_lim)) {
@@ -866,7 +869,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
       {
         const uint32_t u = __float_as_uint(mt);
         const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * qs;
       }
       if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
         const float m_new = fmaxf(m_run, mt);
@@ -879,22 +882,31 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
           for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
         m_run = m_new;
       }
-      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+      const float m6 = ((m_run == -INFINITY) ? 0.0f : m_run) + 6.0f;
       // P operands: step j, k-slots 0-3 fp16(p s) of tokens 8 j + 4 h + i, 4-7 residuals x 2^12
       half8_t P[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float4 vs = *(const float4*)&L.u.s.sc[wave][j >> 1][1][8 * (j & 1) + 4 * h];
         const float vv[4] = {vs.x, vs.y, vs.z, vs.w};
+        float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[4 * j + i] - m_ref - 6.0f);  // p / 64
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * j + i], qs, -m6));  // p / 64
           l_run += p;
-          const float pv = p * vv[i];
-          sps += pv;
-          const _Float16 hp = (_Float16)pv;
-          P[j][i] = hp;
-          P[j][4 + i] = (_Float16)(fmaf((float)hp, -1.0f, pv) * 4096.0f);
+          pv[i] = p * vv[i];
+          sps += pv[i];
+        }
+        // The leading fp16 parts come from one conversion instruction, so the
+        // residuals are taken against exactly the values the product sees
+        // (the bias correction needs their sum to be the sum of p s).
+        const half2_t h01 = __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]);
+        const half2_t h23 = __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]);
+        const _Float16 hp[4] = {(_Float16)h01[0], (_Float16)h01[1], (_Float16)h23[0], (_Float16)h23[1]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          P[j][i] = hp[i];
+          P[j][4 + i] = (_Float16)fmaf((float)hp[i], -4096.0f, pv[i] * 4096.0f);  // exact before the rounding
         }
       }
 
