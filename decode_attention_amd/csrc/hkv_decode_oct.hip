@@ -1,7 +1,10 @@
 // hkv_decode_oct.hip -- split-K paged decode attention over Octave caches on
-// the matrix cores (gfx950), up to 8 query rows per KV head, for two layouts:
+// the matrix cores (gfx950), 8 or 16 query rows per KV head (and 32 in one
+// pass for the compact layout), for three layouts:
 //  * k3v4 at head size 128 with 64 RoPE dims: 4-bit K codes for the RoPE
 //    block, 3-bit for the NoPE block (one scale each), 4-bit V (128-byte slots);
+//  * k3v3 at head size 128 with 64 RoPE dims: the same K, 3-bit V (112-byte
+//    slots);
 //  * k3v3 compact at head size 256: 3-bit K and V, one scale each (196-byte
 //    slots).
 //
@@ -44,19 +47,40 @@ typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // Slot layouts (slot words; vLLM docs, module text and OctaveFormat).
+// kCompact: K is one 3-bit block under one scale (else a 4-bit RoPE block and
+// a 3-bit NoPE block, a scale each); kV3: V is 3-bit (two bit planes), else
+// 4-bit.  kChunks 16-byte chunks are loaded per lane and tile (chunk 4 i + q
+// by lane group q), of which the slot holds kNChunk.
 struct FmtK3V4 {            // octave_k3v4, head size 128, rope 64
   static constexpr bool kCompact = false;
+  static constexpr bool kV3 = false;
   static constexpr int kD = 128;
   static constexpr int kSlot = 128;
   static constexpr int kWNope = 8;    // NoPE low-bit plane (byte 32)
   static constexpr int kWNopeHi = 12; // NoPE high-bit plane (byte 48)
   static constexpr int kWV = 14;      // V codes (byte 56)
   static constexpr int kWScale = 30;  // K scales (RoPE | NoPE << 16); word 31: V scale
-  static constexpr int kChunks = 2;   // 16-byte chunks per lane and tile
+  static constexpr int kChunks = 2;
+  static constexpr int kNChunk = 8;
   static constexpr int kAcc = kD / 32 * 2;  // P.V accumulator tiles
+};
+struct FmtK3V3 {            // octave_k3v3, head size 128, rope 64
+  static constexpr bool kCompact = false;
+  static constexpr bool kV3 = true;
+  static constexpr int kD = 128;
+  static constexpr int kSlot = 112;
+  static constexpr int kWNope = 8;    // NoPE low-bit plane (byte 32)
+  static constexpr int kWNopeHi = 12; // NoPE high-bit plane (byte 48)
+  static constexpr int kWV = 14;      // V low-bit plane (byte 56)
+  static constexpr int kWVHi = 22;    // V high-bit plane (byte 88)
+  static constexpr int kWScale = 26;  // K scales (RoPE | NoPE << 16); word 27: V scale
+  static constexpr int kChunks = 2;
+  static constexpr int kNChunk = 7;   // chunk 7 (lane group 3, second load) is past the slot
+  static constexpr int kAcc = kD / 16;
 };
 struct FmtK3V3C {           // octave_k3v3_compact, head size 256
   static constexpr bool kCompact = true;
+  static constexpr bool kV3 = true;
   static constexpr int kD = 256;
   static constexpr int kSlot = 196;
   static constexpr int kWKHi = 16;    // K high-bit plane (byte 64)
@@ -64,6 +88,7 @@ struct FmtK3V3C {           // octave_k3v3_compact, head size 256
   static constexpr int kWVHi = 40;    // V high-bit plane (byte 160)
   static constexpr int kWScale = 48;  // K scale | V scale << 16
   static constexpr int kChunks = 3;   // 12 chunks of 16 bytes per slot: 3 per lane
+  static constexpr int kNChunk = 12;  // (+ the scale word, loaded on its own)
   static constexpr int kAcc = kD / 16;
 };
 constexpr int kRowsMax = 16;       // query rows per KV head (16-row mode)
@@ -138,7 +163,8 @@ struct Tile {
 template <class F, int RM>
 struct __align__(16) OctLds {
   static constexpr int kD = F::kD;
-  static constexpr int kSlotW = (F::kSlot + 3) / 4;
+  static constexpr int kSlotW = (F::kSlot + 3) / 4 > 16 * F::kChunks ? (F::kSlot + 3) / 4
+                                                                      : 16 * F::kChunks;
   // B operand bytes, [64-dim block][column][dim]: 8-row mode column r + 8 plane,
   // 16-row mode 16 plane + r.
   int8_t qB[kD / 64][2 * RM][64];
@@ -217,7 +243,10 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
                                      (t0 & (ps - 1))) * (int64_t)kSlot;
     const uint8_t* slot = base + min(tl, t_end - 1 - t0) * kSlot;
 #pragma unroll
-    for (int i = 0; i < F::kChunks; ++i) x.c[i] = *(const uint4*)(slot + 16 * (4 * i + gq));
+    for (int i = 0; i < F::kChunks; ++i)
+      x.c[i] = (F::kNChunk == 4 * F::kChunks || 4 * i + gq < F::kNChunk)
+                   ? *(const uint4*)(slot + 16 * (4 * i + gq))
+                   : make_uint4(0u, 0u, 0u, 0u);
     if constexpr (F::kCompact) x.sw = *(const uint32_t*)(slot + 4 * F::kWScale);
   };
   auto fetch = [&](Tile& x, int k) {
@@ -491,7 +520,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       auto gather = [&](const uint4& W) {
         return __builtin_amdgcn_perm(W.y, W.x, gsel_lo) | __builtin_amdgcn_perm(W.w, W.z, gsel_hi);
       };
-      if constexpr (!F::kCompact) {
+      if constexpr (!F::kV3) {
 #pragma unroll
         for (int W = w0 / 2; W < (w0 + nw) / 2; ++W) {
           const int wrd = F::kWV + 4 * W + (n >> 2);
@@ -598,7 +627,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     }
 #pragma unroll
     for (int b = 0; b < kAcc; ++b) {
-      const int d = F::kCompact ? 16 * b + n : 32 * (b >> 1) + 8 * (n >> 2) + (n & 3) + 4 * (b & 1);
+      const int d = F::kV3 ? 16 * b + n : 32 * (b >> 1) + 8 * (n >> 2) + (n & 3) + 4 * (b & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = o[b][i] * fw[i];
     }
@@ -731,7 +760,10 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
                                      (t0 & (ps - 1))) * (int64_t)kSlot;
     const uint8_t* slot = base + min(tl, t_end - 1 - t0) * kSlot;
 #pragma unroll
-    for (int i = 0; i < F::kChunks; ++i) x.c[i] = *(const uint4*)(slot + 16 * (4 * i + gq));
+    for (int i = 0; i < F::kChunks; ++i)
+      x.c[i] = (F::kNChunk == 4 * F::kChunks || 4 * i + gq < F::kNChunk)
+                   ? *(const uint4*)(slot + 16 * (4 * i + gq))
+                   : make_uint4(0u, 0u, 0u, 0u);
     x.sw = *(const uint32_t*)(slot + 4 * F::kWScale);
   };
   auto fetch = [&](Tile& x, int k) {
@@ -1007,11 +1039,16 @@ int oct_mfma_rows(const DevFmt& f, int rows) {
       !pow2)
     return 0;
   bool ok;
-  if (!f.compact)
-    ok = f.D == FmtK3V4::kD && f.k_wide == 64 && f.v_bits == 4 &&
+  if (!f.compact && f.v_bits == 4)
+    ok = f.D == FmtK3V4::kD && f.k_wide == 64 &&
          f.slot_bytes == FmtK3V4::kSlot && f.off_k_nope == 4 * FmtK3V4::kWNope &&
          f.off_v == 4 * FmtK3V4::kWV && f.off_scales == 4 * FmtK3V4::kWScale &&
          f.num_k_scales == 2 && f.k_block == 64;
+  else if (!f.compact)
+    ok = f.D == FmtK3V3::kD && f.k_wide == 64 && f.v_bits == 3 &&
+         f.slot_bytes == FmtK3V3::kSlot && f.off_k_nope == 4 * FmtK3V3::kWNope &&
+         f.off_v == 4 * FmtK3V3::kWV && f.off_scales == 4 * FmtK3V3::kWScale &&
+         f.num_k_scales == 2 && f.k_block == 64 && f.v_block == FmtK3V3::kD;
   else
     ok = f.D == FmtK3V3C::kD && f.v_bits == 3 && f.slot_bytes == FmtK3V3C::kSlot &&
          f.off_v == 4 * FmtK3V3C::kWV && f.off_scales == 4 * FmtK3V3C::kWScale &&
@@ -1025,9 +1062,11 @@ hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipSt
   const dim3 block(kQWaves * kWave);
   if (a.rows_pad == 8) {
     if (f.compact) decode_oct_kernel<FmtK3V3C, 8><<<grid, block, 0, s>>>(f, a);
+    else if (f.v_bits == 3) decode_oct_kernel<FmtK3V3, 8><<<grid, block, 0, s>>>(f, a);
     else decode_oct_kernel<FmtK3V4, 8><<<grid, block, 0, s>>>(f, a);
   } else if (a.rows_pad == 16) {
     if (f.compact) decode_oct_kernel<FmtK3V3C, 16><<<grid, block, 0, s>>>(f, a);
+    else if (f.v_bits == 3) decode_oct_kernel<FmtK3V3, 16><<<grid, block, 0, s>>>(f, a);
     else decode_oct_kernel<FmtK3V4, 16><<<grid, block, 0, s>>>(f, a);
   } else if (a.rows_pad == kR32 && f.compact) {
     decode_oct32_kernel<<<grid, block, 0, s>>>(f, a);

@@ -5,21 +5,30 @@ of the method's arithmetic.  Both the GPU tests/benchmark and the CPU oracle
 consume the arrays it returns.
 
 Recipe (numpy PCG64, seed = 1000 + config number unless given):
-  * outlier channels: drawn first, without replacement, shared by every
-    token and head, multiplied by 20;
-  * K, then V, then the query: standard normal in fp32, outlier channels
-    scaled, then rounded to fp16 (round-to-nearest-even) where the config
-    says fp16 (the fp16 values are what both sides see, widened exactly);
-  * sequence lengths (config 5): uniform integers in [1024, 32768];
+  * outlier channels: drawn first from the main stream (PCG64(seed)),
+    without replacement, shared by every token and head, multiplied by 20;
+  * sequence lengths (config 5): uniform integers in [1024, 32768], next
+    from the main stream;
+  * K, V and the query (tensors 0, 1, 2): standard normal in fp32, in chunks
+    of whole rows (the largest multiple of the head size not above 2^22
+    values) in row-major order; chunk c of tensor k comes from its
+    own stream PCG64(SeedSequence(seed, spawn_key=(k, c))), so the chunks
+    are drawn in parallel and the values do not depend on the thread count;
+    outlier channels scaled, then rounded to fp16 (round-to-nearest-even)
+    where the config says fp16 (the fp16 values are what both sides see,
+    widened exactly);
   * pages: every sequence gets ceil(L / page) pages; physical page ids are a
-    seeded random permutation of all pages (identity for config 1);
+    random permutation of all pages from the main stream (identity for
+    config 1);
   * queries: n_q per sequence; query j of a sequence of length L attends to
     the first L - n_q + j + 1 tokens (causal among the new tokens).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import List, Optional
 
 import numpy as np
@@ -102,20 +111,38 @@ class Workload:
                                for b in range(len(self.lengths))]).astype(np.int64)
 
 
-def _draw(rng: np.random.Generator, shape, scale_ch: Optional[np.ndarray], dtype: str,
-          chunk: int = 1 << 24) -> np.ndarray:
-    """Standard normals of `shape` (last dim = channels), outliers x20, cast."""
+_CHUNK = 1 << 22
+
+
+def _draw(seed: int, tensor: int, shape, scale_ch: Optional[np.ndarray], dtype: str) -> np.ndarray:
+    """Standard normals of `shape` (last dim = channels), outliers x20, cast.
+    Chunk c (whole rows, at most 2^22 values) comes from PCG64(SeedSequence(seed,
+    spawn_key=(tensor, c))); chunks are filled by a thread pool (numpy
+    releases the GIL while it draws)."""
     out_dtype = np.float16 if dtype == "f16" else np.float32
     total = int(np.prod(shape))
     D = shape[-1]
     out = np.empty(total, out_dtype)
-    step = max(D, (chunk // D) * D)
-    for s in range(0, total, step):
+    scale = scale_ch is not None and len(scale_ch) > 0
+    step = max(D, (_CHUNK // D) * D)
+
+    def fill(c: int) -> None:
+        s = c * step
         n = min(step, total - s)
-        x = rng.standard_normal(n, dtype=np.float32).reshape(-1, D)
-        if scale_ch is not None and len(scale_ch):
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tensor, c))))
+        x = g.standard_normal(n, dtype=np.float32)
+        if scale:
+            x = x.reshape(-1, D)
             x[:, scale_ch] *= np.float32(20.0)
         out[s:s + n] = x.reshape(-1).astype(out_dtype)
+
+    n_chunks = (total + step - 1) // step
+    if n_chunks <= 1:
+        for c in range(n_chunks):
+            fill(c)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(min(n_chunks, os.cpu_count() or 1, 16)) as ex:
+            list(ex.map(fill, range(n_chunks)))
     return out.reshape(shape)
 
 
@@ -143,10 +170,10 @@ def make_workload(cfg: Config, seed: Optional[int] = None, batch: Optional[int] 
     seq_start = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
     T = int(seq_start[-1])
 
-    key = _draw(rng, (T, Hkv, D), chans, cfg.in_dtype)
-    value = _draw(rng, (T, Hkv, D), chans, cfg.in_dtype)
+    key = _draw(seed, 0, (T, Hkv, D), chans, cfg.in_dtype)
+    value = _draw(seed, 1, (T, Hkv, D), chans, cfg.in_dtype)
     Q = B * cfg.n_q
-    query = _draw(rng, (Q, Hq, D), chans if cfg.outliers_on_query else None, cfg.in_dtype)
+    query = _draw(seed, 2, (Q, Hq, D), chans if cfg.outliers_on_query else None, cfg.in_dtype)
 
     pages_per_seq = (lengths + P - 1) // P
     num_pages = int(pages_per_seq.sum())

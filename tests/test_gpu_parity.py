@@ -403,3 +403,15 @@ def _full_size_check(ci, seqs, n_slot_samples=4096):
 
 def test_decode_full_size_q4_0_128k():
     _full_size_check(3, [0, 3])
+
+
+@pytest.mark.parametrize("ci,seqs", [(4, [0, 31]), (5, [0, 37, 63])])
+def test_decode_full_size_octave(ci, seqs):
+    _full_size_check(ci, seqs)
+
+
+@pytest.mark.parametrize("ci,seqs", [(6, [0, 15]), (7, [0, 31]), (8, [0, 15]), (9, [1])])
+def test_decode_full_size_wider_formats(ci, seqs):
+    """Query windows of 8 tokens (Q4_0), 3-bit V at head size 128, head size
+    192 and the Q8_0 mode, each at its benchmark size."""
+    _full_size_check(ci, seqs)
