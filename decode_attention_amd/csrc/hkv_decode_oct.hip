@@ -1,10 +1,12 @@
 // hkv_decode_oct.hip -- split-K paged decode attention over Octave caches on
 // the matrix cores (gfx950), 8 or 16 query rows per KV head (and 32 in one
-// pass for the compact layout), for three layouts:
+// pass for the compact layout), for four layouts:
 //  * k3v4 at head size 128 with 64 RoPE dims: 4-bit K codes for the RoPE
 //    block, 3-bit for the NoPE block (one scale each), 4-bit V (128-byte slots);
 //  * k3v3 at head size 128 with 64 RoPE dims: the same K, 3-bit V (112-byte
 //    slots);
+//  * k3v4 at head size 192 with 64 RoPE dims: two 3-bit NoPE blocks, 4-bit V
+//    (184-byte slots);
 //  * k3v3 compact at head size 256: 3-bit K and V, one scale each (196-byte
 //    slots).
 //
@@ -48,9 +50,11 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // Slot layouts (slot words; vLLM docs, module text and OctaveFormat).
 // kCompact: K is one 3-bit block under one scale (else a 4-bit RoPE block and
-// a 3-bit NoPE block, a scale each); kV3: V is 3-bit (two bit planes), else
-// 4-bit.  kChunks 16-byte chunks are loaded per lane and tile (chunk 4 i + q
-// by lane group q), of which the slot holds kNChunk.
+// kNope 3-bit NoPE blocks of 64 dims, a scale each); kV3: V is 3-bit (two bit
+// planes), else 4-bit; the V scale is the half (kVSh) of slot word kWVS.
+// kChunks 16-byte chunks are loaded per lane and tile (chunk 4 i + q by lane
+// group q), of which the slot holds kNChunk (the last one only 8 bytes when
+// kHalfLast).
 struct FmtK3V4 {            // octave_k3v4, head size 128, rope 64
   static constexpr bool kCompact = false;
   static constexpr bool kV3 = false;
@@ -60,9 +64,28 @@ struct FmtK3V4 {            // octave_k3v4, head size 128, rope 64
   static constexpr int kWNopeHi = 12; // NoPE high-bit plane (byte 48)
   static constexpr int kWV = 14;      // V codes (byte 56)
   static constexpr int kWScale = 30;  // K scales (RoPE | NoPE << 16); word 31: V scale
+  static constexpr int kNope = 1;
+  static constexpr int kWVS = 31, kVSh = 0;
   static constexpr int kChunks = 2;
   static constexpr int kNChunk = 8;
+  static constexpr bool kHalfLast = false;
   static constexpr int kAcc = kD / 32 * 2;  // P.V accumulator tiles
+};
+struct FmtK3V4W {           // octave_k3v4, head size 192, rope 64
+  static constexpr bool kCompact = false;
+  static constexpr bool kV3 = false;
+  static constexpr int kD = 192;
+  static constexpr int kSlot = 184;
+  static constexpr int kWNope = 8;    // NoPE low-bit plane, both blocks (byte 32)
+  static constexpr int kWNopeHi = 16; // NoPE high-bit plane (byte 64)
+  static constexpr int kWV = 20;      // V codes (byte 80)
+  static constexpr int kWScale = 44;  // RoPE | NoPE 0 << 16; word 45: NoPE 1 | V << 16
+  static constexpr int kNope = 2;
+  static constexpr int kWVS = 45, kVSh = 16;
+  static constexpr int kChunks = 3;
+  static constexpr int kNChunk = 12;
+  static constexpr bool kHalfLast = true;  // chunk 11: the two scale words only
+  static constexpr int kAcc = kD / 32 * 2;
 };
 struct FmtK3V3 {            // octave_k3v3, head size 128, rope 64
   static constexpr bool kCompact = false;
@@ -74,8 +97,11 @@ struct FmtK3V3 {            // octave_k3v3, head size 128, rope 64
   static constexpr int kWV = 14;      // V low-bit plane (byte 56)
   static constexpr int kWVHi = 22;    // V high-bit plane (byte 88)
   static constexpr int kWScale = 26;  // K scales (RoPE | NoPE << 16); word 27: V scale
+  static constexpr int kNope = 1;
+  static constexpr int kWVS = 27, kVSh = 0;
   static constexpr int kChunks = 2;
   static constexpr int kNChunk = 7;   // chunk 7 (lane group 3, second load) is past the slot
+  static constexpr bool kHalfLast = false;
   static constexpr int kAcc = kD / 16;
 };
 struct FmtK3V3C {           // octave_k3v3_compact, head size 256
@@ -89,6 +115,8 @@ struct FmtK3V3C {           // octave_k3v3_compact, head size 256
   static constexpr int kWScale = 48;  // K scale | V scale << 16
   static constexpr int kChunks = 3;   // 12 chunks of 16 bytes per slot: 3 per lane
   static constexpr int kNChunk = 12;  // (+ the scale word, loaded on its own)
+  static constexpr bool kHalfLast = false;
+  static constexpr int kWVS = 48, kVSh = 16;
   static constexpr int kAcc = kD / 16;
 };
 constexpr int kRowsMax = 16;       // query rows per KV head (16-row mode)
@@ -153,7 +181,20 @@ __device__ __forceinline__ void k4_word(uint32_t w, uint32_t& lo, uint32_t& hi) 
   hi = lut16((w >> 4) & 0x07070707u, byte_sign_mask(w), kK4[0], kK4[1], kK4[2], kK4[3]);
 }
 
-// Chunks q, q + 4, q + 8 (16 bytes each) of token tl (k3v4: the first two),
+// Chunk ci (16 bytes at 16 ci) of a slot: zeros past the slot's end, and
+// only 8 bytes for a half last chunk.
+template <class F>
+__device__ __forceinline__ uint4 load_chunk(const uint8_t* slot, int ci) {
+  if (F::kNChunk == 4 * F::kChunks && !F::kHalfLast) return *(const uint4*)(slot + 16 * ci);
+  if (ci < F::kNChunk - (F::kHalfLast ? 1 : 0)) return *(const uint4*)(slot + 16 * ci);
+  if (F::kHalfLast && ci == F::kNChunk - 1) {
+    const uint2 h = *(const uint2*)(slot + 16 * ci);
+    return make_uint4(h.x, h.y, 0u, 0u);
+  }
+  return make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Chunks q, q + 4, q + 8 (16 bytes each) of token tl (the first kChunks),
 // and for the compact layout the 4-byte scale word.
 struct Tile {
   uint4 c[3];
@@ -243,10 +284,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
                                      (t0 & (ps - 1))) * (int64_t)kSlot;
     const uint8_t* slot = base + min(tl, t_end - 1 - t0) * kSlot;
 #pragma unroll
-    for (int i = 0; i < F::kChunks; ++i)
-      x.c[i] = (F::kNChunk == 4 * F::kChunks || 4 * i + gq < F::kNChunk)
-                   ? *(const uint4*)(slot + 16 * (4 * i + gq))
-                   : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < F::kChunks; ++i) x.c[i] = load_chunk<F>(slot, 4 * i + gq);
     if constexpr (F::kCompact) x.sw = *(const uint32_t*)(slot + 4 * F::kWScale);
   };
   auto fetch = [&](Tile& x, int k) {
@@ -347,6 +385,16 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       const uint4 ks = lds_u4(&tr[F::kWScale * kTS + 4 * g]);
       const uint32_t ksw[4] = {ks.x, ks.y, ks.z, ks.w};
       if constexpr (!F::kCompact) {
+        // K scale of block c (RoPE, NoPE 0, NoPE 1) for token 4 g + i
+        uint32_t ksw2[4] = {0u, 0u, 0u, 0u};
+        if constexpr (F::kNope > 1) {
+          const uint4 k2 = lds_u4(&tr[(F::kWScale + 1) * kTS + 4 * g]);
+          ksw2[0] = k2.x, ksw2[1] = k2.y, ksw2[2] = k2.z, ksw2[3] = k2.w;
+        }
+        auto kscale = [&](int c, int i) {
+          const uint32_t w = c < 2 ? ksw[i] : ksw2[i];
+          return h2f((uint16_t)((c & 1) ? (w >> 16) : (w & 0xffffu)));
+        };
         // RoPE block: words 2g, 2g + 1 of token n (dims 16 g .. 16 g + 15).
         const uint32_t r0 = tr[(2 * g) * kTS + n], r1 = tr[(2 * g + 1) * kTS + n];
         int4_t A0;
@@ -356,34 +404,46 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
           k4_word(r1, l1, h1);
           A0 = (int4_t){(int)l0, (int)h0, (int)l1, (int)h1};
         }
-        // NoPE block: low-bit plane word g, high-bit plane word g >> 1.
-        const uint32_t lw = tr[(F::kWNope + g) * kTS + n];
-        const uint32_t hw = tr[(F::kWNopeHi + (g >> 1)) * kTS + n] >> hsh;
-        int4_t A1;
+        // NoPE block b: low-bit plane word 4 b + g, high-bit plane word
+        // 2 b + (g >> 1) (the planes span all NoPE dims).
+        int4_t A[1 + F::kNope];
+        A[0] = A0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
-          A1[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
-        }
-        if constexpr (!kK16) {
-          const int4_t C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qreg[0], zero4, 0, 0, 0);
-          const int4_t C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qreg[1], zero4, 0, 0, 0);
+        for (int b = 0; b < F::kNope; ++b) {
+          const uint32_t lw = tr[(F::kWNope + 4 * b + g) * kTS + n];
+          const uint32_t hw = tr[(F::kWNopeHi + 2 * b + (g >> 1)) * kTS + n] >> hsh;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float acc = fmaf((float)C0[i], h2f((uint16_t)(ksw[i] & 0xffffu)),
-                                   (float)C1[i] * h2f((uint16_t)(ksw[i] >> 16)));
+            const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
+            A[1 + b][i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
+          }
+        }
+        if constexpr (!kK16) {
+          int4_t C[1 + F::kNope];
+#pragma unroll
+          for (int c = 0; c <= F::kNope; ++c)
+            C[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[c], qreg[c], zero4, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float acc = (float)C[0][i] * kscale(0, i);
+#pragma unroll
+            for (int c = 1; c <= F::kNope; ++c) acc = fmaf((float)C[c][i], kscale(c, i), acc);
             sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
           }
         } else {
           // hi and lo planes joined in int32 (exact: |hi| 256 + |lo| < 2^31).
-          const int4_t H0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qreg[0], zero4, 0, 0, 0);
-          const int4_t L0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, qlo[0], zero4, 0, 0, 0);
-          const int4_t H1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qreg[1], zero4, 0, 0, 0);
-          const int4_t L1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, qlo[1], zero4, 0, 0, 0);
+          int4_t H[1 + F::kNope], Lo[1 + F::kNope];
+#pragma unroll
+          for (int c = 0; c <= F::kNope; ++c) {
+            H[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[c], qreg[c], zero4, 0, 0, 0);
+            Lo[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[c], qlo[c], zero4, 0, 0, 0);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float acc = fmaf((float)(H0[i] * 256 + L0[i]), h2f((uint16_t)(ksw[i] & 0xffffu)),
-                                   (float)(H1[i] * 256 + L1[i]) * h2f((uint16_t)(ksw[i] >> 16)));
+            float acc = (float)(H[0][i] * 256 + Lo[0][i]) * kscale(0, i);
+#pragma unroll
+            for (int c = 1; c <= F::kNope; ++c)
+              acc = fmaf((float)(H[c][i] * 256 + Lo[c][i]), kscale(c, i), acc);
             sc[i] = acc * qs;
           }
         }
@@ -457,8 +517,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       }
       const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
       // V scale: low half of word 31 (k3v4), high half of the scale word (compact).
-      constexpr int kWVs = F::kCompact ? F::kWScale : F::kWScale + 1;
-      constexpr int kVsh = F::kCompact ? 16 : 0;
+      constexpr int kWVs = F::kWVS;
+      constexpr int kVsh = F::kVSh;
       const uint4 va = lds_u4(&L.u.tt[wave][buf][0][kWVs][4 * g]);
       const uint4 vb = lds_u4(&L.u.tt[wave][buf][1][kWVs][4 * g]);
       const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
@@ -760,10 +820,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
                                      (t0 & (ps - 1))) * (int64_t)kSlot;
     const uint8_t* slot = base + min(tl, t_end - 1 - t0) * kSlot;
 #pragma unroll
-    for (int i = 0; i < F::kChunks; ++i)
-      x.c[i] = (F::kNChunk == 4 * F::kChunks || 4 * i + gq < F::kNChunk)
-                   ? *(const uint4*)(slot + 16 * (4 * i + gq))
-                   : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < F::kChunks; ++i) x.c[i] = load_chunk<F>(slot, 4 * i + gq);
     x.sw = *(const uint32_t*)(slot + 4 * F::kWScale);
   };
   auto fetch = [&](Tile& x, int k) {
@@ -1039,7 +1096,11 @@ int oct_mfma_rows(const DevFmt& f, int rows) {
       !pow2)
     return 0;
   bool ok;
-  if (!f.compact && f.v_bits == 4)
+  if (!f.compact && f.v_bits == 4 && f.D == FmtK3V4W::kD)
+    ok = f.k_wide == 64 && f.slot_bytes == FmtK3V4W::kSlot &&
+         f.off_k_nope == 4 * FmtK3V4W::kWNope && f.off_v == 4 * FmtK3V4W::kWV &&
+         f.off_scales == 4 * FmtK3V4W::kWScale && f.num_k_scales == 3 && f.k_block == 64;
+  else if (!f.compact && f.v_bits == 4)
     ok = f.D == FmtK3V4::kD && f.k_wide == 64 &&
          f.slot_bytes == FmtK3V4::kSlot && f.off_k_nope == 4 * FmtK3V4::kWNope &&
          f.off_v == 4 * FmtK3V4::kWV && f.off_scales == 4 * FmtK3V4::kWScale &&
@@ -1063,10 +1124,12 @@ hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipSt
   if (a.rows_pad == 8) {
     if (f.compact) decode_oct_kernel<FmtK3V3C, 8><<<grid, block, 0, s>>>(f, a);
     else if (f.v_bits == 3) decode_oct_kernel<FmtK3V3, 8><<<grid, block, 0, s>>>(f, a);
+    else if (f.D == FmtK3V4W::kD) decode_oct_kernel<FmtK3V4W, 8><<<grid, block, 0, s>>>(f, a);
     else decode_oct_kernel<FmtK3V4, 8><<<grid, block, 0, s>>>(f, a);
   } else if (a.rows_pad == 16) {
     if (f.compact) decode_oct_kernel<FmtK3V3C, 16><<<grid, block, 0, s>>>(f, a);
     else if (f.v_bits == 3) decode_oct_kernel<FmtK3V3, 16><<<grid, block, 0, s>>>(f, a);
+    else if (f.D == FmtK3V4W::kD) decode_oct_kernel<FmtK3V4W, 16><<<grid, block, 0, s>>>(f, a);
     else decode_oct_kernel<FmtK3V4, 16><<<grid, block, 0, s>>>(f, a);
   } else if (a.rows_pad == kR32 && f.compact) {
     decode_oct32_kernel<<<grid, block, 0, s>>>(f, a);

@@ -214,6 +214,8 @@ def test_decode_matches_oracle(ci):
                                                   ("octave_k3v4", 128, 64, 32, 8, 6),
                                                   ("q4_0", 128, 0, 32, 1, 4),
                                                   ("octave_k3v3", 128, 64, 8, 1, 12),
+                                                  ("octave_k3v4", 192, 64, 16, 2, 2),
+                                                  ("octave_k3v4", 192, 64, 12, 4, 5),
                                                   ("q8_0", 256, 0, 16, 2, 4)])
 def test_decode_long_query_windows(dtype, D, R, Hq, Hkv, n_q):
     """Query windows beyond 4 tokens (verify / multi-token prediction): more
