@@ -423,13 +423,15 @@ hipError_t launch_generic_e(const DevFmt& f, const DecArgs& a, int R, dim3 grid,
 
 bool q4_mfma_supported(const DevFmt& f, int rows);
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
+bool q8_mfma_supported(const DevFmt& f, int rows);
+hipError_t launch_decode_q8_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
 int oct_mfma_rows(const DevFmt& f, int rows);
 hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
 
 // Decode kernels: 0 the generic VALU kernel (every format), 1 the Q4_0 MFMA
 // kernel (head size 256, 8 rows), 2 the Octave MFMA kernel (k3v4 at head
 // size 128, k3v3 compact at 256; 8 or 16 rows).
-constexpr int kKernelGeneric = 0, kKernelQ4 = 1, kKernelOctK3v4 = 2;
+constexpr int kKernelGeneric = 0, kKernelQ4 = 1, kKernelOctK3v4 = 2, kKernelQ8 = 3;
 
 constexpr int64_t kTargetSplitsWgs = 512;
 constexpr int kMaxRows = 32;          // query rows per KV head in one pass
@@ -449,6 +451,7 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   q.nsub = 1;
   auto mfma_kernel = [&](int rows) {
     return q4_mfma_supported(f, rows)   ? kKernelQ4
+           : q8_mfma_supported(f, rows) ? kKernelQ8
            : oct_mfma_rows(f, rows) > 0 ? kKernelOctK3v4
                                         : kKernelGeneric;
   };
@@ -477,7 +480,7 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
     }
   }
   if (q.rows > kMaxRows) return false;
-  q.rows_pad = q.kernel == kKernelQ4        ? 8
+  q.rows_pad = q.kernel == kKernelQ4 || q.kernel == kKernelQ8 ? 8
                : q.kernel == kKernelOctK3v4 ? oct_mfma_rows(f, q.rows)
                                             : round_rows(q.rows);
   // Split size: enough splits that (sequence group, KV head, split) fills the
@@ -543,6 +546,8 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   hipError_t e;
   if (p.kernel == kKernelQ4) {
     e = launch_decode_q4_mfma(f, a, grid, s);
+  } else if (p.kernel == kKernelQ8) {
+    e = launch_decode_q8_mfma(f, a, grid, s);
   } else if (p.kernel == kKernelOctK3v4) {
     e = launch_decode_oct(f, a, grid, s);
   } else switch (f.D / kWave) {

@@ -40,6 +40,27 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Lane l <- lane (l ^ 8) within each row of 16 (DPP row_ror:8).
+__device__ __forceinline__ float ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+
+// Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 with the lane-swap
+// instructions (no LDS round trip): swapping a copy of v with itself leaves
+// the partner's value in one of the two results.
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ uint4 lds_u4(const uint32_t* p) {
+  return *(const uint4*)__builtin_assume_aligned(p, 16);
+}
+
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

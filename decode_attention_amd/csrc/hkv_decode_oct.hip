@@ -141,23 +141,6 @@ constexpr uint32_t kV4[4] = {lut_word(kLut4, 0, 128), lut_word(kLut4, 1, 128),
                              lut_word(kLut4, 2, 128), lut_word(kLut4, 3, 128)};
 constexpr uint32_t kV3[2] = {lut_word(kLut3, 0, 128), lut_word(kLut3, 1, 128)};
 
-__device__ __forceinline__ float ror8(float v) {  // lane l <- lane (l ^ 8) within 16
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ float max_xor16_32(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t w = __float_as_uint(v);
-  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ uint4 lds_u4(const uint32_t* p) {
-  return *(const uint4*)__builtin_assume_aligned(p, 16);
-}
-
 // 0xFF in each byte whose bit 7 is set in y, else 0x00 (v_perm_b32
 // sign-replicating selectors 8-11 read bit 7 of bytes 1, 3 of the low and
 // high source words).

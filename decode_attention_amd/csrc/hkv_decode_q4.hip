@@ -54,22 +54,6 @@ constexpr float kLazy = 8.0f;          // log2 headroom before the running max i
 constexpr int kQWaves = 8;             // waves per workgroup (two per SIMD)
 constexpr int kMaxSplitTiles = 256;    // page ids of a split's tiles held in LDS
 
-__device__ __forceinline__ float ror8(float v) {  // lane l <- lane (l ^ 8) within 16
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
-}
-
-// Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 with the lane-swap
-// instructions (no LDS round trip): swapping a copy of v with itself leaves
-// the partner's value in one of the two results.
-__device__ __forceinline__ float max_xor16_32(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t w = __float_as_uint(v);
-  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 __device__ __forceinline__ float f16lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float f16hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
@@ -87,10 +71,6 @@ __device__ __forceinline__ void load_tile(Tile& x, const uint8_t* slot, int gq, 
   x.v0 = *(const uint4*)(slot + kD / 2 + 16 * gq);
   x.v1 = *(const uint4*)(slot + kD / 2 + 16 * (4 + gq));
   x.sc = *(const uint4*)(slot + kD + 16 * scale_kind);
-}
-
-__device__ __forceinline__ uint4 lds_u4(const uint32_t* p) {
-  return *(const uint4*)__builtin_assume_aligned(p, 16);
 }
 
 struct __align__(16) Q4Lds {
