@@ -376,7 +376,7 @@ def main():
     append_ms = max(ms_per_step - decode_ms, 0.0)
 
     # Achievable read bandwidth beside the 8 TB/s peak: a plain streaming-read
-    # probe (16-byte loads, four in flight per thread) over 1 GiB.
+    # probe (nontemporal 16-byte loads, eight in flight per thread) over 1 GiB.
     read_gbs = stream_read_gbs(torch, dev)
 
     # Bulk quantize-append of every token into every copy (same bytes again),
