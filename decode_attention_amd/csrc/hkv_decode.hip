@@ -380,6 +380,77 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   }
 }
 
+// The same merge with one wave per row (kMergeWaves rows per workgroup), for
+// plans with at most kRowChunk splits: a row's live records come in one
+// memory round trip and need no cross-wave combine, so many-row, few-split
+// shapes (tens of thousands of short rows) do not pay a workgroup and a
+// barrier per row.
+constexpr int kRowChunk = 8;
+
+template <int E>
+__global__ __launch_bounds__(kMergeWaves * kWave) void merge_rows_kernel(DevFmt f, DecArgs a,
+                                                                        float* out, int64_t rows) {
+  constexpr int D = E * kWave;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t rowid = (int64_t)blockIdx.x * kMergeWaves + wave;
+  if (rowid >= rows) return;
+  const int i = (int)(rowid / a.num_q_heads);
+  const int h = (int)(rowid % a.num_q_heads);
+  const int gi = i / a.n_q, j = i % a.n_q;
+  const int kvh = h / a.group, g = h % a.group;
+  const int r = j * a.group + g;
+  const int Rp = a.rows_pad;
+  const int klen = a.q_to_klen[i];
+  const int n_live = klen <= 0 ? 0 : min(a.num_splits, (klen + a.tokens_per_split - 1) /
+                                                           a.tokens_per_split);
+  const float* base = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride +
+                      (size_t)r * a.pstride;
+  const size_t sstride = (size_t)Rp * a.pstride;
+  float M = -INFINITY, L = 0.0f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int s0 = 0; s0 < n_live; s0 += kRowChunk) {
+    float2 ml[kRowChunk];
+    float o[kRowChunk][E];
+#pragma unroll
+    for (int c = 0; c < kRowChunk; ++c) {
+      // a split past the end reloads the first one with a zero weight
+      const int s = s0 + c;
+      const float* ps = base + (s < n_live ? s : s0) * sstride;
+      ml[c] = *(const float2*)ps;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[c][e] = ps[kPartialHead + kWave * e + lane];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int c = 0; c < kRowChunk; ++c)
+      if (s0 + c < n_live) Mc = fmaxf(Mc, ml[c].x);
+    const float alpha = exp2f(M - Mc);  // M = -inf before the first chunk: 0
+    L *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int c = 0; c < kRowChunk; ++c) {
+      const float w = s0 + c < n_live ? exp2f(ml[c].x - Mc) : 0.0f;
+      L = fmaf(ml[c].y, w, L);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(o[c][e], w, acc[e]);
+    }
+    M = Mc;
+  }
+  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] *= inv;
+  fwht_strided<E>(acc, f.v_block, f.v_norm);
+  float* dst = out + ((int64_t)i * a.num_q_heads + h) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = kWave * e + lane;
+    dst[d] = f.use_signs ? apply_sign(f, acc[e], d) : acc[e];
+  }
+}
+
 int round_rows(int rows) {
   int R = 1;
   while (R < rows) R <<= 1;
@@ -559,12 +630,23 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   }
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.num_groups * p.n_q * num_q_heads;
-  const dim3 mgrid((unsigned)rows);
-  switch (f.D / kWave) {
-    case 1: merge_kernel<1><<<mgrid, dim3(kMergeWaves * kWave), 0, s>>>(f, a, out); break;
-    case 2: merge_kernel<2><<<mgrid, dim3(kMergeWaves * kWave), 0, s>>>(f, a, out); break;
-    case 3: merge_kernel<3><<<mgrid, dim3(kMergeWaves * kWave), 0, s>>>(f, a, out); break;
-    case 4: merge_kernel<4><<<mgrid, dim3(kMergeWaves * kWave), 0, s>>>(f, a, out); break;
+  const dim3 mblock(kMergeWaves * kWave);
+  if (p.num_splits <= kRowChunk) {
+    const dim3 mgrid((unsigned)((rows + kMergeWaves - 1) / kMergeWaves));
+    switch (f.D / kWave) {
+      case 1: merge_rows_kernel<1><<<mgrid, mblock, 0, s>>>(f, a, out, rows); break;
+      case 2: merge_rows_kernel<2><<<mgrid, mblock, 0, s>>>(f, a, out, rows); break;
+      case 3: merge_rows_kernel<3><<<mgrid, mblock, 0, s>>>(f, a, out, rows); break;
+      case 4: merge_rows_kernel<4><<<mgrid, mblock, 0, s>>>(f, a, out, rows); break;
+    }
+  } else {
+    const dim3 mgrid((unsigned)rows);
+    switch (f.D / kWave) {
+      case 1: merge_kernel<1><<<mgrid, mblock, 0, s>>>(f, a, out); break;
+      case 2: merge_kernel<2><<<mgrid, mblock, 0, s>>>(f, a, out); break;
+      case 3: merge_kernel<3><<<mgrid, mblock, 0, s>>>(f, a, out); break;
+      case 4: merge_kernel<4><<<mgrid, mblock, 0, s>>>(f, a, out); break;
+    }
   }
   return hipGetLastError();
 }
