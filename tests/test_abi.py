@@ -151,3 +151,21 @@ def test_hadamard_host_errors():
     assert h(sb=FAKE + 2) == hkv.HKV_ERR_INVALID_ARG
     assert h(y=FAKE + 1024) == hkv.HKV_ERR_INVALID_ARG          # partial overlap
     assert h(dt=1, y=FAKE) == hkv.HKV_ERR_INVALID_ARG           # f16 input cannot be in place
+
+
+@pytest.mark.parametrize("dtype,D,R,Q,Hq,Hkv,klen,qps,rows_pad,splits,groups", [
+    ("q4_0", 256, 0, 4, 16, 2, 131072, 1, 8, 32, 4),             # 8 rows, 4096-token splits
+    ("q8_0", 256, 0, 4, 16, 2, 131072, 1, 8, 32, 4),             # Q8_0 matrix-core kernel
+    ("q8_0", 128, 0, 4, 16, 2, 131072, 1, 8, 128, 4),            # generic kernel: 1024-token splits
+    ("octave_k3v3_compact", 256, 64, 256, 32, 4, 32768, 4, 32, 8, 64),  # one pass for 32 rows
+    ("octave_k3v4", 192, 64, 16, 16, 4, 32768, 1, 8, 8, 16),     # 4 rows in the 8-row mode
+    ("octave_k3v3", 128, 64, 32, 32, 8, 32768, 1, 8, 8, 32),
+    ("q4_0", 256, 0, 128, 16, 2, 32768, 8, 8, 8, 128),           # 64 rows -> 8-row sub-groups
+])
+def test_decode_plan_workspace(dtype, D, R, Q, Hq, Hkv, klen, qps, rows_pad, splits, groups):
+    """The workspace a plan asks for is one partial record (m, l, two pad
+    words, o[D]) per (query group, KV head, split, padded row): the row
+    padding, split count and sub-grouping the planner picks for these shapes."""
+    f = _fmt(dtype, D, R, 16)
+    want = 4 * (4 + D) * rows_pad * splits * groups * Hkv
+    assert hkv.decode_workspace_bytes(f, Q, Hq, Hkv, klen, qps) == want
