@@ -722,30 +722,32 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 constexpr int kR32 = 32;
 constexpr int kOB = 65;  // row stride (floats) of the cross-wave sum: 64 values + pad
 
+template <int W>
 struct __align__(16) Oct32Lds {
   static constexpr int kWords = 48;  // code words of a compact slot (the scale word is staged as floats)
   int8_t qB[2][8][kR32][32];         // [plane][32-dim block][row][dim in block]
   float qsc[kR32];
-  float mlw[kQWaves][kR32][2];
+  float mlw[W][kR32][2];
   int pid[kMaxSplitTiles];
   int next_unit;
   int pad_[3];
   union {
     struct {
-      uint32_t tt[kQWaves][2][kWords][kTS];  // [tile][slot word][token], one unit per wave
-      float sc[kQWaves][2][2][kT];           // [tile][K | V][token] scales as fp32
+      uint32_t tt[W][2][kWords][kTS];  // [tile][slot word][token], one unit per wave
+      float sc[W][2][2][kT];           // [tile][K | V][token] scales as fp32
     } s;
-    float ob[kQWaves][2][kR32][kOB];         // [wave][l / 32][row][value] for one half of the dims
+    float ob[W][2][kR32][kOB];         // [wave][l / 32][row][value] for one half of the dims
   } u;
 };
 
-__global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt f, DecArgs a) {
+template <int W>
+__global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, DecArgs a) {
   using F = FmtK3V3C;
   constexpr int kD = F::kD;
   constexpr int kSlot = F::kSlot;
   constexpr int kE = kD / kWave;
-  constexpr int kQR = kR32 / kQWaves;  // query rows set up per wave
-  __shared__ Oct32Lds L;
+  constexpr int kQR = kR32 / W;  // query rows set up per wave
+  __shared__ Oct32Lds<W> L;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -755,7 +757,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
   float qx[kQR][kE];
 #pragma unroll
   for (int k = 0; k < kQR; ++k) {
-    const int r = wave + kQWaves * k;
+    const int r = wave + W * k;
     if (r < a.rows) {
       const int j = r / a.group, g = r % a.group;
       const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
@@ -795,7 +797,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
   const int nt = (t_end - t_begin + kT - 1) / kT;
   const int nu = (nt + 1) >> 1;
   for (int t = threadIdx.x; t < nt; t += blockDim.x) L.pid[t] = bt[(t_begin + kT * t) >> ps_shift];
-  if (threadIdx.x == 0) L.next_unit = kQWaves;
+  if (threadIdx.x == 0) L.next_unit = W;
   const int tl = lane & 15, gq = lane >> 4;
   auto fetch_pid = [&](Tile& x, int kc, int page) {
     const int t0 = t_begin + kT * kc;
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
   }
 #pragma unroll
   for (int k = 0; k < kQR; ++k) {
-    const int r = wave + kQWaves * k;
+    const int r = wave + W * k;
     float x[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e)
@@ -871,7 +873,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const Tile& x = hb ? tb : ta;
-        uint32_t* w = tw + hb * (Oct32Lds::kWords * kTS) + tl;
+        uint32_t* w = tw + hb * (Oct32Lds<W>::kWords * kTS) + tl;
 #pragma unroll
         for (int i = 0; i < F::kChunks; ++i) {
           w[(16 * i + 4 * gq + 0) * kTS] = x.c[i].x;
@@ -896,7 +898,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
       // ---- scores: 32 tokens x 32 rows ----
       i32x16 chi = {}, clo = {};
       {
-        const uint32_t* tk = tw + (n >> 4) * (Oct32Lds::kWords * kTS) + (n & 15);
+        const uint32_t* tk = tw + (n >> 4) * (Oct32Lds<W>::kWords * kTS) + (n & 15);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const uint32_t lw = tk[(2 * c + h) * kTS];
@@ -985,7 +987,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
       // ---- P.V: 8 accumulator tiles of 32 dims ----
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t* vt = tw + (j >> 1) * (Oct32Lds::kWords * kTS) + 8 * (j & 1) + 4 * h;
+        const uint32_t* vt = tw + (j >> 1) * (Oct32Lds<W>::kWords * kTS) + 8 * (j & 1) + 4 * h;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const uint4 wl = lds_u4(vt + (F::kWV + 8 * b + vm) * kTS);
@@ -1032,7 +1034,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
   {
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][n][0]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, L.mlw[w][n][0]);
     fw = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
   }
   const float bias = 1152.0f * psum;  // the values entered as 1152 + LUT[c]
@@ -1051,15 +1053,15 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct32_kernel(DevFmt
       const int hh = mp & 1, k = 4 * (mp >> 1) + j;
       float acc = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kQWaves; ++w) acc += L.u.ob[w][hh][r][16 * i + k];
+      for (int w = 0; w < W; ++w) acc += L.u.ob[w][hh][r][16 * i + k];
       part[r * a.pstride + kPartialHead + 128 * b + dd] = acc;
     }
   }
   if (threadIdx.x < a.rows) {
     const int r = threadIdx.x;
     float M = -INFINITY, L_ = 0.0f;
-    for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
-    for (int w = 0; w < kQWaves; ++w) {
+    for (int w = 0; w < W; ++w) M = fmaxf(M, L.mlw[w][r][0]);
+    for (int w = 0; w < W; ++w) {
       const float mw = L.mlw[w][r][0];
       if (mw != -INFINITY) L_ += L.mlw[w][r][1] * exp2f(mw - M);
     }
@@ -1115,7 +1117,7 @@ hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipSt
     else if (f.D == FmtK3V4W::kD) decode_oct_kernel<FmtK3V4W, 16><<<grid, block, 0, s>>>(f, a);
     else decode_oct_kernel<FmtK3V4, 16><<<grid, block, 0, s>>>(f, a);
   } else if (a.rows_pad == kR32 && f.compact) {
-    decode_oct32_kernel<<<grid, block, 0, s>>>(f, a);
+    decode_oct32_kernel<kQWaves><<<grid, block, 0, s>>>(f, a);
   } else {
     return hipErrorInvalidValue;
   }
