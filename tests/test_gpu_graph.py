@@ -20,7 +20,9 @@ DEV = "cuda:0"
 
 
 @pytest.mark.parametrize("ci,sizes", [(3, dict(batch=2, seq_len=1537)),
-                                      (4, dict(batch=3, seq_len=700, min_len=300))])
+                                      (4, dict(batch=3, seq_len=700, min_len=300)),
+                                      (5, dict(batch=3, seq_len=1300, min_len=200)),
+                                      (9, dict(batch=2, seq_len=1537))])
 def test_graph_replay_matches_eager(ci, sizes):
     cfg = W.CONFIGS[ci]
     w = W.make_workload(cfg, **sizes)
