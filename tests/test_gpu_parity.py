@@ -417,3 +417,51 @@ def test_decode_full_size_wider_formats(ci, seqs):
     """Query windows of 8 tokens (Q4_0), 3-bit V at head size 128, head size
     192 and the Q8_0 mode, each at its benchmark size."""
     _full_size_check(ci, seqs)
+
+
+@pytest.mark.parametrize("P", [32, 64, 24, 1])
+@pytest.mark.parametrize("dtype,D,R,Hq,Hkv,qps", [("q4_0", 256, 0, 16, 2, 1),
+                                                  ("q8_0", 256, 0, 16, 2, 1),
+                                                  ("octave_k3v4", 128, 64, 32, 8, 1),
+                                                  ("octave_k3v3", 128, 64, 16, 4, 4),
+                                                  ("octave_k3v4", 192, 64, 8, 2, 1),
+                                                  ("octave_k3v3_compact", 256, 64, 32, 4, 4)])
+def test_decode_page_sizes(P, dtype, D, R, Hq, Hkv, qps):
+    """Pages other than 16 tokens: 32 and 64 (the matrix-core kernels' tiles
+    start inside a page), and 24 and 1 (not a multiple of the 16-token tile:
+    the generic kernel)."""
+    lens = [5, 100, 700, 2049]
+    rng = np.random.default_rng(P * 31 + D + Hq)
+    T = sum(lens)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    pages = [(L + P - 1) // P for L in lens]
+    perm = rng.permutation(sum(pages))
+    bt = np.zeros((len(lens), max(pages)), np.int32)
+    sm = np.empty(T, np.int64)
+    off = t0 = 0
+    for b, L in enumerate(lens):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+        pos = np.arange(L)
+        sm[t0:t0 + L] = bt[b, pos // P].astype(np.int64) * P + pos % P
+        t0 += L
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
+    cache = hkv.new_cache(f, sum(pages), Hkv, DEV)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    ref_cache = np.zeros(tuple(cache.shape), np.uint8)
+    ref_cache[sm // P, :, sm % P] = slots
+    assert np.array_equal(cache.cpu().numpy(), ref_cache)
+    q_to_req = np.arange(len(lens), dtype=np.int32).repeat(qps)
+    q_to_klen = np.array([[L - qps + 1 + j for j in range(qps)] for L in lens], np.int32).reshape(-1)
+    q = rng.standard_normal((len(q_to_req), Hq, D)).astype(np.float32)
+    scale = W.default_sm_scale(D)
+    got = hkv.decode_attention(f, torch.from_numpy(q).to(DEV), cache, torch.from_numpy(bt).to(DEV),
+                               torch.from_numpy(q_to_req).to(DEV),
+                               torch.from_numpy(q_to_klen).to(DEV), int(q_to_klen.max()), qps,
+                               scale).cpu().numpy()
+    ref = O.attention(fo, q, ref_cache, bt, q_to_req, q_to_klen, scale)
+    _assert_close(got, ref, f"{dtype} D={D} page {P}")
