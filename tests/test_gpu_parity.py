@@ -465,3 +465,60 @@ def test_decode_page_sizes(P, dtype, D, R, Hq, Hkv, qps):
                                scale).cpu().numpy()
     ref = O.attention(fo, q, ref_cache, bt, q_to_req, q_to_klen, scale)
     _assert_close(got, ref, f"{dtype} D={D} page {P}")
+
+
+@pytest.mark.parametrize("dtype,D,R,Hq,Hkv,qps,num_pages", [("q4_0", 256, 0, 16, 2, 1, 600_000),
+                                                            ("q8_0", 256, 0, 16, 2, 1, 300_000),
+                                                            ("octave_k3v3_compact", 256, 64, 32, 4, 4, 350_000),
+                                                            ("octave_k3v4", 128, 64, 32, 8, 1, 300_000)])
+def test_decode_cache_beyond_4gib(dtype, D, R, Hq, Hkv, qps, num_pages):
+    """A cache of more than 4 GiB with the sequences' pages near its end, so
+    every slot address needs 64 bits.  The oracle sees the same pages at low
+    ids in a small cache of its own (nothing it uses comes from the GPU)."""
+    P = 16
+    lens = [300, 1500]
+    rng = np.random.default_rng(D + Hkv)
+    T = sum(lens)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    pages = [(L + P - 1) // P for L in lens]
+    n_used = sum(pages)
+    low = rng.permutation(n_used)                    # the oracle's page ids
+    high = (num_pages - n_used - 7) + low            # the GPU's page ids, near the end
+    bt_low = np.zeros((len(lens), max(pages)), np.int32)
+    sm_low = np.empty(T, np.int64)
+    off = t0 = 0
+    for b, L in enumerate(lens):
+        bt_low[b, :pages[b]] = low[off:off + pages[b]]
+        off += pages[b]
+        pos = np.arange(L)
+        sm_low[t0:t0 + L] = bt_low[b, pos // P].astype(np.int64) * P + pos % P
+        t0 += L
+    shift = num_pages - n_used - 7
+    bt_high = np.where(np.arange(bt_low.shape[1])[None, :] < np.array(pages)[:, None],
+                       bt_low + shift, 0).astype(np.int32)
+    sm_high = sm_low + shift * P
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
+    cache = hkv.new_cache(f, num_pages, Hkv, DEV)
+    assert cache.numel() > (1 << 32)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm_high).to(DEV), cache)
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    ref_cache = np.zeros((n_used, Hkv, P, f.slot_bytes), np.uint8)
+    ref_cache[sm_low // P, :, sm_low % P] = slots
+    got_pages = cache[torch.from_numpy(np.arange(n_used) + shift).to(DEV)].cpu().numpy()
+    assert np.array_equal(got_pages, ref_cache)
+    q_to_req = np.arange(len(lens), dtype=np.int32).repeat(qps)
+    q_to_klen = np.array([[L - qps + 1 + j for j in range(qps)] for L in lens], np.int32).reshape(-1)
+    q = rng.standard_normal((len(q_to_req), Hq, D)).astype(np.float32)
+    scale = W.default_sm_scale(D)
+    got = hkv.decode_attention(f, torch.from_numpy(q).to(DEV), cache,
+                               torch.from_numpy(bt_high).to(DEV),
+                               torch.from_numpy(q_to_req).to(DEV),
+                               torch.from_numpy(q_to_klen).to(DEV), int(q_to_klen.max()), qps,
+                               scale).cpu().numpy()
+    ref = O.attention(fo, q, ref_cache, bt_low, q_to_req, q_to_klen, scale)
+    _assert_close(got, ref, f"{dtype} cache of {cache.numel() / 2**30:.1f} GiB")
+    del cache
+    torch.cuda.empty_cache()
