@@ -289,6 +289,33 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DevFmt f, DecArgs a
 constexpr int kMergeWaves = 8;
 constexpr int kMergeChunk = 4;
 
+// Row (query i, head h) of merge workgroup `id`.  The split kernel puts all
+// splits of one (request group, KV head) item on one XCD when the items per
+// split are a multiple of 8 (see wg_item): XCD (rg Hkv + kvh) mod 8.  The
+// merge ids are dealt the same way, id = 8 (rows_per_item (p / 8) + rr) +
+// p mod 8 for row rr of item p, so a row is merged on the XCD whose L2 holds
+// its partial records.  False for the ids past the last row.
+__device__ __forceinline__ bool merge_row(const DecArgs& a, uint32_t id, int& i, int& h) {
+  const uint32_t per_item = (uint32_t)(a.nsub * a.n_q * a.group);
+  const uint32_t k = id >> 3;
+  const uint32_t rr = k % per_item;
+  const uint32_t p = 8u * (k / per_item) + (id & 7u);
+  const uint32_t items = (uint32_t)(a.num_groups / a.nsub) * (uint32_t)a.num_kv_heads;
+  if (p >= items) return false;
+  const uint32_t rg = p / (uint32_t)a.num_kv_heads, kvh = p % (uint32_t)a.num_kv_heads;
+  const uint32_t qg = (uint32_t)(a.n_q * a.group);
+  const uint32_t sub = rr / qg, jg = rr % qg;
+  const uint32_t gi = rg * (uint32_t)a.nsub + sub;
+  i = (int)(gi * (uint32_t)a.n_q + jg / (uint32_t)a.group);
+  h = (int)(kvh * (uint32_t)a.group + jg % (uint32_t)a.group);
+  return true;
+}
+
+inline int64_t merge_wgs(int num_groups, int nsub, int num_kv_heads, int n_q, int group) {
+  const int64_t items = (int64_t)(num_groups / nsub) * num_kv_heads;
+  return 8 * (int64_t)nsub * n_q * group * ((items + 7) / 8);
+}
+
 template <int E>
 __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, DecArgs a,
                                                                    float* out) {
@@ -296,9 +323,8 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   __shared__ float red[kMergeWaves][D + 2];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t rowid = blockIdx.x;
-  const int i = (int)(rowid / a.num_q_heads);
-  const int h = (int)(rowid % a.num_q_heads);
+  int i, h;
+  if (!merge_row(a, blockIdx.x, i, h)) return;
   const int gi = i / a.n_q, j = i % a.n_q;
   const int kvh = h / a.group, g = h % a.group;
   const int r = j * a.group + g;
@@ -571,7 +597,9 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   q.num_splits = max_klen > 0 ? (max_klen + q.tokens_per_split - 1) / q.tokens_per_split : 1;
   // Grid sizes in work-items are 32-bit (512-lane workgroups at most).
   const int64_t wgs = decode_wgs(q.num_groups, q.nsub, num_kv_heads, q.num_splits);
-  const int64_t merge_rows = (int64_t)q.num_groups * q.n_q * num_q_heads;
+  const int64_t merge_rows = std::max<int64_t>(
+      (int64_t)q.num_groups * q.n_q * num_q_heads,
+      merge_wgs(q.num_groups, q.nsub, num_kv_heads, q.n_q, q.group));
   if (wgs * 512 > (int64_t)UINT32_MAX || merge_rows * kMergeWaves * kWave > (int64_t)UINT32_MAX)
     return false;
   q.num_wgs = wgs;
@@ -640,7 +668,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
       case 4: merge_rows_kernel<4><<<mgrid, mblock, 0, s>>>(f, a, out, rows); break;
     }
   } else {
-    const dim3 mgrid((unsigned)rows);
+    const dim3 mgrid((unsigned)merge_wgs(p.num_groups, p.nsub, num_kv_heads, p.n_q, p.group));
     switch (f.D / kWave) {
       case 1: merge_kernel<1><<<mgrid, mblock, 0, s>>>(f, a, out); break;
       case 2: merge_kernel<2><<<mgrid, mblock, 0, s>>>(f, a, out); break;
