@@ -32,6 +32,7 @@ METRIC = ("decode-attn packed-KV GB/s (% HBM peak) at 128K ctx; "
           "quantize-append tokens/s")
 INFINITY_CACHE_BYTES = 256 << 20
 WARM_SECONDS = 0.3
+DIST_BLOCKS = 20    # blocks of 10 decode calls for the median / p10 / p90
 
 
 def parse():
@@ -375,6 +376,22 @@ def main():
     decode_ms = d0.elapsed_time(d1) / n_t
     append_ms = max(ms_per_step - decode_ms, 0.0)
 
+    # Spread of the decode call: blocks of 10 calls in one back-to-back run,
+    # an event between blocks (per-call events would add their own gaps, and
+    # a synchronisation per block would let the clocks drop); median, p10 and
+    # p90 of the block averages.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(DIST_BLOCKS + 1)]
+    evs[0].record()
+    for b in range(DIST_BLOCKS):
+        for i in range(10):
+            run_decode(10 * b + i)
+        evs[b + 1].record()
+    torch.cuda.synchronize()
+    blk = [evs[b].elapsed_time(evs[b + 1]) / 10 * 1e3 for b in range(DIST_BLOCKS)]
+    dist = {"median": round(float(np.median(blk)), 3), "p10": round(float(np.percentile(blk, 10)), 3),
+            "p90": round(float(np.percentile(blk, 90)), 3), "blocks": DIST_BLOCKS,
+            "calls_per_block": 10}
+
     # Achievable read bandwidth beside the 8 TB/s peak: a plain streaming-read
     # probe (nontemporal 16-byte loads, eight in flight per thread) over 1 GiB.
     read_gbs = stream_read_gbs(torch, dev)
@@ -421,6 +438,7 @@ def main():
                             "probe": "nontemporal 16-byte streaming reads of 1 GiB, "
                                      "8192 x 256 threads, 8 loads in flight each",
                             "decode_frac": round(achieved / read_gbs, 4)},
+        "decode_us_dist": dist,
         "append_us": round(append_ms * 1e3, 3),
         "append_tokens_per_s": (round(len(rows) / (append_ms * 1e-3), 1)
                                 if append_ms > 0 else None),
