@@ -283,9 +283,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DevFmt f, DecArgs a
 // chunks of kMergeChunk, loading the (m, l) pair and o of every split of a
 // chunk together (one memory round trip per chunk), and keeps a running
 // (M, L, acc) in the exp2 domain; the waves then combine through LDS.  Only
-// the splits that start below the row's own klen are visited: each of those
+// the splits that start below the row's own klen are counted: each of those
 // holds at least one of the row's tokens, so its whole record was written and
-// is finite.
+// is finite.  The first chunk is requested before the klen is known (the
+// records of any split of the launch are in bounds) and the others only for
+// counted splits.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeChunk = 4;
 
@@ -316,6 +318,72 @@ inline int64_t merge_wgs(int num_groups, int nsub, int num_kv_heads, int n_q, in
   return 8 * (int64_t)nsub * n_q * group * ((items + 7) / 8);
 }
 
+// Sign words of the output dims kWave e + lane (e < E) of this lane, zero
+// without a sign pattern; fetched at the start, beside the other loads.
+template <int E>
+__device__ __forceinline__ void merge_signs(const DevFmt& f, int lane, uint32_t (&sw)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) sw[e] = f.use_signs ? f.sign_bits[2 * e + (lane >> 5)] : 0u;
+}
+
+// The (m, l) pairs and o of C records, splits s0 + st c.
+template <int E, int C>
+struct MergeChunk {
+  float2 ml[C];
+  float o[C][E];
+};
+
+// Requests the records of one chunk; splits at or past `lim` (at most
+// num_splits) load split 0's record instead, which is never counted for them.
+template <int E, int C>
+__device__ __forceinline__ void merge_load(MergeChunk<E, C>& k, const float* base, size_t sstride,
+                                           int s0, int st, int lim, int lane) {
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int s = s0 + st * c;
+    const float* ps = base + (s < lim ? s : 0) * sstride;
+    k.ml[c] = *(const float2*)ps;
+#pragma unroll
+    for (int e = 0; e < E; ++e) k.o[c][e] = ps[kPartialHead + kWave * e + lane];
+  }
+}
+
+// Folds a chunk into the running (M, L, acc) in the exp2 domain.  Records
+// at or past `n_live` (or with m = -inf) are skipped by select, never
+// multiplied, so whatever such a record holds cannot reach the sums.
+template <int E, int C>
+__device__ __forceinline__ void merge_fold(const MergeChunk<E, C>& k, int s0, int st, int n_live,
+                                           float& M, float& L, float (&acc)[E]) {
+  bool live[C];
+  float Mc = M;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    live[c] = s0 + st * c < n_live && k.ml[c].x != -INFINITY;
+    if (live[c]) Mc = fmaxf(Mc, k.ml[c].x);
+  }
+  // no live record yet: M = Mc = -inf and acc, L are still 0
+  const float alpha = Mc == -INFINITY ? 1.0f : exp2f(M - Mc);
+  L *= alpha;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const float w = live[c] ? exp2f(k.ml[c].x - Mc) : 0.0f;
+    L = live[c] ? fmaf(k.ml[c].y, w, L) : L;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = live[c] ? fmaf(k.o[c][e], w, acc[e]) : acc[e];
+  }
+  M = Mc;
+}
+
+// Splits holding tokens of a row of key length klen: each of them holds at
+// least one, so its whole record was written and is finite.
+__device__ __forceinline__ int merge_live(const DecArgs& a, int klen) {
+  return klen <= 0 ? 0 : min(a.num_splits, (klen + a.tokens_per_split - 1) / a.tokens_per_split);
+}
+
+// The first chunk of a row's records is requested together with the row's
+// key length (one memory round trip), and folded once the length is known.
 template <int E>
 __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, DecArgs a,
                                                                    float* out) {
@@ -323,49 +391,35 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   __shared__ float red[kMergeWaves][D + 2];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  int v_block = f.v_block;
+  float v_norm = f.v_norm;
+  asm("" : "+s"(v_block), "+s"(v_norm));
+  pin_args(a);
+  out = pin_global(out);
   int i, h;
   if (!merge_row(a, blockIdx.x, i, h)) return;
   const int gi = i / a.n_q, j = i % a.n_q;
   const int kvh = h / a.group, g = h % a.group;
   const int r = j * a.group + g;
   const int Rp = a.rows_pad;
-  const int klen = a.q_to_klen[i];
-  const int n_live = klen <= 0 ? 0 : min(a.num_splits, (klen + a.tokens_per_split - 1) /
-                                                           a.tokens_per_split);
   const float* base = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride +
                       (size_t)r * a.pstride;
   const size_t sstride = (size_t)Rp * a.pstride;
+  const int klen = a.q_to_klen[i];
+  uint32_t sw[E];
+  merge_signs<E>(f, lane, sw);
   float M = -INFINITY, L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int s0 = wave; s0 < n_live; s0 += kMergeWaves * kMergeChunk) {
-    float2 ml[kMergeChunk];
-    float o[kMergeChunk][E];
-#pragma unroll
-    for (int c = 0; c < kMergeChunk; ++c) {
-      // a split past the end reloads the first one with a zero weight
-      const int s = s0 + kMergeWaves * c;
-      const float* ps = base + (s < n_live ? s : s0) * sstride;
-      ml[c] = *(const float2*)ps;
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[c][e] = ps[kPartialHead + kWave * e + lane];
-    }
-    float Mc = M;
-#pragma unroll
-    for (int c = 0; c < kMergeChunk; ++c)
-      if (s0 + kMergeWaves * c < n_live) Mc = fmaxf(Mc, ml[c].x);
-    const float alpha = exp2f(M - Mc);  // M = -inf before the first chunk: 0
-    L *= alpha;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int c = 0; c < kMergeChunk; ++c) {
-      const float w = s0 + kMergeWaves * c < n_live ? exp2f(ml[c].x - Mc) : 0.0f;
-      L = fmaf(ml[c].y, w, L);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(o[c][e], w, acc[e]);
-    }
-    M = Mc;
+  // wave w takes splits w, w + kMergeWaves, ... in chunks of kMergeChunk
+  constexpr int kStep = kMergeWaves * kMergeChunk;
+  MergeChunk<E, kMergeChunk> k;
+  merge_load(k, base, sstride, wave, kMergeWaves, a.num_splits, lane);
+  const int n_live = merge_live(a, klen);
+  merge_fold(k, wave, kMergeWaves, n_live, M, L, acc);
+  for (int s0 = wave + kStep; s0 < n_live; s0 += kStep) {
+    merge_load(k, base, sstride, s0, kMergeWaves, n_live, lane);
+    merge_fold(k, s0, kMergeWaves, n_live, M, L, acc);
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) red[wave][kWave * e + lane] = acc[e];
@@ -397,20 +451,19 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] *= inv;
-  fwht_strided<E>(acc, f.v_block, f.v_norm);
+  fwht_strided<E>(acc, v_block, v_norm);
   float* dst = out + ((int64_t)i * a.num_q_heads + h) * D;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int d = kWave * e + lane;
-    dst[d] = f.use_signs ? apply_sign(f, acc[e], d) : acc[e];
-  }
+  for (int e = 0; e < E; ++e)
+    dst[kWave * e + lane] =
+        __uint_as_float(__float_as_uint(acc[e]) ^ (((sw[e] >> (lane & 31)) & 1u) << 31));
 }
 
 // The same merge with one wave per row (kMergeWaves rows per workgroup), for
-// plans with at most kRowChunk splits: a row's live records come in one
-// memory round trip and need no cross-wave combine, so many-row, few-split
-// shapes (tens of thousands of short rows) do not pay a workgroup and a
-// barrier per row.
+// plans with at most kRowChunk splits: a row's records come in one memory
+// round trip, together with its key length, and need no cross-wave combine,
+// so many-row, few-split shapes (tens of thousands of short rows) do not pay
+// a workgroup and a barrier per row.
 constexpr int kRowChunk = 8;
 
 template <int E>
@@ -419,6 +472,11 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_rows_kernel(DevFmt 
   constexpr int D = E * kWave;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  int v_block = f.v_block;
+  float v_norm = f.v_norm;
+  asm("" : "+s"(v_block), "+s"(v_norm));
+  pin_args(a);
+  out = pin_global(out);
   const int64_t rowid = (int64_t)blockIdx.x * kMergeWaves + wave;
   if (rowid >= rows) return;
   const int i = (int)(rowid / a.num_q_heads);
@@ -427,54 +485,32 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_rows_kernel(DevFmt 
   const int kvh = h / a.group, g = h % a.group;
   const int r = j * a.group + g;
   const int Rp = a.rows_pad;
-  const int klen = a.q_to_klen[i];
-  const int n_live = klen <= 0 ? 0 : min(a.num_splits, (klen + a.tokens_per_split - 1) /
-                                                           a.tokens_per_split);
   const float* base = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits) * Rp * a.pstride +
                       (size_t)r * a.pstride;
   const size_t sstride = (size_t)Rp * a.pstride;
+  const int klen = a.q_to_klen[i];
+  uint32_t sw[E];
+  merge_signs<E>(f, lane, sw);
   float M = -INFINITY, L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int s0 = 0; s0 < n_live; s0 += kRowChunk) {
-    float2 ml[kRowChunk];
-    float o[kRowChunk][E];
-#pragma unroll
-    for (int c = 0; c < kRowChunk; ++c) {
-      // a split past the end reloads the first one with a zero weight
-      const int s = s0 + c;
-      const float* ps = base + (s < n_live ? s : s0) * sstride;
-      ml[c] = *(const float2*)ps;
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[c][e] = ps[kPartialHead + kWave * e + lane];
-    }
-    float Mc = M;
-#pragma unroll
-    for (int c = 0; c < kRowChunk; ++c)
-      if (s0 + c < n_live) Mc = fmaxf(Mc, ml[c].x);
-    const float alpha = exp2f(M - Mc);  // M = -inf before the first chunk: 0
-    L *= alpha;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int c = 0; c < kRowChunk; ++c) {
-      const float w = s0 + c < n_live ? exp2f(ml[c].x - Mc) : 0.0f;
-      L = fmaf(ml[c].y, w, L);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(o[c][e], w, acc[e]);
-    }
-    M = Mc;
+  MergeChunk<E, kRowChunk> k;
+  merge_load(k, base, sstride, 0, 1, a.num_splits, lane);
+  const int n_live = merge_live(a, klen);
+  merge_fold(k, 0, 1, n_live, M, L, acc);
+  for (int s0 = kRowChunk; s0 < n_live; s0 += kRowChunk) {
+    merge_load(k, base, sstride, s0, 1, n_live, lane);
+    merge_fold(k, s0, 1, n_live, M, L, acc);
   }
   const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] *= inv;
-  fwht_strided<E>(acc, f.v_block, f.v_norm);
+  fwht_strided<E>(acc, v_block, v_norm);
   float* dst = out + ((int64_t)i * a.num_q_heads + h) * D;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int d = kWave * e + lane;
-    dst[d] = f.use_signs ? apply_sign(f, acc[e], d) : acc[e];
-  }
+  for (int e = 0; e < E; ++e)
+    dst[kWave * e + lane] =
+        __uint_as_float(__float_as_uint(acc[e]) ^ (((sw[e] >> (lane & 31)) & 1u) << 31));
 }
 
 int round_rows(int rows) {

@@ -97,6 +97,87 @@ __device__ __forceinline__ bool wg_item(const DecArgs& a, int& split, int& kvh, 
   return true;
 }
 
+// A kernel-argument pointer held in scalar registers from this point on,
+// still known to the compiler as a global-memory pointer.
+template <class T>
+__device__ __forceinline__ T* pin_global(T* p) {
+  uint64_t v = (uint64_t)(uintptr_t)p;
+  asm("" : "+s"(v));
+  return (T*)(__attribute__((address_space(1))) T*)v;
+}
+
+// Every word of the decode arguments fetched at this point, in one round
+// trip.  Left alone, the compiler loads each argument near its first use,
+// which in a kernel prologue puts several dependent kernel-argument fetches
+// ahead of the first cache load.  (The request map and the key lengths stay
+// plain argument pointers, so that their uniform reads remain scalar loads,
+// whose wait does not hold back the vector loads issued after them.)
+__device__ __forceinline__ void pin_args(DecArgs& a) {
+  asm("" : "+s"(a.q_f16), "+s"(a.num_q_heads), "+s"(a.num_kv_heads), "+s"(a.group),
+               "+s"(a.n_q), "+s"(a.rows), "+s"(a.rows_pad), "+s"(a.num_queries),
+               "+s"(a.num_groups), "+s"(a.nsub), "+s"(a.max_pages), "+s"(a.tokens_per_split),
+               "+s"(a.num_splits), "+s"(a.pstride));
+  a.query = pin_global(a.query);
+  a.cache = pin_global(a.cache);
+  a.block_table = pin_global(a.block_table);
+  a.ws = pin_global(a.ws);
+}
+
+// Raw bits of the values kWave e + lane (e < E) of query row r of the group
+// at q0 for KV head kvh, as one batch of loads with no wait between them
+// (rows past the group read row 0; query_value zeroes them).
+template <int E>
+__device__ __forceinline__ void query_row_raw(const DecArgs& a, int q0, int kvh, int r, int lane,
+                                              uint32_t (&qw)[E]) {
+  constexpr int D = E * kWave;
+  const int rq = r < a.rows ? r : 0;
+  const int64_t qrow = (int64_t)(q0 + rq / a.group) * a.num_q_heads + kvh * a.group + rq % a.group;
+  if (a.q_f16) {
+    const uint16_t* qp = (const uint16_t*)a.query + qrow * D + lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) qw[e] = qp[kWave * e];
+  } else {
+    const uint32_t* qp = (const uint32_t*)a.query + qrow * D + lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) qw[e] = qp[kWave * e];
+  }
+}
+
+__device__ __forceinline__ float query_value(const DecArgs& a, uint32_t w, bool live) {
+  const float v = a.q_f16 ? h2f((uint16_t)w) : __uint_as_float(w);
+  return live ? v : 0.0f;
+}
+
+// Sign words of the dims kWave e + lane (e < E) of this lane (word
+// 2 e + lane / 32, bit lane % 32), zero without a sign pattern.
+template <int E>
+__device__ __forceinline__ void lane_sign_words(const DevFmt& f, int lane, uint32_t (&sw)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) sw[e] = f.use_signs ? f.sign_bits[2 * e + (lane >> 5)] : 0u;
+}
+
+__device__ __forceinline__ float flip_sign(float x, uint32_t w, int lane) {
+  return __uint_as_float(__float_as_uint(x) ^ (((w >> (lane & 31)) & 1u) << 31));
+}
+
+// Key lengths of the group's queries, one per lane: lane l holds that of
+// query q0 + min(l, n_q - 1) (n_q <= kWave), from one vector load.
+__device__ __forceinline__ int group_klen_lane(const DecArgs& a, int q0, int lane) {
+  return a.q_to_klen[q0 + min(lane, a.n_q - 1)];
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, kWave));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 // Workgroups of a decode launch (see wg_item).
 inline int64_t decode_wgs(int num_groups, int nsub, int num_kv_heads, int num_splits) {
   const int64_t items = (int64_t)(num_groups / nsub) * num_kv_heads * num_splits;

@@ -215,36 +215,35 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
+  static_assert(kMaxSplitTiles <= kQWaves * kWave, "one page id per thread");
+  int page_size = f.page_size, k_block = f.k_block;
+  float k_norm = f.k_norm;
+  asm("" : "+s"(page_size), "+s"(k_block), "+s"(k_norm));
+  pin_args(a);
   int split, kvh, gi;
   if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
-  // Query rows wave + 8 k: their loads go out first, independent of the page table.
-  float qx[kQR][kE];
+  // ---- prologue: three memory round trips before the stream -------------
+  // (1) query rows wave + 8 k (raw bits), the key lengths of the group's
+  //     queries (one per lane, n_q <= RM) and the request; (2) the split's
+  //     page ids, to LDS, and this wave's first two (scalar); (3) the first
+  //     unit's tiles.  Every load of the prologue is unconditional (clamped
+  //     indices), so no wait before the barrier covers a later round trip.
+  uint32_t qw[kQR][kE];
 #pragma unroll
-  for (int k = 0; k < kQR; ++k) {
-    const int r = wave + kQWaves * k;
-    if (r < a.rows) {
-      const int j = r / a.group, g = r % a.group;
-      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
-#pragma unroll
-      for (int e = 0; e < kE; ++e) {
-        const int d = kWave * e + lane;
-        qx[k][e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
-                           : ((const float*)a.query)[qrow * kD + d];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < kE; ++e) qx[k][e] = 0.0f;
-    }
-  }
+  for (int k = 0; k < kQR; ++k) query_row_raw<kE>(a, q0, kvh, wave + kQWaves * k, lane, qw[k]);
+  uint32_t sw[kE];
+  lane_sign_words<kE>(f, lane, sw);
+  const int kl = group_klen_lane(a, q0, lane);
   const int req = a.q_to_req[q0];
-  int kmax = 0;
-  for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
+  const int kmax = wave_max_int(kl);
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(t_begin + a.tokens_per_split, kmax);
   float* part = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits + split) * RM *
                            a.pstride;
-  if (t_begin >= t_end) {
+  // (req < 0 never holds for a valid request map; testing it keeps the load
+  // of req ahead of this branch, in the first round trip.)
+  if (t_begin >= t_end || req < 0) {
     for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
       part[r * a.pstride + 0] = -INFINITY;
       part[r * a.pstride + 1] = 0.0f;
@@ -252,14 +251,16 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     return;
   }
 
-  // ---- page ids, first tiles, query planes ---------------------------------
   const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
-  const int ps = f.page_size;  // a power of two, multiple of kT
+  const int ps = page_size;  // a power of two, multiple of kT
   const int ps_shift = 31 - __builtin_clz(ps);
   const int nt = (t_end - t_begin + kT - 1) / kT;
   const int nu = (nt + 1) >> 1;
-  for (int t = threadIdx.x; t < nt; t += blockDim.x) L.pid[t] = bt[(t_begin + kT * t) >> ps_shift];
-  if (threadIdx.x == 0) L.next_unit = 2 * kQWaves;
+  // One page id per thread (nt <= kMaxSplitTiles); threads past the last
+  // tile load and later store the last one again.
+  const int tpid = min((int)threadIdx.x, nt - 1);
+  const int pidv = bt[(t_begin + kT * tpid) >> ps_shift];
+  __builtin_amdgcn_sched_barrier(0);
   const int tl = lane & 15, gq = lane >> 4;
   auto fetch_pid = [&](Tile& x, int kc, int page) {
     const int t0 = t_begin + kT * kc;
@@ -274,21 +275,27 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     const int kc = min(k, nt - 1);
     fetch_pid(x, kc, __builtin_amdgcn_readfirstlane(L.pid[kc]));
   };
+  // The first unit's tiles, with page ids read directly (a wave with no
+  // unit loads the last tile and never uses it).
   Tile ta, tb;
   const bool has_work = wave < nu;
-  if (has_work) {
-    const int k0 = 2 * wave, k1 = min(2 * wave + 1, nt - 1);
-    fetch_pid(ta, k0, bt[(t_begin + kT * k0) >> ps_shift]);
-    fetch_pid(tb, k1, bt[(t_begin + kT * k1) >> ps_shift]);
+  {
+    const int k0 = min(2 * wave, nt - 1), k1 = min(2 * wave + 1, nt - 1);
+    const int pg0 = bt[(t_begin + kT * k0) >> ps_shift];
+    const int pg1 = bt[(t_begin + kT * k1) >> ps_shift];
+    fetch_pid(ta, k0, pg0);
+    fetch_pid(tb, k1, pg1);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  L.pid[tpid] = pidv;
+  if (threadIdx.x == 0) L.next_unit = 2 * kQWaves;
 #pragma unroll
   for (int k = 0; k < kQR; ++k) {
     const int r = wave + kQWaves * k;
     float x[kE];
 #pragma unroll
-    for (int e = 0; e < kE; ++e)
-      x[e] = f.use_signs ? apply_sign(f, qx[k][e], kWave * e + lane) : qx[k][e];
-    if (r < a.rows) fwht_strided<kE>(x, f.k_block, f.k_norm);
+    for (int e = 0; e < kE; ++e) x[e] = flip_sign(query_value(a, qw[k][e], r < a.rows), sw[e], lane);
+    fwht_strided<kE>(x, k_block, k_norm);
     float qmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < kE; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
@@ -312,9 +319,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   // The score row of this lane: 8-row mode row n & 7 (lanes n, n + 8 hold its
   // hi and lo planes), 16-row mode row n.
   const int row = kK16 ? n : (n & 7);
-  const int klen_row = row < a.rows ? a.q_to_klen[q0 + row / a.group] : 0;
-  int kmin = kmax;
-  for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
+  const int klen_lane_row = __shfl(kl, (row < a.rows ? row : 0) / a.group, kWave);
+  const int klen_row = row < a.rows ? klen_lane_row : 0;
+  const int kmin = wave_min_int(kl);
   __syncthreads();
 
   const float qs = L.qsc[row];
@@ -751,38 +758,32 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  static_assert(kMaxSplitTiles <= W * kWave, "one page id per thread");
+  int page_size = f.page_size, k_block = f.k_block;
+  float k_norm = f.k_norm;
+  asm("" : "+s"(page_size), "+s"(k_block), "+s"(k_norm));
+  pin_args(a);
   int split, kvh, gi;
   if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
-  float qx[kQR][kE];
+  // ---- prologue: three memory round trips before the stream (as in
+  // decode_oct_kernel): query rows and key lengths, page ids, first tiles.
+  uint32_t qw[kQR][kE];
 #pragma unroll
-  for (int k = 0; k < kQR; ++k) {
-    const int r = wave + W * k;
-    if (r < a.rows) {
-      const int j = r / a.group, g = r % a.group;
-      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
-#pragma unroll
-      for (int e = 0; e < kE; ++e) {
-        const int d = kWave * e + lane;
-        qx[k][e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
-                           : ((const float*)a.query)[qrow * kD + d];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < kE; ++e) qx[k][e] = 0.0f;
-    }
-  }
+  for (int k = 0; k < kQR; ++k) query_row_raw<kE>(a, q0, kvh, wave + W * k, lane, qw[k]);
+  uint32_t sw[kE];
+  lane_sign_words<kE>(f, lane, sw);
+  const int kl = group_klen_lane(a, q0, lane);  // n_q <= kR32
   const int req = a.q_to_req[q0];
-  int kmax = 0, kmin = INT32_MAX;
-  for (int j = 0; j < a.n_q; ++j) {
-    kmax = max(kmax, a.q_to_klen[q0 + j]);
-    kmin = min(kmin, a.q_to_klen[q0 + j]);
-  }
+  const int kmax = wave_max_int(kl);
+  const int kmin = wave_min_int(kl);
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(t_begin + a.tokens_per_split, kmax);
   float* part = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits + split) * kR32 *
                            a.pstride;
-  if (t_begin >= t_end) {
+  // (req < 0 never holds for a valid request map; testing it keeps the load
+  // of req ahead of this branch, in the first round trip.)
+  if (t_begin >= t_end || req < 0) {
     for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
       part[r * a.pstride + 0] = -INFINITY;
       part[r * a.pstride + 1] = 0.0f;
@@ -790,14 +791,14 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
     return;
   }
 
-  // ---- page ids, first unit, query planes ---------------------------------
   const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
-  const int ps = f.page_size;
+  const int ps = page_size;
   const int ps_shift = 31 - __builtin_clz(ps);
   const int nt = (t_end - t_begin + kT - 1) / kT;
   const int nu = (nt + 1) >> 1;
-  for (int t = threadIdx.x; t < nt; t += blockDim.x) L.pid[t] = bt[(t_begin + kT * t) >> ps_shift];
-  if (threadIdx.x == 0) L.next_unit = W;
+  const int tpid = min((int)threadIdx.x, nt - 1);
+  const int pidv = bt[(t_begin + kT * tpid) >> ps_shift];
+  __builtin_amdgcn_sched_barrier(0);
   const int tl = lane & 15, gq = lane >> 4;
   auto fetch_pid = [&](Tile& x, int kc, int page) {
     const int t0 = t_begin + kT * kc;
@@ -814,19 +815,23 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
   };
   Tile ta, tb;
   const bool has_work = wave < nu;
-  if (has_work) {
-    const int k0 = 2 * wave, k1 = min(2 * wave + 1, nt - 1);
-    fetch_pid(ta, k0, bt[(t_begin + kT * k0) >> ps_shift]);
-    fetch_pid(tb, k1, bt[(t_begin + kT * k1) >> ps_shift]);
+  {
+    const int k0 = min(2 * wave, nt - 1), k1 = min(2 * wave + 1, nt - 1);
+    const int pg0 = bt[(t_begin + kT * k0) >> ps_shift];
+    const int pg1 = bt[(t_begin + kT * k1) >> ps_shift];
+    fetch_pid(ta, k0, pg0);
+    fetch_pid(tb, k1, pg1);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  L.pid[tpid] = pidv;
+  if (threadIdx.x == 0) L.next_unit = W;
 #pragma unroll
   for (int k = 0; k < kQR; ++k) {
     const int r = wave + W * k;
     float x[kE];
 #pragma unroll
-    for (int e = 0; e < kE; ++e)
-      x[e] = f.use_signs ? apply_sign(f, qx[k][e], kWave * e + lane) : qx[k][e];
-    if (r < a.rows) fwht_strided<kE>(x, f.k_block, f.k_norm);
+    for (int e = 0; e < kE; ++e) x[e] = flip_sign(query_value(a, qw[k][e], r < a.rows), sw[e], lane);
+    fwht_strided<kE>(x, k_block, k_norm);
     float qmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < kE; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
@@ -847,7 +852,8 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
   }
   const int n = lane & 31;  // this lane's query row (scores, P.V columns) and token (K operand)
   const int h = lane >> 5;
-  const int klen_row = n < a.rows ? a.q_to_klen[q0 + n / a.group] : 0;
+  const int klen_lane_row = __shfl(kl, (n < a.rows ? n : 0) / a.group, kWave);
+  const int klen_row = n < a.rows ? klen_lane_row : 0;
   const int t_lim = min(t_end, kmin);
   // V operand rows: dim 16 (8 b + m') + 4 i + j for row n = 4 m' + j.
   const int vm = n >> 2, vj = n & 3;

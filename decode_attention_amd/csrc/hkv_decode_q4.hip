@@ -53,6 +53,7 @@ constexpr int kVStride = kT + 4;       // padded token stride of the transposed 
 constexpr float kLazy = 8.0f;          // log2 headroom before the running max is raised
 constexpr int kQWaves = 8;             // waves per workgroup (two per SIMD)
 constexpr int kMaxSplitTiles = 256;    // page ids of a split's tiles held in LDS
+static_assert(kMaxSplitTiles <= kQWaves * kWave, "one page id per thread");
 
 __device__ __forceinline__ float f16lo(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float f16hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
@@ -106,35 +107,52 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
+  int page_size = f.page_size, k_block = f.k_block;
+  float k_norm = f.k_norm;
+  asm("" : "+s"(page_size), "+s"(k_block), "+s"(k_norm));
+  pin_args(a);
   int split, kvh, gi;
   if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
-  // Query row `wave`: its loads go out first, independent of the page table.
-  float qx[4];
-  {
-    const int r = wave;
-    if (r < a.rows) {
-      const int j = r / a.group, g = r % a.group;
-      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
+  // ---- prologue: three memory round trips before the stream -------------
+  // (1) the query row of this wave (raw bits), the request and the key
+  //     lengths of the group's queries; (2) the split's page ids, to LDS, and
+  //     this wave's first two (scalar); (3) the first unit's tiles.  Nothing
+  //     waits on a later round trip before the barrier: every load of the
+  //     prologue is unconditional (clamped indices), so the counter waits
+  //     stay partial across the tile loads.  Rows past the group load row 0
+  //     and are zeroed.
+  const bool live_q = wave < a.rows;
+  const int rq = live_q ? wave : 0;
+  const int64_t qrow = (int64_t)(q0 + rq / a.group) * a.num_q_heads + kvh * a.group + rq % a.group;
+  uint32_t qw[4];
+  if (a.q_f16) {
+    const uint16_t* qp = (const uint16_t*)a.query + qrow * kD + lane;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = kWave * e + lane;
-        qx[e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
-                        : ((const float*)a.query)[qrow * kD + d];
-      }
-    } else {
+    for (int e = 0; e < 4; ++e) qw[e] = qp[kWave * e];
+  } else {
+    const uint32_t* qp = (const uint32_t*)a.query + qrow * kD + lane;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qx[e] = 0.0f;
-    }
+    for (int e = 0; e < 4; ++e) qw[e] = qp[kWave * e];
   }
   const int req = a.q_to_req[q0];
-  int kmax = 0;
-  for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
+  int kl[kRows];  // key lengths of the group's queries (the last one repeated)
+#pragma unroll
+  for (int j = 0; j < kRows; ++j) kl[j] = a.q_to_klen[q0 + min(j, a.n_q - 1)];
+  int kmax = kl[0], kmin = kl[0];
+#pragma unroll
+  for (int j = 1; j < kRows; ++j) {
+    kmax = max(kmax, kl[j]);
+    kmin = min(kmin, kl[j]);
+  }
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(t_begin + a.tokens_per_split, kmax);
   float* part = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits + split) * kRows *
                            a.pstride;
-  if (t_begin >= t_end) {
+  // (req < 0 never holds for a valid request map; testing it here keeps the
+  // load of req ahead of this branch, in the same round trip as the key
+  // lengths, instead of sunk below it.)
+  if (t_begin >= t_end || req < 0) {
     for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
       part[r * a.pstride + 0] = -INFINITY;
       part[r * a.pstride + 1] = 0.0f;
@@ -142,18 +160,20 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
     return;
   }
 
-  // ---- page ids, first tiles, query planes ---------------------------------
   // The split is a queue of units of two consecutive 16-token tiles.  Wave w
   // starts with units w and w + 8 and then takes the next untaken unit, so
   // the two waves sharing a SIMD finish together however the issue slots
   // fall between them.
   const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
-  const int ps = f.page_size;                 // a power of two, multiple of kT
+  const int ps = page_size;                   // a power of two, multiple of kT
   const int ps_shift = 31 - __builtin_clz(ps);
   const int nt = (t_end - t_begin + kT - 1) / kT;              // tiles in the split
   const int nu = (nt + 1) >> 1;                                // units in the split
-  for (int t = threadIdx.x; t < nt; t += blockDim.x) L.pid[t] = bt[(t_begin + kT * t) >> ps_shift];
-  if (threadIdx.x == 0) L.next_unit = 2 * kQWaves;
+  // One page id per thread (nt <= kMaxSplitTiles); threads past the last
+  // tile load and later store the last one again.
+  const int tpid = min((int)threadIdx.x, nt - 1);
+  const int pidv = bt[(t_begin + kT * tpid) >> ps_shift];
+  __builtin_amdgcn_sched_barrier(0);
   const int tl = lane & 15, gq = lane >> 4;
   const int scale_kind = (lane >> 4) & 1;
   // Tile k of the split (clamped to the last tile: the scores of a tile past
@@ -170,23 +190,32 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
     const int kc = min(k, nt - 1);
     fetch_pid(x, kc, __builtin_amdgcn_readfirstlane(L.pid[kc]));
   };
-  // The first unit's tiles are requested before the query work, with page
-  // ids read directly, so their latency overlaps it.
+  // The first unit's tiles, with page ids read directly (a wave with no
+  // unit loads the last tile and never uses it).
   Tile ta, tb;
   const bool has_work = wave < nu;
-  if (has_work) {
-    const int k0 = 2 * wave, k1 = min(2 * wave + 1, nt - 1);
-    fetch_pid(ta, k0, bt[(t_begin + kT * k0) >> ps_shift]);
-    fetch_pid(tb, k1, bt[(t_begin + kT * k1) >> ps_shift]);
+  {
+    const int k0 = min(2 * wave, nt - 1), k1 = min(2 * wave + 1, nt - 1);
+    const int pg0 = bt[(t_begin + kT * k0) >> ps_shift];
+    const int pg1 = bt[(t_begin + kT * k1) >> ps_shift];
+    fetch_pid(ta, k0, pg0);
+    fetch_pid(tb, k1, pg1);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  L.pid[tpid] = pidv;
+  if (threadIdx.x == 0) L.next_unit = 2 * kQWaves;
 
-  // Query row `wave` -> rotated, scaled int8 planes (B operand).
+  // Query row `wave` -> rotated, scaled int8 planes (B operand).  Q4_0 has
+  // no sign pattern.
   {
     const int r = wave;
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = f.use_signs ? apply_sign(f, qx[e], kWave * e + lane) : qx[e];
-    if (r < a.rows) fwht_strided<4>(x, f.k_block, f.k_norm);
+    for (int e = 0; e < 4; ++e) {
+      const float v = a.q_f16 ? h2f((uint16_t)qw[e]) : __uint_as_float(qw[e]);
+      x[e] = live_q ? v : 0.0f;
+    }
+    fwht_strided<4>(x, k_block, k_norm);
     float qmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
@@ -209,9 +238,12 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
   const int n = lane & 15;   // score column (row r = n & 7, plane = n >> 3)
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of a tile in the score layout
   const int row = n & 7;
-  const int klen_row = row < a.rows ? a.q_to_klen[q0 + row / a.group] : 0;
-  int kmin = kmax;
-  for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
+  int klen_row = 0;
+  if (row < a.rows) {
+    const int jr = row / a.group;
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) klen_row = j == jr ? kl[j] : klen_row;
+  }
   __syncthreads();
 
   const float qs = L.qsc[row];
@@ -553,7 +585,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
 
 bool q4_mfma_supported(const DevFmt& f, int rows) {
   const bool pow2 = (f.page_size & (f.page_size - 1)) == 0;
-  return f.kind == HKV_KIND_Q4_0 && f.D == kD && rows <= kRows && f.page_size % kT == 0 && pow2;
+  return f.kind == HKV_KIND_Q4_0 && !f.use_signs && f.D == kD && rows <= kRows &&
+         f.page_size % kT == 0 && pow2;
 }
 
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {

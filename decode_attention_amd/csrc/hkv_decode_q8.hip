@@ -52,6 +52,7 @@ constexpr int kVS = kT + 4;             // padded token stride of the transposed
 constexpr float kLazy = 8.0f;           // log2 headroom before the running max is raised
 constexpr int kQWaves = 8;              // waves per workgroup (two per SIMD)
 constexpr int kMaxSplitTiles = 256;     // page ids of a split's tiles held in LDS
+static_assert(kMaxSplitTiles <= kQWaves * kWave, "one page id per thread");
 
 // Lane (tl, gq) of a tile: token tl's K codes 32 b + 8 gq .. + 7 of every
 // block b (the score A operand of lane (tl, gq)), V chunks gq, 4 + gq,
@@ -87,35 +88,33 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
+  int page_size = f.page_size, k_block = f.k_block;
+  float k_norm = f.k_norm;
+  asm("" : "+s"(page_size), "+s"(k_block), "+s"(k_norm));
+  pin_args(a);
   int split, kvh, gi;
   if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
-  // Query row `wave`: its loads go out first, independent of the page table.
-  float qx[4];
-  {
-    const int r = wave;
-    if (r < a.rows) {
-      const int j = r / a.group, g = r % a.group;
-      const int64_t qrow = (int64_t)(q0 + j) * a.num_q_heads + kvh * a.group + g;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = kWave * e + lane;
-        qx[e] = a.q_f16 ? h2f(((const uint16_t*)a.query)[qrow * kD + d])
-                        : ((const float*)a.query)[qrow * kD + d];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qx[e] = 0.0f;
-    }
-  }
+  // ---- prologue: three memory round trips before the stream -------------
+  // (1) the query row of this wave (raw bits), the key lengths of the
+  //     group's queries (one per lane) and the request; (2) the split's page
+  //     ids, to LDS, and this wave's first two (scalar); (3) the first unit's
+  //     tiles.  Every load of the prologue is unconditional (clamped
+  //     indices), so no wait before the barrier covers a later round trip.
+  uint32_t qw[4];
+  query_row_raw<4>(a, q0, kvh, wave, lane, qw);
+  uint32_t sw[4];
+  lane_sign_words<4>(f, lane, sw);
+  const int kl = group_klen_lane(a, q0, lane);
   const int req = a.q_to_req[q0];
-  int kmax = 0;
-  for (int j = 0; j < a.n_q; ++j) kmax = max(kmax, a.q_to_klen[q0 + j]);
+  const int kmax = wave_max_int(kl);
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(t_begin + a.tokens_per_split, kmax);
   float* part = a.ws + (((size_t)gi * a.num_kv_heads + kvh) * a.num_splits + split) * kRows *
                            a.pstride;
-  if (t_begin >= t_end) {
+  // (req < 0 never holds for a valid request map; testing it keeps the load
+  // of req ahead of this branch, in the first round trip.)
+  if (t_begin >= t_end || req < 0) {
     for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
       part[r * a.pstride + 0] = -INFINITY;
       part[r * a.pstride + 1] = 0.0f;
@@ -123,14 +122,16 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
     return;
   }
 
-  // ---- page ids, first unit, query planes ---------------------------------
   const int32_t* bt = a.block_table + (int64_t)req * a.max_pages;
-  const int ps = f.page_size;                 // a power of two, multiple of kT
+  const int ps = page_size;                   // a power of two, multiple of kT
   const int ps_shift = 31 - __builtin_clz(ps);
   const int nt = (t_end - t_begin + kT - 1) / kT;  // tiles in the split
   const int nu = (nt + 1) >> 1;                    // units in the split
-  for (int t = threadIdx.x; t < nt; t += blockDim.x) L.pid[t] = bt[(t_begin + kT * t) >> ps_shift];
-  if (threadIdx.x == 0) L.next_unit = kQWaves;
+  // One page id per thread (nt <= kMaxSplitTiles); threads past the last
+  // tile load and later store the last one again.
+  const int tpid = min((int)threadIdx.x, nt - 1);
+  const int pidv = bt[(t_begin + kT * tpid) >> ps_shift];
+  __builtin_amdgcn_sched_barrier(0);
   const int tl = lane & 15, gq = lane >> 4;
   // Tile k of the split (clamped to the last tile: the scores of a tile past
   // the end are masked, so reloading the last one keeps every load in
@@ -150,21 +151,28 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
     const int kc = min(k, nt - 1);
     fetch_pid(x, kc, __builtin_amdgcn_readfirstlane(L.pid[kc]));
   };
+  // The first unit's tiles, with page ids read directly (a wave with no
+  // unit loads the last tile and never uses it).
   Tile8 ta, tb;
   const bool has_work = wave < nu;
-  if (has_work) {
-    const int k0 = 2 * wave, k1 = min(2 * wave + 1, nt - 1);
-    fetch_pid(ta, k0, bt[(t_begin + kT * k0) >> ps_shift]);
-    fetch_pid(tb, k1, bt[(t_begin + kT * k1) >> ps_shift]);
+  {
+    const int k0 = min(2 * wave, nt - 1), k1 = min(2 * wave + 1, nt - 1);
+    const int pg0 = bt[(t_begin + kT * k0) >> ps_shift];
+    const int pg1 = bt[(t_begin + kT * k1) >> ps_shift];
+    fetch_pid(ta, k0, pg0);
+    fetch_pid(tb, k1, pg1);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  L.pid[tpid] = pidv;
+  if (threadIdx.x == 0) L.next_unit = kQWaves;
 
   // Query row `wave` -> rotated, scaled int8 planes (B operand).
   {
     const int r = wave;
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = f.use_signs ? apply_sign(f, qx[e], kWave * e + lane) : qx[e];
-    if (r < a.rows) fwht_strided<4>(x, f.k_block, f.k_norm);
+    for (int e = 0; e < 4; ++e) x[e] = flip_sign(query_value(a, qw[e], r < a.rows), sw[e], lane);
+    fwht_strided<4>(x, k_block, k_norm);
     float qmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
@@ -187,9 +195,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
   const int n = lane & 15;   // score column (row r = n & 7, plane = n >> 3)
   const int g = lane >> 4;   // lane group: tokens 4g..4g+3 of a tile in the score layout
   const int row = n & 7;
-  const int klen_row = row < a.rows ? a.q_to_klen[q0 + row / a.group] : 0;
-  int kmin = kmax;
-  for (int j = 0; j < a.n_q; ++j) kmin = min(kmin, a.q_to_klen[q0 + j]);
+  const int klen_lane_row = __shfl(kl, (row < a.rows ? row : 0) / a.group, kWave);
+  const int klen_row = row < a.rows ? klen_lane_row : 0;
+  const int kmin = wave_min_int(kl);
   __syncthreads();
 
   const float qs = L.qsc[row];
