@@ -394,18 +394,150 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_append_kernel(
 // ---------------------------------------------------------------------------
 // Q4_0 and Q8_0 quantize-append for many rows: 16 lanes per row, four rows
 // per wave.
-// Lane l of a 16-lane row holds elements 64q + 4l + i (i = 0..3) of its row
-// for each 64-wide group q, so the element index bits 0-1 live in a
-// register, bits 2-5 in the lane (exchanges stay inside the 16-lane DPP
-// row), bits 6-7 in q.  The butterfly stages still run in ascending stride
-// (1, 2 in registers; 4..32 across lanes; 64, 128 in registers), each as the
-// same (a + b, a - b) pair, so the bytes equal those of the kernel above.
-// A 32-value block is one q of one 8-lane half-row.
+// A lane of a 16-lane row holds four consecutive elements 64q + 4e + i
+// (i = 0..3) of its row for each 64-wide group q, so the element index bits
+// 0-1 live in a register, bits 2-5 (e) in the lane (exchanges stay inside
+// the 16-lane DPP row), bits 6-7 in q.  The butterfly stages still run in
+// ascending stride (1, 2 in registers; 4..32 across lanes; 64, 128 in
+// registers), each as the same (a + b, a - b) pair up to sign, so the bytes
+// equal those of the kernel above.  A 32-value block is one q of one 8-lane
+// half-row.
+
+// Lane order of the Q4_0 / Q8_0 many-row kernel.  Element bits 2-5 of a
+// 64-wide group, e = (e2, e3, e4, e5), sit in lane e2 ^ 2 e3 ^ 7 e4 ^ 8 e5
+// of the 16-lane row, so the partner of every cross-lane butterfly stage is
+// one DPP move: lane xor 1 (quad_perm [1,0,3,2]), xor 2 (quad_perm
+// [2,3,0,1]), xor 7 (row_half_mirror) and xor 8 (row_ror:8).  Flipping e5
+// flips lane bit 3 only, so a 32-value block (fixed e5) is still a half-row;
+// flipping e2 flips lane bit 0 only, so the two nibbles of a Q4_0 byte are
+// still lanes l and l ^ 1.  Returns e (bits 0-3) of lane l.
+__device__ __forceinline__ int qrow_elem(int l) {
+  const int e4 = (l >> 2) & 1, e5 = (l >> 3) & 1;
+  const int e3 = ((l >> 1) & 1) ^ e4, e2 = (l & 1) ^ e4;
+  return e2 | (e3 << 1) | (e4 << 2) | (e5 << 3);
+}
+
+// One cross-lane butterfly stage as one fused DPP multiply-add per value:
+// x + sgn * partner with sgn = -1 in the upper lanes of the stage.  The lower
+// lane gets a + b; the upper lane gets b - a, the negated a - b.  The two
+// lanes of a later pair differ only in a bit not yet transformed, so they
+// carry the same sign, and the lower/upper results of that stage are again
+// a + b and the negated a - b of the signed values; round-to-nearest is
+// symmetric in the sign, so every magnitude is bitwise the one of the plain
+// (a + b, a - b) stage.  The accumulated sign, (-1)^(e2 + e3 + e4 + e5), is
+// removed by the final normalisation multiply.  (Only the sign of an exact
+// zero can differ; neither quantizer reads it.)
+//
+// The compiler does not fold a DPP move into v_fmac_f32, so the stage is
+// written out: v_fmac_f32_dpp x, x(partner), sgn reads the partner's x
+// through the DPP lane pattern and adds sgn times it to the lane's own x.
+// Each block opens and closes with two wait states (s_nop 1), the distance
+// a DPP read of a register must keep from a VALU write of it; inside a block
+// no instruction reads a register an earlier one wrote.
+#define HKV_FMAC_DPP(CTL, N) "v_fmac_f32_dpp %" #N ", %" #N ", %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"
+#define HKV_FMAC_DPP4(CTL, A, B, C, D) \
+  HKV_FMAC_DPP(CTL, A) HKV_FMAC_DPP(CTL, B) HKV_FMAC_DPP(CTL, C) HKV_FMAC_DPP(CTL, D)
+
+template <int Q>
+struct FwhtStageAsm;
+template <>
+struct FwhtStageAsm<1> {
+  template <int CTRL>
+  static __device__ __forceinline__ void run(float (&x)[1][4], float sgn);
+};
+template <>
+struct FwhtStageAsm<2> {
+  template <int CTRL>
+  static __device__ __forceinline__ void run(float (&x)[2][4], float sgn);
+};
+template <>
+struct FwhtStageAsm<4> {
+  template <int CTRL>
+  static __device__ __forceinline__ void run(float (&x)[4][4], float sgn);
+};
+
+#define HKV_STAGE_DEFS(CTRL, CTL)                                                                \
+  template <>                                                                                   \
+  __device__ __forceinline__ void FwhtStageAsm<1>::run<CTRL>(float (&x)[1][4], float sgn) {     \
+    asm("s_nop 1\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) "s_nop 1"                                  \
+        : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3])                           \
+        : [s] "v"(sgn));                                                                        \
+  }                                                                                             \
+  template <>                                                                                   \
+  __device__ __forceinline__ void FwhtStageAsm<2>::run<CTRL>(float (&x)[2][4], float sgn) {     \
+    asm("s_nop 1\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) HKV_FMAC_DPP4(CTL, 4, 5, 6, 7) "s_nop 1"   \
+        : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]),            \
+          "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3])                                           \
+        : [s] "v"(sgn));                                                                        \
+  }                                                                                             \
+  template <>                                                                                   \
+  __device__ __forceinline__ void FwhtStageAsm<4>::run<CTRL>(float (&x)[4][4], float sgn) {     \
+    asm("s_nop 1\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) HKV_FMAC_DPP4(CTL, 4, 5, 6, 7)              \
+            HKV_FMAC_DPP4(CTL, 8, 9, 10, 11) HKV_FMAC_DPP4(CTL, 12, 13, 14, 15) "s_nop 1"         \
+        : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]),            \
+          "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3]), "+v"(x[2][0]), "+v"(x[2][1]),            \
+          "+v"(x[2][2]), "+v"(x[2][3]), "+v"(x[3][0]), "+v"(x[3][1]), "+v"(x[3][2]),            \
+          "+v"(x[3][3])                                                                         \
+        : [s] "v"(sgn));                                                                        \
+  }
+
+HKV_STAGE_DEFS(0xB1, "quad_perm:[1,0,3,2]")
+HKV_STAGE_DEFS(0x4E, "quad_perm:[2,3,0,1]")
+HKV_STAGE_DEFS(0x141, "row_half_mirror")
+HKV_STAGE_DEFS(0x128, "row_ror:8")
+#undef HKV_STAGE_DEFS
+#undef HKV_FMAC_DPP4
+#undef HKV_FMAC_DPP
+
+template <int CTRL, int Q>
+__device__ __forceinline__ void fwht_stage_fused(float (&x)[Q][4], float sgn) {
+  FwhtStageAsm<Q>::template run<CTRL>(x, sgn);
+}
+
+// fwht_rows16 in the lane order of qrow_elem.
+template <int Q>
+__device__ __forceinline__ void fwht_rows16_q(float (&x)[Q][4], int e, float norm) {
+  // h = 1, 2: registers
+#pragma unroll
+  for (int h = 1; h <= 2; h <<= 1)
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((i & h) == 0) {
+          const float a = x[q][i], b = x[q][i + h];
+          x[q][i] = a + b;
+          x[q][i + h] = a - b;
+        }
+  // h = 4, 8, 16, 32: element bits 2, 3, 4, 5 across lanes
+  fwht_stage_fused<0xB1>(x, (e & 1) ? -1.0f : 1.0f);
+  fwht_stage_fused<0x4E>(x, (e & 2) ? -1.0f : 1.0f);
+  fwht_stage_fused<0x141>(x, (e & 4) ? -1.0f : 1.0f);
+  fwht_stage_fused<0x128>(x, (e & 8) ? -1.0f : 1.0f);
+  // h = 64, 128: register groups (both values carry the lane's sign)
+#pragma unroll
+  for (int hq = 1; hq < Q; hq <<= 1)
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if ((q & hq) == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = x[q][i], b = x[q + hq][i];
+          x[q][i] = a + b;
+          x[q + hq][i] = a - b;
+        }
+  const float sn = (__builtin_popcount(e) & 1) ? -norm : norm;
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * sn;
+}
 
 // One 64-wide group: codes packed into the words of this lane pair and the
-// fp16 scales of its two blocks.  On return `word` (even lanes) is slot word
-// 8q + l/2 of the segment and `scale` (lanes 0-7 of the row) is the scale
-// word of the group (block 2q | block 2q+1 << 16).
+// fp16 scales of its two blocks, in the lane order of qrow_elem.  On return
+// `word` (lanes with e2 = 0) is slot word 8q + e/2 of the segment and `scale`
+// (lanes 0-7 of the row) is the scale word of the group (block 2q | block
+// 2q+1 << 16).
 __device__ __forceinline__ void q4_group16(const float (&x)[4], uint32_t* word,
                                            uint32_t* scale) {
   uint32_t key[4];
@@ -435,9 +567,9 @@ __device__ __forceinline__ void q4_group16(const float (&x)[4], uint32_t* word,
   *scale = h | (dpp<0x128>(h) << 16);  // row_ror:8 -> the other block's scale
 }
 
-// Q8_0 over one 64-wide group in the 16-lane layout: `word` is slot word
-// 16q + l (this lane's four int8 codes), `scale` (lanes 0-7) the scale word
-// of the group, as for Q4_0.
+// Q8_0 over one 64-wide group in the lane order of qrow_elem: `word` is slot
+// word 16q + e (this lane's four int8 codes), `scale` (lanes 0-7) the scale
+// word of the group, as for Q4_0.
 __device__ __forceinline__ void q8_group16(const float (&x)[4], uint32_t* word,
                                            uint32_t* scale) {
   uint32_t a = max(max(__float_as_uint(x[0]) & 0x7FFFFFFFu, __float_as_uint(x[1]) & 0x7FFFFFFFu),
@@ -455,15 +587,16 @@ __device__ __forceinline__ void q8_group16(const float (&x)[4], uint32_t* word,
   *scale = h | (dpp<0x128>(h) << 16);
 }
 
+// Elements 64q + e4 .. + 3 (q < Q) of the row's K and V, for this lane's
+// element offset e4 in a 64-wide group.
 template <int Q, bool F16>
-__device__ __forceinline__ void fetch_rows16(const void* key, const void* value, int row,
+__device__ __forceinline__ void fetch_rows16(const void* key, const void* value, int row, int e4,
                                              uint32_t (&rk)[Q][F16 ? 2 : 4],
                                              uint32_t (&rv)[Q][F16 ? 2 : 4]) {
-  const int l = lane_id() & 15;
   constexpr int D = 64 * Q;
   if (F16) {
-    const uint2* pk = (const uint2*)((const uint16_t*)key + (int64_t)row * D + 4 * l);
-    const uint2* pv = (const uint2*)((const uint16_t*)value + (int64_t)row * D + 4 * l);
+    const uint2* pk = (const uint2*)((const uint16_t*)key + (int64_t)row * D + e4);
+    const uint2* pv = (const uint2*)((const uint16_t*)value + (int64_t)row * D + e4);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const uint2 a = pk[16 * q], b = pv[16 * q];
@@ -471,8 +604,8 @@ __device__ __forceinline__ void fetch_rows16(const void* key, const void* value,
       rv[q][0] = b.x, rv[q][1] = b.y;
     }
   } else {
-    const uint4* pk = (const uint4*)((const float*)key + (int64_t)row * D + 4 * l);
-    const uint4* pv = (const uint4*)((const float*)value + (int64_t)row * D + 4 * l);
+    const uint4* pk = (const uint4*)((const float*)key + (int64_t)row * D + e4);
+    const uint4* pv = (const uint4*)((const float*)value + (int64_t)row * D + e4);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const uint4 a = pk[16 * q], b = pv[16 * q];
@@ -509,13 +642,14 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
   constexpr int R = F16 ? 2 : 4;
   const int lane = lane_id();
   const int l = lane & 15;
+  const int e = qrow_elem(l);  // this lane's element bits 2-5
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int stride = (int)gridDim.x * kQuantWaves * 4;
   int base = ((int)blockIdx.x * kQuantWaves + wave) * 4;
   if (base >= rows) return;
   uint32_t rk[Q][R], rv[Q][R];
   int row = base + (lane >> 4);
-  fetch_rows16<Q, F16>(key, value, min(row, rows - 1), rk, rv);
+  fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * e, rk, rv);
   int64_t sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
   for (;;) {
     float k[Q][4], v[Q][4];
@@ -526,11 +660,11 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
     base += stride;
     row += stride;
     if (base < rows) {  // the next four rows load during this group
-      fetch_rows16<Q, F16>(key, value, min(row, rows - 1), rk, rv);
+      fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * e, rk, rv);
       sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
     }
-    fwht_rows16<Q>(k, f.k_norm);
-    fwht_rows16<Q>(v, f.v_norm);
+    fwht_rows16_q<Q>(k, e, f.k_norm);
+    fwht_rows16_q<Q>(v, e, f.v_norm);
     uint32_t wk[Q], wv[Q], sk[Q], sv[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
@@ -564,14 +698,14 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
       if (KIND == HKV_KIND_Q8_0) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-          dst[16 * q + l] = wk[q];
-          dst[f.off_v / 4 + 16 * q + l] = wv[q];
+          dst[16 * q + e] = wk[q];
+          dst[f.off_v / 4 + 16 * q + e] = wv[q];
         }
-      } else if ((l & 1) == 0) {
+      } else if ((e & 1) == 0) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-          dst[8 * q + (l >> 1)] = wk[q];
-          dst[f.off_v / 4 + 8 * q + (l >> 1)] = wv[q];
+          dst[8 * q + (e >> 1)] = wk[q];
+          dst[f.off_v / 4 + 8 * q + (e >> 1)] = wv[q];
         }
       }
       if (l < 2 * Q) dst[f.off_scales / 4 + l] = sw;
@@ -815,7 +949,7 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
   const int nsw = (f.slot_bytes - f.off_scales) / 4;
   uint32_t rk[Q][R], rv[Q][R];
   int row = base + (lane >> 4);
-  fetch_rows16<Q, F16>(key, value, min(row, rows - 1), rk, rv);
+  fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * (lane & 15), rk, rv);
   int64_t sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
   for (;;) {
     float k[Q][4], v[Q][4];
@@ -826,7 +960,7 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
     base += stride;
     row += stride;
     if (base < rows) {  // the next four rows load during this group
-      fetch_rows16<Q, F16>(key, value, min(row, rows - 1), rk, rv);
+      fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * (lane & 15), rk, rv);
       sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
     }
 #pragma unroll
