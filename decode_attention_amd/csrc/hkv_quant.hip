@@ -494,6 +494,48 @@ __device__ __forceinline__ void fwht_stage_fused(float (&x)[Q][4], float sgn) {
   FwhtStageAsm<Q>::template run<CTRL>(x, sgn);
 }
 
+// The same stage over four values, with the partner read through the DPP
+// pattern from x itself (in place) or from a separate register t (for a
+// partner two DPP patterns away: t holds the first, the fused instruction
+// applies the second).
+template <int CTRL>
+__device__ __forceinline__ void fwht_fmac4(float (&x)[4], float sgn);
+template <int CTRL>
+__device__ __forceinline__ void fwht_fmac4_src(float (&x)[4], const float (&t)[4], float sgn);
+
+#define HKV_FMAC4_DEF(CTRL, CTL)                                                                  \
+  template <>                                                                                    \
+  __device__ __forceinline__ void fwht_fmac4<CTRL>(float (&x)[4], float sgn) {                   \
+    asm("s_nop 1\n\t"                                                                             \
+        "v_fmac_f32_dpp %0, %0, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
+        "v_fmac_f32_dpp %1, %1, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
+        "v_fmac_f32_dpp %2, %2, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
+        "v_fmac_f32_dpp %3, %3, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
+        "s_nop 1"                                                                                \
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])                                         \
+        : [s] "v"(sgn));                                                                         \
+  }
+#define HKV_FMAC4_SRC_DEF(CTRL, CTL)                                                              \
+  template <>                                                                                    \
+  __device__ __forceinline__ void fwht_fmac4_src<CTRL>(float (&x)[4], const float (&t)[4],       \
+                                                       float sgn) {                              \
+    asm("s_nop 1\n\t"                                                                             \
+        "v_fmac_f32_dpp %0, %4, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
+        "v_fmac_f32_dpp %1, %5, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
+        "v_fmac_f32_dpp %2, %6, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
+        "v_fmac_f32_dpp %3, %7, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
+        "s_nop 1"                                                                                \
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])                                         \
+        : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), [s] "v"(sgn));                             \
+  }
+
+HKV_FMAC4_DEF(0xB1, "quad_perm:[1,0,3,2]")
+HKV_FMAC4_DEF(0x4E, "quad_perm:[2,3,0,1]")
+HKV_FMAC4_DEF(0x128, "row_ror:8")
+HKV_FMAC4_SRC_DEF(0x1B, "quad_perm:[3,2,1,0]")
+#undef HKV_FMAC4_DEF
+#undef HKV_FMAC4_SRC_DEF
+
 // fwht_rows16 in the lane order of qrow_elem.
 template <int Q>
 __device__ __forceinline__ void fwht_rows16_q(float (&x)[Q][4], int e, float norm) {
@@ -779,14 +821,23 @@ __device__ __forceinline__ void fwht_rows16b(float (&x)[Q][4], int block, float 
           x[q][i] = a + b;
           x[q][i + h] = a - b;
         }
+  // h = 4 .. 32: lane strides 1, 2, 4, 8, one fused DPP multiply-add per
+  // value (see fwht_stage_fused; lane xor 4 is the half-row mirror followed
+  // by the quad reversal); the values end with the lane's sign
+  // (-1)^popcount(l), removed with the normalisation.
 #pragma unroll
-  for (int m = 1; m <= 8; m <<= 1) {
-    const float sgn = (l & m) ? -1.0f : 1.0f;
+  for (int q = 0; q < Q; ++q) fwht_fmac4<0xB1>(x[q], (l & 1) ? -1.0f : 1.0f);
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
+  for (int q = 0; q < Q; ++q) fwht_fmac4<0x4E>(x[q], (l & 2) ? -1.0f : 1.0f);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[q][i] = fmaf(x[q][i], sgn, shfl_xor(x[q][i], m));
+  for (int q = 0; q < Q; ++q) {
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = __uint_as_float(dpp<0x141>(__float_as_uint(x[q][i])));
+    fwht_fmac4_src<0x1B>(x[q], t, (l & 4) ? -1.0f : 1.0f);
   }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) fwht_fmac4<0x128>(x[q], (l & 8) ? -1.0f : 1.0f);
 #pragma unroll
   for (int hq = 1; hq < Q; hq <<= 1) {
     if (64 * hq < block) {
@@ -801,10 +852,11 @@ __device__ __forceinline__ void fwht_rows16b(float (&x)[Q][4], int block, float 
           }
     }
   }
+  const float sn = (__builtin_popcount(l) & 1) ? -norm : norm;
 #pragma unroll
   for (int q = 0; q < Q; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * norm;
+    for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * sn;
 }
 
 // Sum of t over groups [q0, q0 + NQ) of one 16-lane row in the oracle's
