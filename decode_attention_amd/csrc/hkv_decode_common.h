@@ -97,15 +97,6 @@ __device__ __forceinline__ bool wg_item(const DecArgs& a, int& split, int& kvh, 
   return true;
 }
 
-// A kernel-argument pointer held in scalar registers from this point on,
-// still known to the compiler as a global-memory pointer.
-template <class T>
-__device__ __forceinline__ T* pin_global(T* p) {
-  uint64_t v = (uint64_t)(uintptr_t)p;
-  asm("" : "+s"(v));
-  return (T*)(__attribute__((address_space(1))) T*)v;
-}
-
 // Every word of the decode arguments fetched at this point, in one round
 // trip.  Left alone, the compiler loads each argument near its first use,
 // which in a kernel prologue puts several dependent kernel-argument fetches

@@ -38,6 +38,17 @@ struct DevFmt {
   uint32_t sign_bits[kMaxHead / 32];
 };
 
+// A kernel-argument pointer held in scalar registers from this point on,
+// still known to the compiler as a global-memory pointer.  (The empty asm
+// makes the argument word an input at this point, so its fetch is issued
+// with the other arguments pinned here rather than near its first use.)
+template <class T>
+__device__ __forceinline__ T* pin_global(T* p) {
+  uint64_t v = (uint64_t)(uintptr_t)p;
+  asm("" : "+s"(v));
+  return (T*)(__attribute__((address_space(1))) T*)v;
+}
+
 // ---------------------------------------------------------------------------
 // Wave shuffles.
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -350,6 +350,16 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_append_kernel(
     DevFmt f, const void* key, const void* value, int rows, int num_kv_heads,
     const int64_t* slot_mapping, uint8_t* cache) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // The argument words in one fetch (the row count alone would otherwise go
+  // first, ahead of the branch below, and the rest after it); the format's
+  // words are read here once so that later reads of them hit the cache.
+  int page_size = f.page_size;
+  float k_norm = f.k_norm;
+  asm("" : "+s"(rows), "+s"(num_kv_heads), "+s"(page_size), "+s"(k_norm));
+  key = pin_global(key);
+  value = pin_global(value);
+  slot_mapping = pin_global(slot_mapping);
+  cache = pin_global(cache);
   const int stride = (int)gridDim.x * kQuantWaves;
   int row = (int)blockIdx.x * kQuantWaves + wave;
   if (row >= rows) return;
