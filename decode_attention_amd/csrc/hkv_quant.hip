@@ -402,6 +402,88 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_append_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Q4_0 and Q8_0 quantize-append of few rows (a decode step's new tokens): one
+// wave per (row, K or V), so the append runs twice as many waves as rows,
+// each with half of a row's work.  A few hundred waves leave most SIMDs
+// empty, so the time of such an append is the latency of one wave's chain
+// (argument fetch, row load, rotation, codes, stores), which this halves.
+// The K and V halves write disjoint words of the slot: their code segments
+// and their scale words (K scales first, then V, as in q4_row / q8_row).
+constexpr int kHalfMaxRows = 1024;  // above this the one-row-per-wave kernel fills the chip
+
+template <int E, bool F16, int KIND>
+__global__ __launch_bounds__(kQuantWaves * kWave) void quantize_half_kernel(
+    DevFmt f, const void* key, const void* value, int rows, int num_kv_heads,
+    const int64_t* slot_mapping, uint8_t* cache) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  int page_size = f.page_size;
+  float k_norm = f.k_norm;
+  asm("" : "+s"(rows), "+s"(num_kv_heads), "+s"(page_size), "+s"(k_norm));
+  key = pin_global(key);
+  value = pin_global(value);
+  slot_mapping = pin_global(slot_mapping);
+  cache = pin_global(cache);
+  const int item = (int)blockIdx.x * kQuantWaves + wave;  // 2 row + part
+  if (item >= 2 * rows) return;
+  const int row = item >> 1, part = item & 1;
+  const void* src = part ? value : key;
+  uint32_t raw[E];
+  {
+    const int64_t base = (int64_t)row * (E * kWave) + lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      raw[e] = F16 ? (uint32_t)((const uint16_t*)src)[base + kWave * e]
+                   : ((const uint32_t*)src)[base + kWave * e];
+  }
+  const int64_t sm = slot_mapping[row / num_kv_heads];
+  if (sm < 0) return;
+  int64_t page;
+  int off;
+  if ((sm >> 32) == 0) {
+    const uint32_t s32 = (uint32_t)sm;
+    page = s32 / (uint32_t)page_size;
+    off = (int)(s32 % (uint32_t)page_size);
+  } else {
+    page = sm / page_size;
+    off = (int)(sm % page_size);
+  }
+  uint32_t* dst = (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, row % num_kv_heads);
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = F16 ? h2f((uint16_t)raw[e]) : __uint_as_float(raw[e]);
+  fwht_strided<E>(x, part ? f.v_block : f.k_block, part ? f.v_norm : k_norm);
+  uint32_t w[E];
+  uint32_t word = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint32_t c;
+    uint32_t sc;
+    if (KIND == HKV_KIND_Q8_0) {
+      sc = q8_block(x[e], &c);
+      w[e] = or_quad(c << (8 * (lane & 3)));
+    } else {
+      sc = q4_block(x[e], &c);
+      w[e] = pack4_lanes(c);
+    }
+    // scale word e pairs the blocks of register e (lower half first)
+    const auto r = __builtin_amdgcn_permlane32_swap(sc, sc, false, false);
+    word = (lane == e) ? (r[0] | (r[1] << 16)) : word;
+  }
+  uint32_t* seg = dst + (part ? f.off_v / 4 : 0);
+  if (KIND == HKV_KIND_Q8_0) {
+    if ((lane & 3) == 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) seg[(lane >> 2) + 16 * e] = w[e];
+    }
+  } else if ((lane & 7) == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) seg[(lane >> 3) + 8 * e] = w[e];
+  }
+  if (lane < E) dst[f.off_scales / 4 + part * E + lane] = word;
+}
+
+// ---------------------------------------------------------------------------
 // Q4_0 and Q8_0 quantize-append for many rows: 16 lanes per row, four rows
 // per wave.
 // A lane of a 16-lane row holds four consecutive elements 64q + 4e + i
@@ -441,9 +523,11 @@ __device__ __forceinline__ int qrow_elem(int l) {
 // The compiler does not fold a DPP move into v_fmac_f32, so the stage is
 // written out: v_fmac_f32_dpp x, x(partner), sgn reads the partner's x
 // through the DPP lane pattern and adds sgn times it to the lane's own x.
-// Each block opens and closes with two wait states (s_nop 1), the distance
-// a DPP read of a register must keep from a VALU write of it; inside a block
-// no instruction reads a register an earlier one wrote.
+// Each block opens with five wait states (s_nop 4: two are what a DPP read
+// of a register needs after a VALU write of it, five what it needs after a
+// VALU write of EXEC) and closes with two (a DPP read by the code after the
+// block); inside a block no instruction reads a register an earlier one
+// wrote.
 #define HKV_FMAC_DPP(CTL, N) "v_fmac_f32_dpp %" #N ", %" #N ", %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"
 #define HKV_FMAC_DPP4(CTL, A, B, C, D) \
   HKV_FMAC_DPP(CTL, A) HKV_FMAC_DPP(CTL, B) HKV_FMAC_DPP(CTL, C) HKV_FMAC_DPP(CTL, D)
@@ -469,20 +553,20 @@ struct FwhtStageAsm<4> {
 #define HKV_STAGE_DEFS(CTRL, CTL)                                                                \
   template <>                                                                                   \
   __device__ __forceinline__ void FwhtStageAsm<1>::run<CTRL>(float (&x)[1][4], float sgn) {     \
-    asm("s_nop 1\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) "s_nop 1"                                  \
+    asm("s_nop 4\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) "s_nop 1"                                  \
         : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3])                           \
         : [s] "v"(sgn));                                                                        \
   }                                                                                             \
   template <>                                                                                   \
   __device__ __forceinline__ void FwhtStageAsm<2>::run<CTRL>(float (&x)[2][4], float sgn) {     \
-    asm("s_nop 1\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) HKV_FMAC_DPP4(CTL, 4, 5, 6, 7) "s_nop 1"   \
+    asm("s_nop 4\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) HKV_FMAC_DPP4(CTL, 4, 5, 6, 7) "s_nop 1"   \
         : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]),            \
           "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3])                                           \
         : [s] "v"(sgn));                                                                        \
   }                                                                                             \
   template <>                                                                                   \
   __device__ __forceinline__ void FwhtStageAsm<4>::run<CTRL>(float (&x)[4][4], float sgn) {     \
-    asm("s_nop 1\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) HKV_FMAC_DPP4(CTL, 4, 5, 6, 7)              \
+    asm("s_nop 4\n\t" HKV_FMAC_DPP4(CTL, 0, 1, 2, 3) HKV_FMAC_DPP4(CTL, 4, 5, 6, 7)              \
             HKV_FMAC_DPP4(CTL, 8, 9, 10, 11) HKV_FMAC_DPP4(CTL, 12, 13, 14, 15) "s_nop 1"         \
         : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]),            \
           "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3]), "+v"(x[2][0]), "+v"(x[2][1]),            \
@@ -516,7 +600,7 @@ __device__ __forceinline__ void fwht_fmac4_src(float (&x)[4], const float (&t)[4
 #define HKV_FMAC4_DEF(CTRL, CTL)                                                                  \
   template <>                                                                                    \
   __device__ __forceinline__ void fwht_fmac4<CTRL>(float (&x)[4], float sgn) {                   \
-    asm("s_nop 1\n\t"                                                                             \
+    asm("s_nop 4\n\t"                                                                             \
         "v_fmac_f32_dpp %0, %0, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
         "v_fmac_f32_dpp %1, %1, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
         "v_fmac_f32_dpp %2, %2, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
@@ -529,7 +613,7 @@ __device__ __forceinline__ void fwht_fmac4_src(float (&x)[4], const float (&t)[4
   template <>                                                                                    \
   __device__ __forceinline__ void fwht_fmac4_src<CTRL>(float (&x)[4], const float (&t)[4],       \
                                                        float sgn) {                              \
-    asm("s_nop 1\n\t"                                                                             \
+    asm("s_nop 4\n\t"                                                                             \
         "v_fmac_f32_dpp %0, %4, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
         "v_fmac_f32_dpp %1, %5, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
         "v_fmac_f32_dpp %2, %6, %[s] " CTL " row_mask:0xf bank_mask:0xf\n\t"                      \
@@ -1182,6 +1266,26 @@ hipError_t launch_quantize_append(const DevFmt& f, const void* key, const void* 
       default: return hipErrorInvalidValue;
     }
 #undef HKV_O16
+    return hipGetLastError();
+  }
+  if ((q4 || q8) && rows <= kHalfMaxRows) {
+    const int64_t gh = (2 * rows + kQuantWaves - 1) / kQuantWaves;
+    const dim3 gridh((unsigned)gh);
+#define HKV_QHK(E_, K_)                                                                      \
+  (in_f16 ? (quantize_half_kernel<E_, true, K_><<<gridh, block, 0, s>>>(                     \
+                f, key, value, r, num_kv_heads, slot_mapping, cache))                        \
+          : (quantize_half_kernel<E_, false, K_><<<gridh, block, 0, s>>>(                    \
+                f, key, value, r, num_kv_heads, slot_mapping, cache)))
+#define HKV_QH(E_) (q8 ? HKV_QHK(E_, HKV_KIND_Q8_0) : HKV_QHK(E_, HKV_KIND_Q4_0))
+    switch (f.D / kWave) {
+      case 1: HKV_QH(1); break;
+      case 2: HKV_QH(2); break;
+      case 3: HKV_QH(3); break;
+      case 4: HKV_QH(4); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef HKV_QH
+#undef HKV_QHK
     return hipGetLastError();
   }
 #define HKV_QA1(E_, F16_, Q4_)                                                         \
