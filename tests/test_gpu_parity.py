@@ -167,6 +167,41 @@ def test_quantize_many_rows(dtype, D, R, in_dtype, misaligned):
     assert np.all(flat[untouched] == 0xA5)
 
 
+@pytest.mark.parametrize("dtype,D", [("q4_0", 256), ("q4_0", 128), ("q4_0", 64), ("q8_0", 256)])
+@pytest.mark.parametrize("in_dtype", [np.float32, np.float16])
+@pytest.mark.parametrize("T", [3, 512, 513, 1000])
+def test_quantize_row_count_paths(dtype, D, in_dtype, T):
+    """Q4_0 / Q8_0 appends of 6, 1024, 1026 and 2000 (token, head) rows: up to
+    1024 rows each row's K and V halves go to separate waves, above that one
+    wave takes a whole row.  Both give the oracle's bytes, with skipped
+    slots, zero rows and max-abs ties, and write nothing else."""
+    rng = np.random.default_rng(11 * D + T + len(dtype) + (1 if in_dtype == np.float16 else 0))
+    H, P = 2, 16
+    k = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
+    v = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(in_dtype)
+    k[T // 2] = 0
+    v[T - 1, 1] = 0
+    k[0, 1, :32] = -np.abs(k[0, 1, :32]).max()     # max-abs ties inside one block
+    k[0, 1, 3] = -k[0, 1, 3]
+    f = hkv.format_init(dtype, D, 0, P)
+    fo = O.format_init(dtype, D, 0)
+    pages = (T + P - 1) // P + 2
+    sm = rng.permutation(pages * P)[:T].astype(np.int64)
+    sm[T // 3] = -1
+    cache = hkv.new_cache(f, pages, H, DEV)
+    cache.fill_(0xA5)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    got = cache.cpu().numpy()
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    keep = sm >= 0
+    assert np.array_equal(got[sm[keep] // P, :, sm[keep] % P], slots[keep])
+    untouched = np.ones(pages * P, bool)
+    untouched[sm[keep]] = False
+    flat = got.transpose(0, 2, 1, 3).reshape(pages * P, H, -1)
+    assert np.all(flat[untouched] == 0xA5)
+
+
 @pytest.mark.parametrize("dtype,R", [("q4_0", 0), ("q8_0", 0), ("octave_k3v3_compact", 64),
                                      ("octave_k3v4", 128)])
 def test_quantize_many_rows_several_passes(dtype, R):
