@@ -318,14 +318,6 @@ inline int64_t merge_wgs(int num_groups, int nsub, int num_kv_heads, int n_q, in
   return 8 * (int64_t)nsub * n_q * group * ((items + 7) / 8);
 }
 
-// Sign words of the output dims kWave e + lane (e < E) of this lane, zero
-// without a sign pattern; fetched at the start, beside the other loads.
-template <int E>
-__device__ __forceinline__ void merge_signs(const DevFmt& f, int lane, uint32_t (&sw)[E]) {
-#pragma unroll
-  for (int e = 0; e < E; ++e) sw[e] = f.use_signs ? f.sign_bits[2 * e + (lane >> 5)] : 0u;
-}
-
 // The (m, l) pairs and o of C records, splits s0 + st c.
 template <int E, int C>
 struct MergeChunk {
@@ -407,7 +399,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   const size_t sstride = (size_t)Rp * a.pstride;
   const int klen = a.q_to_klen[i];
   uint32_t sw[E];
-  merge_signs<E>(f, lane, sw);
+  lane_sign_words<E>(f, lane, sw);  // with the other loads
   float M = -INFINITY, L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
@@ -455,8 +447,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   float* dst = out + ((int64_t)i * a.num_q_heads + h) * D;
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    dst[kWave * e + lane] =
-        __uint_as_float(__float_as_uint(acc[e]) ^ (((sw[e] >> (lane & 31)) & 1u) << 31));
+    dst[kWave * e + lane] = flip_sign(acc[e], sw[e], lane);
 }
 
 // The same merge with one wave per row (kMergeWaves rows per workgroup), for
@@ -490,7 +481,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_rows_kernel(DevFmt 
   const size_t sstride = (size_t)Rp * a.pstride;
   const int klen = a.q_to_klen[i];
   uint32_t sw[E];
-  merge_signs<E>(f, lane, sw);
+  lane_sign_words<E>(f, lane, sw);  // with the other loads
   float M = -INFINITY, L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
@@ -509,8 +500,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_rows_kernel(DevFmt 
   float* dst = out + ((int64_t)i * a.num_q_heads + h) * D;
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    dst[kWave * e + lane] =
-        __uint_as_float(__float_as_uint(acc[e]) ^ (((sw[e] >> (lane & 31)) & 1u) << 31));
+    dst[kWave * e + lane] = flip_sign(acc[e], sw[e], lane);
 }
 
 int round_rows(int rows) {
@@ -620,7 +610,10 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   // chip with one resident round of workgroups (the MFMA kernel: one
   // 8-wave workgroup per CU; the generic kernel: two 4-wave ones), in whole
   // 64-token steps, capped where the per-split fixed cost (query set-up,
-  // partial record) is well amortised.
+  // partial record) is well amortised.  An MFMA split takes at least 256
+  // tokens, one 32-token unit per wave: shorter splits leave waves idle and
+  // add workgroups and partial records for nothing (an 8K context: 64-token
+  // splits 19.7 us per call, 256-token splits 16.7 us).
   {
     const int64_t units = (int64_t)q.num_groups * num_kv_heads;
     const bool mfma = q.kernel != kKernelGeneric;
@@ -628,7 +621,7 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
     const int64_t target = mfma ? kTargetSplitsWgs / 2 : kTargetSplitsWgs;
     int64_t tps = units > 0 ? ((int64_t)max(max_klen, 1) * units + target - 1) / target : cap;
     tps = (tps + 63) / 64 * 64;
-    q.tokens_per_split = (int)std::min<int64_t>(cap, std::max<int64_t>(64, tps));
+    q.tokens_per_split = (int)std::min<int64_t>(cap, std::max<int64_t>(mfma ? 256 : 64, tps));
   }
   q.num_splits = max_klen > 0 ? (max_klen + q.tokens_per_split - 1) / q.tokens_per_split : 1;
   // Grid sizes in work-items are 32-bit (512-lane workgroups at most).

@@ -105,9 +105,9 @@ __device__ __forceinline__ bool wg_item(const DecArgs& a, int& split, int& kvh, 
 // whose wait does not hold back the vector loads issued after them.)
 __device__ __forceinline__ void pin_args(DecArgs& a) {
   asm("" : "+s"(a.q_f16), "+s"(a.num_q_heads), "+s"(a.num_kv_heads), "+s"(a.group),
-               "+s"(a.n_q), "+s"(a.rows), "+s"(a.rows_pad), "+s"(a.num_queries),
-               "+s"(a.num_groups), "+s"(a.nsub), "+s"(a.max_pages), "+s"(a.tokens_per_split),
-               "+s"(a.num_splits), "+s"(a.pstride));
+      "+s"(a.n_q), "+s"(a.rows), "+s"(a.rows_pad), "+s"(a.num_queries), "+s"(a.num_groups),
+      "+s"(a.nsub), "+s"(a.max_pages), "+s"(a.tokens_per_split), "+s"(a.num_splits),
+      "+s"(a.pstride));
   a.query = pin_global(a.query);
   a.cache = pin_global(a.cache);
   a.block_table = pin_global(a.block_table);
