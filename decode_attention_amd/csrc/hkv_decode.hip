@@ -383,10 +383,9 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   __shared__ float red[kMergeWaves][D + 2];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  int v_block = f.v_block;
+  int v_block = f.v_block, use_signs = f.use_signs;
   float v_norm = f.v_norm;
-  asm("" : "+s"(v_block), "+s"(v_norm));
-  pin_args(a);
+  pin_args(a, v_block, use_signs, v_norm);
   out = pin_global(out);
   int i, h;
   if (!merge_row(a, blockIdx.x, i, h)) return;
@@ -399,7 +398,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(DevFmt f, De
   const size_t sstride = (size_t)Rp * a.pstride;
   const int klen = a.q_to_klen[i];
   uint32_t sw[E];
-  lane_sign_words<E>(f, lane, sw);  // with the other loads
+  lane_sign_words<E>(f, use_signs, lane, sw);  // with the other loads
   float M = -INFINITY, L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
@@ -463,10 +462,9 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_rows_kernel(DevFmt 
   constexpr int D = E * kWave;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  int v_block = f.v_block;
+  int v_block = f.v_block, use_signs = f.use_signs;
   float v_norm = f.v_norm;
-  asm("" : "+s"(v_block), "+s"(v_norm));
-  pin_args(a);
+  pin_args(a, v_block, use_signs, v_norm);
   out = pin_global(out);
   const int64_t rowid = (int64_t)blockIdx.x * kMergeWaves + wave;
   if (rowid >= rows) return;
@@ -481,7 +479,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_rows_kernel(DevFmt 
   const size_t sstride = (size_t)Rp * a.pstride;
   const int klen = a.q_to_klen[i];
   uint32_t sw[E];
-  lane_sign_words<E>(f, lane, sw);  // with the other loads
+  lane_sign_words<E>(f, use_signs, lane, sw);  // with the other loads
   float M = -INFINITY, L = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;

@@ -103,11 +103,13 @@ __device__ __forceinline__ bool wg_item(const DecArgs& a, int& split, int& kvh, 
 // ahead of the first cache load.  (The request map and the key lengths stay
 // plain argument pointers, so that their uniform reads remain scalar loads,
 // whose wait does not hold back the vector loads issued after them.)
-__device__ __forceinline__ void pin_args(DecArgs& a) {
+// Three words of the format (x0, x1, y) join the same fetch: one statement,
+// so that none of them is sunk to its first use, which can be late.
+__device__ __forceinline__ void pin_args(DecArgs& a, int& x0, int& x1, float& y) {
   asm("" : "+s"(a.q_f16), "+s"(a.num_q_heads), "+s"(a.num_kv_heads), "+s"(a.group),
       "+s"(a.n_q), "+s"(a.rows), "+s"(a.rows_pad), "+s"(a.num_queries), "+s"(a.num_groups),
       "+s"(a.nsub), "+s"(a.max_pages), "+s"(a.tokens_per_split), "+s"(a.num_splits),
-      "+s"(a.pstride));
+      "+s"(a.pstride), "+s"(x0), "+s"(x1), "+s"(y));
   a.query = pin_global(a.query);
   a.cache = pin_global(a.cache);
   a.block_table = pin_global(a.block_table);
@@ -142,9 +144,10 @@ __device__ __forceinline__ float query_value(const DecArgs& a, uint32_t w, bool 
 // Sign words of the dims kWave e + lane (e < E) of this lane (word
 // 2 e + lane / 32, bit lane % 32), zero without a sign pattern.
 template <int E>
-__device__ __forceinline__ void lane_sign_words(const DevFmt& f, int lane, uint32_t (&sw)[E]) {
+__device__ __forceinline__ void lane_sign_words(const DevFmt& f, bool use_signs, int lane,
+                                                uint32_t (&sw)[E]) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) sw[e] = f.use_signs ? f.sign_bits[2 * e + (lane >> 5)] : 0u;
+  for (int e = 0; e < E; ++e) sw[e] = use_signs ? f.sign_bits[2 * e + (lane >> 5)] : 0u;
 }
 
 __device__ __forceinline__ float flip_sign(float x, uint32_t w, int lane) {

@@ -218,8 +218,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   static_assert(kMaxSplitTiles <= kQWaves * kWave, "one page id per thread");
   int page_size = f.page_size, k_block = f.k_block;
   float k_norm = f.k_norm;
-  asm("" : "+s"(page_size), "+s"(k_block), "+s"(k_norm));
-  pin_args(a);
+  pin_args(a, page_size, k_block, k_norm);
   int split, kvh, gi;
   if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
@@ -233,7 +232,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 #pragma unroll
   for (int k = 0; k < kQR; ++k) query_row_raw<kE>(a, q0, kvh, wave + kQWaves * k, lane, qw[k]);
   uint32_t sw[kE];
-  lane_sign_words<kE>(f, lane, sw);
+  lane_sign_words<kE>(f, f.use_signs, lane, sw);
   const int kl = group_klen_lane(a, q0, lane);
   const int req = a.q_to_req[q0];
   const int kmax = wave_max_int(kl);
@@ -761,8 +760,7 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
   static_assert(kMaxSplitTiles <= W * kWave, "one page id per thread");
   int page_size = f.page_size, k_block = f.k_block;
   float k_norm = f.k_norm;
-  asm("" : "+s"(page_size), "+s"(k_block), "+s"(k_norm));
-  pin_args(a);
+  pin_args(a, page_size, k_block, k_norm);
   int split, kvh, gi;
   if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
@@ -772,7 +770,7 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
 #pragma unroll
   for (int k = 0; k < kQR; ++k) query_row_raw<kE>(a, q0, kvh, wave + W * k, lane, qw[k]);
   uint32_t sw[kE];
-  lane_sign_words<kE>(f, lane, sw);
+  lane_sign_words<kE>(f, f.use_signs, lane, sw);
   const int kl = group_klen_lane(a, q0, lane);  // n_q <= kR32
   const int req = a.q_to_req[q0];
   const int kmax = wave_max_int(kl);

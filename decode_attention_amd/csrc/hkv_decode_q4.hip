@@ -109,8 +109,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
   const int lane = threadIdx.x & 63;
   int page_size = f.page_size, k_block = f.k_block;
   float k_norm = f.k_norm;
-  asm("" : "+s"(page_size), "+s"(k_block), "+s"(k_norm));
-  pin_args(a);
+  pin_args(a, page_size, k_block, k_norm);
   int split, kvh, gi;
   if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;

@@ -90,8 +90,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
   const int lane = threadIdx.x & 63;
   int page_size = f.page_size, k_block = f.k_block;
   float k_norm = f.k_norm;
-  asm("" : "+s"(page_size), "+s"(k_block), "+s"(k_norm));
-  pin_args(a);
+  pin_args(a, page_size, k_block, k_norm);
   int split, kvh, gi;
   if (!wg_item(a, split, kvh, gi)) return;
   const int q0 = gi * a.n_q;
@@ -104,7 +103,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
   uint32_t qw[4];
   query_row_raw<4>(a, q0, kvh, wave, lane, qw);
   uint32_t sw[4];
-  lane_sign_words<4>(f, lane, sw);
+  lane_sign_words<4>(f, f.use_signs, lane, sw);
   const int kl = group_klen_lane(a, q0, lane);
   const int req = a.q_to_req[q0];
   const int kmax = wave_max_int(kl);
