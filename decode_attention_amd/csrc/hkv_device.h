@@ -49,6 +49,19 @@ __device__ __forceinline__ T* pin_global(T* p) {
   return (T*)(__attribute__((address_space(1))) T*)v;
 }
 
+// 1/x rounded to nearest, as the IEEE division gives it: v_rcp_f32 and one
+// Newton step of two fused multiply-adds.  On gfx950 this equals the IEEE
+// quotient for every float with 2^-100 <= |x| <= 2^100 (checked on the
+// hardware over all such floats); outside that range the division is used.
+__device__ __forceinline__ float recip_rn(float x) {
+  const float ax = fabsf(x);
+  if (ax >= 0x1p-100f && ax <= 0x1p100f) {
+    const float r = __builtin_amdgcn_rcpf(x);
+    return fmaf(fmaf(-x, r, 1.0f), r, r);
+  }
+  return 1.0f / x;
+}
+
 // ---------------------------------------------------------------------------
 // Wave shuffles.
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

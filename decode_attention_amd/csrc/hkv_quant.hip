@@ -113,7 +113,7 @@ __device__ __forceinline__ uint32_t q4_block(float x, uint32_t* code) {
   // an all-zero block keeps the initial +0 of the scan
   const float m = (key >> 1) == 0 ? 0.0f : __uint_as_float((key >> 1) | ((~key) << 31));
   const float d = m / -8.0f;
-  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const float id = (d != 0.0f) ? recip_rn(d) : 0.0f;
   const float u = x * id + 8.5f;
   int c = (int)u;
   c = c > 15 ? 15 : c;
@@ -214,7 +214,7 @@ __device__ __forceinline__ uint32_t q8_block(float x, uint32_t* code) {
     a = max(r[0], r[1]);
   }
   const float d = __uint_as_float(a) / 127.0f;
-  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const float id = (d != 0.0f) ? recip_rn(d) : 0.0f;
   const float t = x * id;
   *code = (uint32_t)(int)roundf(t) & 0xFFu;
   return f2h(d);
@@ -688,7 +688,7 @@ __device__ __forceinline__ void q4_group16(const float (&x)[4], uint32_t* word,
   kmax = max(kmax, dpp<0x141>(kmax));  // half-row mirror: the 8 lanes of the block
   const float m = (kmax >> 1) == 0 ? 0.0f : __uint_as_float((kmax >> 1) | ((~kmax) << 31));
   const float d = m / -8.0f;
-  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const float id = (d != 0.0f) ? recip_rn(d) : 0.0f;
   uint32_t c[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -714,7 +714,7 @@ __device__ __forceinline__ void q8_group16(const float (&x)[4], uint32_t* word,
   a = max(a, dpp<0x4E>(a));   // quad [2,3,0,1]
   a = max(a, dpp<0x141>(a));  // half-row mirror: the 8 lanes of the block
   const float d = __uint_as_float(a) / 127.0f;
-  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const float id = (d != 0.0f) ? recip_rn(d) : 0.0f;
   uint32_t w = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) w |= ((uint32_t)(int)roundf(x[i] * id) & 0xFFu) << (8 * i);
