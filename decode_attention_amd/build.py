@@ -12,7 +12,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhkv.so")
-# Measurement aid for the benchmark (a streaming-read probe), not the library.
+# Measurement aid for the benchmark (a streaming-read probe) and a check of
+# the library's reciprocal, not the library.
 PROBE_LIB = os.path.join(HERE, "libhkv_probe.so")
 ARCH = os.environ.get("HKV_OFFLOAD_ARCH", "gfx950")
 
@@ -33,7 +34,9 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
     probe = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+             "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
              "-o", PROBE_LIB + ".tmp", os.path.join(HERE, "probe", "hkv_probe.hip")]
     if verbose:
         print(" ".join(probe))

@@ -7,8 +7,14 @@
 // loads in flight per iteration (the fastest of the shapes tried: 1024-16384
 // workgroups, 4/8/16 loads, cached or nontemporal), folds the words with xor
 // (so the loads cannot be dropped) and writes one word per thread.
+//
+// It also holds a check of the library's reciprocal (recip_rn in
+// hkv_device.h) against the IEEE quotient over every float, which the
+// quantizers' bit-exactness rests on.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "hkv_device.h"
 
 namespace {
 
@@ -36,6 +42,21 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* src,
   sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// recip_rn(x) against 1.0f / x, bit for bit, for the 2^31 float bit patterns
+// base .. base + 2^31 - 1: out[0] counts the mismatches, out[1..8] hold the
+// first ones found.
+__global__ __launch_bounds__(kThreads) void recip_check_kernel(uint32_t base, uint32_t* out) {
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < 0x80000000u; i += stride) {
+    const uint32_t u = base + i;
+    const float x = __uint_as_float(u);
+    if (__float_as_uint(hkv::recip_rn(x)) != __float_as_uint(1.0f / x)) {
+      const uint32_t k = atomicAdd(&out[0], 1u);
+      if (k < 8) out[1 + k] = u;
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -48,6 +69,15 @@ int hkv_probe_stream_read(const void* src, int64_t bytes, int32_t blocks, uint32
   if (!src || !sink || bytes <= 0 || bytes % 16 || blocks <= 0) return 1;
   stream_read_kernel<<<blocks, kThreads, 0, (hipStream_t)stream>>>((const uint4*)src, bytes / 16,
                                                                    sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Runs the reciprocal check over all 2^32 float bit patterns; out is 9
+// device words, zeroed by the caller (mismatch count, first mismatches).
+int hkv_probe_recip_check(uint32_t* out, void* stream) {
+  if (!out) return 1;
+  for (uint32_t half = 0; half < 2; ++half)
+    recip_check_kernel<<<4096, kThreads, 0, (hipStream_t)stream>>>(half << 31, out);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 }
