@@ -28,7 +28,7 @@
 //    skipped by a branch.  V words, K words and scales pass through a
 //    double-buffered per-wave LDS area.
 //  * Online softmax in the exp2 domain, rescaling only when a row maximum
-//    grows by more than kLazy; the four waves merge in LDS and write one
+//    grows by more than kLazy; the eight waves merge in LDS and write one
 //    partial record per row; the shared merge kernel combines the splits and
 //    rotates the output back.
 #include "hkv_decode_common.h"
