@@ -38,8 +38,8 @@ DIST_BLOCKS = 20    # blocks of 10 decode calls for the median / p10 / p90
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=3)
     p.add_argument("--copies", type=int, default=0,
                    help="cache copies rotated between steps (0: enough to exceed the "
