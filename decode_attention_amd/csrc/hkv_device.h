@@ -62,6 +62,21 @@ __device__ __forceinline__ float recip_rn(float x) {
   return 1.0f / x;
 }
 
+// x / 127 rounded to nearest, as the IEEE division gives it: the product
+// with RN(1/127), its exact remainder and one correction (Markstein's
+// quotient).  On gfx950 this equals the IEEE quotient for every float with
+// 2^-100 <= |x| <= 2^100 (checked on the hardware over all such floats);
+// outside that range the division is used.
+__device__ __forceinline__ float div127_rn(float x) {
+  const float ax = fabsf(x);
+  if (ax >= 0x1p-100f && ax <= 0x1p100f) {
+    constexpr float y = 1.0f / 127.0f;
+    const float q0 = x * y;
+    return fmaf(fmaf(-127.0f, q0, x), y, q0);
+  }
+  return x / 127.0f;
+}
+
 // ---------------------------------------------------------------------------
 // Wave shuffles.
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -213,7 +213,7 @@ __device__ __forceinline__ uint32_t q8_block(float x, uint32_t* code) {
     const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
     a = max(r[0], r[1]);
   }
-  const float d = __uint_as_float(a) / 127.0f;
+  const float d = div127_rn(__uint_as_float(a));
   const float id = (d != 0.0f) ? recip_rn(d) : 0.0f;
   const float t = x * id;
   *code = (uint32_t)(int)roundf(t) & 0xFFu;
@@ -713,7 +713,7 @@ __device__ __forceinline__ void q8_group16(const float (&x)[4], uint32_t* word,
   a = max(a, dpp<0xB1>(a));   // quad [1,0,3,2]
   a = max(a, dpp<0x4E>(a));   // quad [2,3,0,1]
   a = max(a, dpp<0x141>(a));  // half-row mirror: the 8 lanes of the block
-  const float d = __uint_as_float(a) / 127.0f;
+  const float d = div127_rn(__uint_as_float(a));
   const float id = (d != 0.0f) ? recip_rn(d) : 0.0f;
   uint32_t w = 0;
 #pragma unroll
@@ -1003,7 +1003,7 @@ __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float 
   const float ss = tree16<Q, NQ>(t, q0);
   float rms = sqrtf(ss / (float)(NQ * kWave));
   rms = rms < 1e-12f ? 1e-12f : rms;
-  const float ry = 1.0f / rms;
+  const float ry = recip_rn(rms);
   float qv[NQ][4];
   bool tiny = false;
 #pragma unroll

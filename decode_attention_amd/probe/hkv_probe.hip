@@ -8,9 +8,9 @@
 // workgroups, 4/8/16 loads, cached or nontemporal), folds the words with xor
 // (so the loads cannot be dropped) and writes one word per thread.
 //
-// It also holds a check of the library's reciprocal (recip_rn in
-// hkv_device.h) against the IEEE quotient over every float, which the
-// quantizers' bit-exactness rests on.
+// It also holds a check of the library's reciprocal and x / 127 (recip_rn
+// and div127_rn in hkv_device.h) against the IEEE quotients over every
+// float, which the quantizers' bit-exactness rests on.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,9 +42,10 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* src,
   sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
-// recip_rn(x) against 1.0f / x, bit for bit, for the 2^31 float bit patterns
-// base .. base + 2^31 - 1: out[0] counts the mismatches, out[1..8] hold the
-// first ones found.
+// recip_rn(x) against 1.0f / x and div127_rn(x) against x / 127.0f, bit for
+// bit, for the 2^31 float bit patterns base .. base + 2^31 - 1: out[0] and
+// out[9] count the mismatches, out[1..8] and out[10..17] hold the first ones
+// found.
 __global__ __launch_bounds__(kThreads) void recip_check_kernel(uint32_t base, uint32_t* out) {
   const uint32_t stride = gridDim.x * kThreads;
   for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < 0x80000000u; i += stride) {
@@ -53,6 +54,10 @@ __global__ __launch_bounds__(kThreads) void recip_check_kernel(uint32_t base, ui
     if (__float_as_uint(hkv::recip_rn(x)) != __float_as_uint(1.0f / x)) {
       const uint32_t k = atomicAdd(&out[0], 1u);
       if (k < 8) out[1 + k] = u;
+    }
+    if (__float_as_uint(hkv::div127_rn(x)) != __float_as_uint(x / 127.0f)) {
+      const uint32_t k = atomicAdd(&out[9], 1u);
+      if (k < 8) out[10 + k] = u;
     }
   }
 }
@@ -72,8 +77,9 @@ int hkv_probe_stream_read(const void* src, int64_t bytes, int32_t blocks, uint32
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-// Runs the reciprocal check over all 2^32 float bit patterns; out is 9
-// device words, zeroed by the caller (mismatch count, first mismatches).
+// Runs the reciprocal and the x / 127 checks over all 2^32 float bit
+// patterns; out is 18 device words, zeroed by the caller (per check: the
+// mismatch count, then the first mismatches).
 int hkv_probe_recip_check(uint32_t* out, void* stream) {
   if (!out) return 1;
   for (uint32_t half = 0; half < 2; ++half)
