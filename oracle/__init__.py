@@ -59,6 +59,8 @@ def lib():
             L.orc_lut_one.restype = i32
             L.orc_bucket.argtypes = [f32, i32]
             L.orc_bucket.restype = i32
+            L.orc_block_sum.argtypes = [P(f32), i32]
+            L.orc_block_sum.restype = f32
             L.orc_quantize_lut.argtypes = [P(f32), i32, i32, P(ctypes.c_uint8), P(f32)]
             L.orc_q4_0_block.argtypes = [P(f32), P(ctypes.c_uint8), P(ctypes.c_uint16)]
             L.orc_q8_0_block.argtypes = [P(f32), P(ctypes.c_int8), P(ctypes.c_uint16)]
@@ -139,6 +141,13 @@ def lut_one() -> int:
 
 def bucket(y: float, bits: int) -> int:
     return int(lib().orc_bucket(float(np.float32(y)), bits))
+
+
+def block_sum(x: np.ndarray) -> float:
+    """fp32 sum of a block in the quantizer's order (64-value pieces added
+    position by position, then folded in halves)."""
+    x = np.ascontiguousarray(x, np.float32)
+    return float(np.float32(lib().orc_block_sum(_p(x, ctypes.c_float), x.shape[-1])))
 
 
 def quantize_lut(x: np.ndarray, bits: int):

@@ -325,20 +325,18 @@ int32_t orc_bucket(float y, int32_t bits) {
   return code;
 }
 
-/* READING of the unspecified reduction order of a torch sum: pairwise tree.
- * When n = 64*m with m > 1 not a power of two, the m blocks of 64 are first
- * added elementwise from left to right; then, while the count is even, the
- * upper half is added onto the lower half; what is left is added from left
- * to right.  Each product is rounded on its own. */
-static float tree_sum(float* t, int32_t n) {
-  if (n > 64 && n % 64 == 0 && !is_pow2(n / 64)) {
-    for (int32_t i = 0; i < 64; ++i) {
-      float acc = t[i];
-      for (int32_t b = 1; b < n / 64; ++b) acc = acc + t[64 * b + i];
-      t[i] = acc;
-    }
-    n = 64;
-  }
+/* READING of the order of a block sum.  The pages sum the squares and the
+ * products of a quantizer block over its last axis and leave the order of
+ * the additions open.  Read here: the block is cut into pieces of
+ * HADAMARD_BLOCK = 64 values, the unit the format rotates in ([OCT] module
+ * text: every K block, and the V vector of a head size that is not a power
+ * of two, are rotated in 64-value pieces).  The pieces are added position
+ * by position first -- upper half of the pieces onto the lower half while
+ * their count is even, then the remaining pieces from left to right -- and
+ * the 64 partial sums are then folded the same way, upper half onto lower
+ * half, down to one value.  A block shorter than 64 (a power of two) is
+ * folded directly.  Every addition is one fp32 addition; t is overwritten. */
+static float fold_halves(float* t, int32_t n) {
   while (n > 1 && n % 2 == 0) {
     const int32_t h = n / 2;
     for (int32_t i = 0; i < h; ++i) t[i] = t[i] + t[i + h];
@@ -349,25 +347,62 @@ static float tree_sum(float* t, int32_t n) {
   return s;
 }
 
-/* [OCT] _quantize_lut over one block of n values. */
+static float block_sum_inplace(float* t, int32_t n) {
+  const int32_t piece = ORC_HADAMARD_BLOCK;
+  if (n <= piece || n % piece) return fold_halves(t, n);
+  int32_t m = n / piece; /* pieces */
+  while (m > 1 && m % 2 == 0) {
+    const int32_t h = m / 2;
+    for (int32_t i = 0; i < h * piece; ++i) t[i] = t[i] + t[i + h * piece];
+    m = h;
+  }
+  for (int32_t b = 1; b < m; ++b)
+    for (int32_t i = 0; i < piece; ++i) t[i] = t[i] + t[b * piece + i];
+  return fold_halves(t, piece);
+}
+
+float orc_block_sum(const float* v, int32_t n) {
+  float* t = (float*)malloc(sizeof(float) * (size_t)n);
+  memcpy(t, v, sizeof(float) * (size_t)n);
+  const float s = block_sum_inplace(t, n);
+  free(t);
+  return s;
+}
+
+/* [OCT] _quantize_lut over one block of n values: each value takes the
+ * codebook entry nearest to it once the block is measured in units of its
+ * RMS (the codebook is for N(0,1)), and the block's scale is chosen so that
+ * the reconstruction x_hat keeps the dot product x . x_hat equal to |x|^2.
+ * (A least-squares scale would shrink the reconstruction instead.)  The
+ * steps and their fp32 roundings:
+ *   ss    = block sum of x_i * x_i                     (order: orc_block_sum)
+ *   rms   = sqrt(ss / n), at least 1e-12               (floor for zero blocks)
+ *   c_i   = number of codebook midpoints below (x_i / rms) * LUT_MULT[bits]
+ *   dot   = block sum of x_i * LUT[c_i]
+ *   scale = LUT_ONE * (dot > 0 ? ss / max(dot, 1e-30) : 0)
+ * so that x_i ~ LUT[c_i] * scale / LUT_ONE. */
+static float block_rms(float ss, int32_t n) {
+  const float r = sqrtf(ss / (float)n);
+  return r < 1e-12f ? 1e-12f : r;
+}
+
+static float norm_preserving_scale(float ss, float dot) {
+  const float q = dot > 0.0f ? ss / (dot > 1e-30f ? dot : 1e-30f) : 0.0f;
+  return q * (float)ORC_LUT_ONE;
+}
+
 void orc_quantize_lut(const float* x, int32_t n, int32_t bits, uint8_t* codes,
                       float* scale) {
   codebooks_init();
   float* t = (float*)malloc(sizeof(float) * (size_t)n);
   for (int32_t i = 0; i < n; ++i) t[i] = x[i] * x[i];
-  const float ss = tree_sum(t, n);
-  float rms = sqrtf(ss / (float)n);
-  if (rms < 1e-12f) rms = 1e-12f; /* clamp_min(1e-12) */
+  const float ss = block_sum_inplace(t, n);
+  const float rms = block_rms(ss, n);
   const float mult = (float)g_mult[bits];
-  for (int32_t i = 0; i < n; ++i) {
-    const float y = (x[i] / rms) * mult;
-    codes[i] = (uint8_t)orc_bucket(y, bits);
-  }
+  for (int32_t i = 0; i < n; ++i) codes[i] = (uint8_t)orc_bucket((x[i] / rms) * mult, bits);
   for (int32_t i = 0; i < n; ++i) t[i] = x[i] * (float)g_lut[bits][codes[i]];
-  const float dot = tree_sum(t, n);
-  float s = 0.0f;
-  if (dot > 0.0f) s = ss / (dot > 1e-30f ? dot : 1e-30f);
-  *scale = s * (float)ORC_LUT_ONE;
+  const float dot = block_sum_inplace(t, n);
+  *scale = norm_preserving_scale(ss, dot);
   free(t);
 }
 

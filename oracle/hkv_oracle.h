@@ -71,8 +71,9 @@ int orc_format_init(orc_format* f, const char* cache_dtype, int32_t head_size,
 uint16_t orc_f32_to_f16(float x);
 float orc_f16_to_f32(uint16_t h);
 
-/* Orthonormal Walsh-Hadamard transform over consecutive blocks ([OCT]
- * fwht_blocks), in fp32 and in fp64. n must be a multiple of block. */
+/* Blockwise orthonormal Hadamard rotation: every run of `block` values is
+ * transformed on its own ([OCT] fwht_blocks), in fp32 and in fp64.  n must
+ * be a multiple of block. */
 void orc_fwht_f32(float* x, int32_t n, int32_t block);
 void orc_fwht_f64(double* x, int32_t n, int32_t block);
 
@@ -90,6 +91,10 @@ int32_t orc_codebook(int32_t bits, int32_t* lut);
 int32_t orc_lut_one(void);
 /* Code of a normalised value y: the number of codebook midpoints < y. */
 int32_t orc_bucket(float y, int32_t bits);
+
+/* Sum of n fp32 values in the order the quantizer block sums use (READING:
+ * 64-value pieces added position by position, then folded in halves). */
+float orc_block_sum(const float* v, int32_t n);
 
 /* Block quantizers. */
 void orc_quantize_lut(const float* x, int32_t n, int32_t bits, uint8_t* codes,
