@@ -93,17 +93,43 @@ def load_traffic(workload: str):
     return t
 
 
+CPU_WORKERS = 16   # host threads a GPU job may use on the benchmark machines
+
+
+def host_cpus() -> int:
+    """CPUs this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, w, threads: int, scale: float, min_seconds: float = 10.0):
-    """The oracle, as it is, on the host cores: quantize the appended rows and
-    run the fp64 attention for every query, one query per thread."""
+    """The oracle, as it is, on the host cores: quantize the appended rows,
+    then the fp64 attention of every query.  Attention is independent per
+    (query, KV head), so the oracle is called on each such sub-problem (the
+    query's G heads of that KV head over that head's cache), one thread per
+    sub-problem."""
     import oracle as O
     from decode_attention_amd import workloads as W
 
     fo = O.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim)
     S = fo.slot_bytes
+    Hkv, G = cfg.num_kv_heads, cfg.num_q_heads // cfg.num_kv_heads
     # Oracle cache of the whole workload (setup, not timed), built in parallel.
     T = w.key.shape[0]
-    slots = np.zeros((T, cfg.num_kv_heads, S), np.uint8)
+    slots = np.zeros((T, Hkv, S), np.uint8)
     chunks = np.array_split(np.arange(T), max(1, threads))
 
     def qwork(ix):
@@ -113,27 +139,32 @@ def cpu_baseline(cfg, w, threads: int, scale: float, min_seconds: float = 10.0):
     th = [threading.Thread(target=qwork, args=(c,)) for c in chunks]
     [t.start() for t in th]
     [t.join() for t in th]
-    cache = np.zeros((w.num_pages, cfg.num_kv_heads, cfg.page_size, S), np.uint8)
-    cache[w.slot_mapping // cfg.page_size, :, w.slot_mapping % cfg.page_size] = slots
+    # One cache per KV head, (pages, 1, page_size, S).
+    head_cache = []
+    for h in range(Hkv):
+        c = np.zeros((w.num_pages, 1, cfg.page_size, S), np.uint8)
+        c[w.slot_mapping // cfg.page_size, 0, w.slot_mapping % cfg.page_size] = slots[:, h]
+        head_cache.append(c)
     rows = w.append_rows()
     qf = w.query.astype(np.float32)
     kf = w.key[rows].astype(np.float32)
     vf = w.value[rows].astype(np.float32)
-    groups = [np.nonzero(w.q_to_req == b)[0] for b in range(len(w.lengths))]
-    n_threads = min(threads, len(groups))
-    results = [None] * len(groups)
+    subs = [(i, h) for i in range(len(w.q_to_req)) for h in range(Hkv)]
+    n_threads = max(1, min(threads, len(subs)))
+    results = [None] * len(subs)
 
-    def awork(gi):
-        for g in range(gi, len(groups), n_threads):
-            ix = groups[g]
-            results[g] = O.attention(fo, qf[ix], cache, w.block_table, w.q_to_req[ix],
-                                     w.q_to_klen[ix], scale)
+    def awork(k0):
+        for k in range(k0, len(subs), n_threads):
+            i, h = subs[k]
+            results[k] = O.attention(fo, np.ascontiguousarray(qf[i:i + 1, h * G:(h + 1) * G]),
+                                     head_cache[h], w.block_table, w.q_to_req[i:i + 1],
+                                     w.q_to_klen[i:i + 1], scale)
     # One pass = the whole step; passes repeat until min_seconds have elapsed.
     reps = 0
     t0 = time.perf_counter()
     while True:
         O.quantize(fo, kf, vf)
-        th = [threading.Thread(target=awork, args=(i,)) for i in range(n_threads)]
+        th = [threading.Thread(target=awork, args=(k,)) for k in range(n_threads)]
         [t.start() for t in th]
         [t.join() for t in th]
         reps += 1
@@ -143,11 +174,12 @@ def cpu_baseline(cfg, w, threads: int, scale: float, min_seconds: float = 10.0):
     dt = total / reps
     nbytes = W.packed_bytes(w, S)
     return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": n_threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": host_cpus(), "cpu_model": cpu_model(),
             "sample": (f"the full step of the workload, {reps} passes: quantize of {len(rows)} "
                        f"appended token rows and fp64 attention of {len(w.q_to_req)} queries over "
-                       f"{nbytes} packed-KV bytes; {dt:.3f} s per pass, {total:.1f} s wall on "
-                       f"{n_threads} threads (one per sequence)")}
+                       f"{nbytes} packed-KV bytes, as {len(subs)} independent (query, KV head) "
+                       f"calls of the oracle; {dt:.3f} s per pass, {total:.1f} s wall on "
+                       f"{n_threads} threads ({host_cpus()} host CPUs available)")}
 
 
 def stream_read_gbs(torch, dev, nbytes: int = 1 << 30, reps: int = 20) -> float:
@@ -448,7 +480,7 @@ def main():
                                     3),
     }
     if not args.no_cpu_baseline and not args.profile:
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        threads = args.cpu_threads or min(CPU_WORKERS, host_cpus())
         rec["cpu_baseline"] = cpu_baseline(cfg, w, threads, scale)
     print(json.dumps(rec), flush=True)
 

@@ -202,7 +202,7 @@ hkv_status hkv_format_init(hkv_format* f, const char* cache_dtype, int32_t head_
 }
 
 hkv_status hkv_quantize_append(const hkv_format* f, const void* key, const void* value,
-                               hkv_dtype in_dtype, int64_t num_tokens, int32_t num_kv_heads,
+                               int32_t in_dtype, int64_t num_tokens, int32_t num_kv_heads,
                                const int64_t* slot_mapping, uint8_t* cache, void* stream) {
   hkv_status st = check_format(f);
   if (st != HKV_OK) return st;
@@ -243,7 +243,7 @@ hkv_status hkv_dequantize(const hkv_format* f, const uint8_t* cache, int32_t num
   return e == hipSuccess ? HKV_OK : hip_fail(e, "dequantize launch");
 }
 
-hkv_status hkv_hadamard(const void* x, hkv_dtype in_dtype, float* y, int64_t rows, int32_t n,
+hkv_status hkv_hadamard(const void* x, int32_t in_dtype, float* y, int64_t rows, int32_t n,
                         int32_t block, const uint32_t* sign_bits, int32_t inverse,
                         void* stream) {
   if (in_dtype != HKV_F32 && in_dtype != HKV_F16)
@@ -284,7 +284,7 @@ size_t hkv_decode_workspace_bytes(const hkv_format* f, int32_t num_queries, int3
   return p.workspace_bytes;
 }
 
-hkv_status hkv_decode_attention(const hkv_format* f, const void* query, hkv_dtype q_dtype,
+hkv_status hkv_decode_attention(const hkv_format* f, const void* query, int32_t q_dtype,
                                 int32_t num_queries, int32_t num_q_heads, int32_t num_kv_heads,
                                 const uint8_t* cache, const int32_t* block_table,
                                 int32_t max_pages_per_req, const int32_t* q_to_req,

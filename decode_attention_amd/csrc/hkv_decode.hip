@@ -23,6 +23,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 namespace hkv {
 namespace {
@@ -516,13 +517,16 @@ size_t generic_lds_bytes(const DevFmt& f, int R) {
 template <int E, int R>
 hipError_t launch_generic_er(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
   const size_t lds = generic_lds_bytes(f, R);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_generic_kernel<E, R>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // The dynamic-LDS limit of this kernel instance is raised once per process
+  // (thread-safe); the largest size any format needs is set, since the
+  // attribute is per kernel, not per launch.
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [] {
+    attr_err = hipFuncSetAttribute((const void*)decode_generic_kernel<E, R>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (attr_err != hipSuccess) return attr_err;
   decode_generic_kernel<E, R><<<grid, dim3(kWaves * kWave), lds, s>>>(f, a);
   return hipGetLastError();
 }

@@ -65,18 +65,18 @@ def lib():
             i32, i64, vp, P = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER
             L.hkv_format_init.argtypes = [P(HkvFormat), ctypes.c_char_p, i32, i32, i32]
             L.hkv_format_init.restype = ctypes.c_int
-            L.hkv_quantize_append.argtypes = [P(HkvFormat), vp, vp, ctypes.c_int, i64, i32, vp,
+            L.hkv_quantize_append.argtypes = [P(HkvFormat), vp, vp, i32, i64, i32, vp,
                                               vp, vp]
             L.hkv_quantize_append.restype = ctypes.c_int
             L.hkv_dequantize.argtypes = [P(HkvFormat), vp, i32, vp, i64, i32, vp, vp, vp]
             L.hkv_dequantize.restype = ctypes.c_int
             L.hkv_decode_workspace_bytes.argtypes = [P(HkvFormat), i32, i32, i32, i32, i32]
             L.hkv_decode_workspace_bytes.restype = ctypes.c_size_t
-            L.hkv_decode_attention.argtypes = [P(HkvFormat), vp, ctypes.c_int, i32, i32, i32, vp,
+            L.hkv_decode_attention.argtypes = [P(HkvFormat), vp, i32, i32, i32, i32, vp,
                                                vp, i32, vp, vp, i32, i32, ctypes.c_float, vp, vp,
                                                ctypes.c_size_t, vp]
             L.hkv_decode_attention.restype = ctypes.c_int
-            L.hkv_hadamard.argtypes = [vp, ctypes.c_int, vp, i64, i32, i32, vp, i32, vp]
+            L.hkv_hadamard.argtypes = [vp, i32, vp, i64, i32, i32, vp, i32, vp]
             L.hkv_hadamard.restype = ctypes.c_int
             L.hkv_last_error.restype = ctypes.c_char_p
             L.hkv_version.restype = ctypes.c_char_p
@@ -109,17 +109,25 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; need float32 or float16")
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, dims=None):
+def _need(t: torch.Tensor, name: str, dtype=None, dims=None, device: bool = True):
+    """Type, layout, dtype and rank checks; the device check comes last (and
+    can be left to a later _on_device call, so that shape errors are reported
+    the same way for host tensors)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    if device:
+        _on_device(t, name)
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
+
+
+def _on_device(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
 
 
 def format_init(cache_dtype: str, head_size: int, rope_dim: int = 0,
@@ -155,10 +163,14 @@ def quantize_append(fmt: HkvFormat, key: torch.Tensor, value: torch.Tensor,
 def dequantize(fmt: HkvFormat, cache: torch.Tensor, slot_ids: torch.Tensor, rotated: bool = False,
                k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
                stream=None):
-    _need(cache, "cache", dtype=torch.uint8, dims=4)
-    _need(slot_ids, "slot_ids", dtype=torch.int64, dims=1)
+    _need(cache, "cache", dtype=torch.uint8, dims=4, device=False)
+    _need(slot_ids, "slot_ids", dtype=torch.int64, dims=1, device=False)
     H = cache.shape[1]
     T = slot_ids.shape[0]
+    if cache.shape[2] != fmt.page_size or cache.shape[3] != fmt.slot_bytes:
+        raise ValueError("dequantize: cache shape does not match the format")
+    _on_device(cache, "cache")
+    _on_device(slot_ids, "slot_ids")
     shape = (T, H, fmt.head_size)
     if k_out is None:
         k_out = torch.empty(shape, dtype=torch.float32, device=cache.device)
@@ -184,18 +196,37 @@ def decode_attention(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
                      max_klen: int, queries_per_seq: int = 1, sm_scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
-    _need(query, "query", dims=3)
-    _need(cache, "cache", dtype=torch.uint8, dims=4)
-    _need(block_table, "block_table", dtype=torch.int32, dims=2)
-    _need(q_to_req, "q_to_req", dtype=torch.int32, dims=1)
-    _need(q_to_klen, "q_to_klen", dtype=torch.int32, dims=1)
+    _need(query, "query", dims=3, device=False)
+    _need(cache, "cache", dtype=torch.uint8, dims=4, device=False)
+    _need(block_table, "block_table", dtype=torch.int32, dims=2, device=False)
+    _need(q_to_req, "q_to_req", dtype=torch.int32, dims=1, device=False)
+    _need(q_to_klen, "q_to_klen", dtype=torch.int32, dims=1, device=False)
     Q, Hq, D = query.shape
     Hkv = cache.shape[1]
+    if D != fmt.head_size:
+        raise ValueError(f"decode_attention: query head size {D} != format head_size "
+                         f"{fmt.head_size}")
+    if cache.shape[2] != fmt.page_size or cache.shape[3] != fmt.slot_bytes:
+        raise ValueError("decode_attention: cache shape does not match the format "
+                         f"(page_size {fmt.page_size}, slot_bytes {fmt.slot_bytes})")
+    if q_to_req.shape[0] != Q or q_to_klen.shape[0] != Q:
+        raise ValueError(f"decode_attention: q_to_req and q_to_klen need {Q} entries")
+    if out is not None:
+        _need(out, "out", dtype=torch.float32, dims=3, device=False)
+        if tuple(out.shape) != (Q, Hq, D):
+            raise ValueError(f"decode_attention: out must be {(Q, Hq, D)}, "
+                             f"got {tuple(out.shape)}")
+    if workspace is not None:
+        _need(workspace, "workspace", device=False)
+    for t, n in ((query, "query"), (cache, "cache"), (block_table, "block_table"),
+                 (q_to_req, "q_to_req"), (q_to_klen, "q_to_klen"), (out, "out"),
+                 (workspace, "workspace")):
+        if t is not None:
+            _on_device(t, n)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((Q, Hq, D), dtype=torch.float32, device=query.device)
-    _need(out, "out", dtype=torch.float32, dims=3)
     if workspace is None:  # a caller's workspace is size-checked by the library
         need = decode_workspace_bytes(fmt, Q, Hq, Hkv, max_klen, queries_per_seq)
         if need:

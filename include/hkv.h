@@ -45,6 +45,9 @@ typedef enum {
   HKV_ERR_HIP = 4
 } hkv_status;
 
+/* Element types.  Entry points take them as int32_t (an hkv_dtype value), so
+ * that an out-of-range value from a caller is an error the library reports,
+ * not an invalid enum. */
 typedef enum { HKV_F32 = 0, HKV_F16 = 1 } hkv_dtype;
 
 typedef enum { HKV_KIND_Q4_0 = 0, HKV_KIND_OCTAVE = 1, HKV_KIND_Q8_0 = 2 } hkv_kind;
@@ -117,7 +120,7 @@ hkv_status hkv_format_init(hkv_format* f, const char* cache_dtype, int32_t head_
  * The packed bytes are a pure function of the K/V values (deterministic).
  */
 hkv_status hkv_quantize_append(const hkv_format* f /*host*/, const void* key,
-                               const void* value, hkv_dtype in_dtype,
+                               const void* value, int32_t in_dtype,
                                int64_t num_tokens, int32_t num_kv_heads,
                                const int64_t* slot_mapping, uint8_t* cache,
                                void* stream);
@@ -167,7 +170,7 @@ size_t hkv_decode_workspace_bytes(const hkv_format* f /*host*/, int32_t num_quer
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  */
 hkv_status hkv_decode_attention(const hkv_format* f /*host*/, const void* query,
-                                hkv_dtype q_dtype, int32_t num_queries,
+                                int32_t q_dtype, int32_t num_queries,
                                 int32_t num_q_heads, int32_t num_kv_heads,
                                 const uint8_t* cache, const int32_t* block_table,
                                 int32_t max_pages_per_req, const int32_t* q_to_req,
@@ -194,7 +197,7 @@ hkv_status hkv_decode_attention(const hkv_format* f /*host*/, const void* query,
  * cache rotation uses, so the values are bitwise those of the formats'
  * rotation.  The transform is its own inverse up to rounding.
  */
-hkv_status hkv_hadamard(const void* x, hkv_dtype in_dtype, float* y, int64_t rows, int32_t n,
+hkv_status hkv_hadamard(const void* x, int32_t in_dtype, float* y, int64_t rows, int32_t n,
                         int32_t block, const uint32_t* sign_bits, int32_t inverse,
                         void* stream);
 

@@ -169,3 +169,49 @@ def test_decode_plan_workspace(dtype, D, R, Q, Hq, Hkv, klen, qps, rows_pad, spl
     f = _fmt(dtype, D, R, 16)
     want = 4 * (4 + D) * rows_pad * splits * groups * Hkv
     assert hkv.decode_workspace_bytes(f, Q, Hq, Hkv, klen, qps) == want
+
+
+def _decode_args(**over):
+    """Well-shaped host tensors for config-2-like decode arguments."""
+    import torch
+    f = hkv.format_init("q4_0", 256, 0, 16)
+    a = dict(fmt=f, query=torch.zeros((2, 16, 256)), cache=torch.zeros((8, 2, 16, 288),
+             dtype=torch.uint8), block_table=torch.zeros((2, 4), dtype=torch.int32),
+             q_to_req=torch.zeros(2, dtype=torch.int32), q_to_klen=torch.zeros(2, dtype=torch.int32),
+             max_klen=64)
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("bad,match", [
+    ({"query": "q128"}, "head size"),
+    ({"cache": "page8"}, "cache shape"),
+    ({"cache": "slot"}, "cache shape"),
+    ({"q_to_req": "short"}, "entries"),
+    ({"q_to_klen": "short"}, "entries"),
+    ({"out": "shape"}, "out must be"),
+])
+def test_decode_binding_rejects_mismatched_shapes(bad, match):
+    import torch
+    make = {"q128": lambda: torch.zeros((2, 16, 128)),
+            "page8": lambda: torch.zeros((8, 2, 8, 288), dtype=torch.uint8),
+            "slot": lambda: torch.zeros((8, 2, 16, 272), dtype=torch.uint8),
+            "short": lambda: torch.zeros(1, dtype=torch.int32),
+            "shape": lambda: torch.zeros((2, 16, 128))}
+    (k, v), = bad.items()
+    a = _decode_args(**{k: make[v]()})
+    with pytest.raises(ValueError, match=match):
+        hkv.decode_attention(**a)
+
+
+def test_decode_binding_needs_device_tensors():
+    with pytest.raises(ValueError, match="device tensor"):
+        hkv.decode_attention(**_decode_args())
+
+
+def test_dequantize_binding_rejects_mismatched_cache():
+    import torch
+    f = hkv.format_init("q4_0", 256, 0, 16)
+    with pytest.raises(ValueError, match="does not match the format"):
+        hkv.dequantize(f, torch.zeros((8, 2, 16, 272), dtype=torch.uint8),
+                       torch.zeros(4, dtype=torch.int64))
