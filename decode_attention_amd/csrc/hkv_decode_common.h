@@ -181,4 +181,61 @@ inline int64_t decode_wgs(int num_groups, int nsub, int num_kv_heads, int num_sp
 // Partial record of one (query row, split): m, l, two pad words, o[D].
 constexpr int kPartialHead = 4;
 
+// The (m, l) pairs and o of C records, splits s0 + st c.
+template <int E, int C>
+struct MergeChunk {
+  float2 ml[C];
+  float o[C][E];
+};
+
+// Requests the records of one chunk; splits at or past `lim` (at most
+// num_splits) load split 0's record instead, which is never counted for them.
+template <int E, int C>
+__device__ __forceinline__ void merge_load(MergeChunk<E, C>& k, const float* base, size_t sstride,
+                                           int s0, int st, int lim, int lane) {
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int s = s0 + st * c;
+    const float* ps = base + (s < lim ? s : 0) * sstride;
+    k.ml[c] = *(const float2*)ps;
+#pragma unroll
+    for (int e = 0; e < E; ++e) k.o[c][e] = ps[kPartialHead + kWave * e + lane];
+  }
+}
+
+// Folds a chunk into the running (M, L, acc) in the exp2 domain.  Records
+// at or past `n_live` (or with m = -inf) are skipped by select, never
+// multiplied, so whatever such a record holds cannot reach the sums.
+template <int E, int C>
+__device__ __forceinline__ void merge_fold(const MergeChunk<E, C>& k, int s0, int st, int n_live,
+                                           float& M, float& L, float (&acc)[E]) {
+  bool live[C];
+  float Mc = M;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    live[c] = s0 + st * c < n_live && k.ml[c].x != -INFINITY;
+    if (live[c]) Mc = fmaxf(Mc, k.ml[c].x);
+  }
+  // no live record yet: M = Mc = -inf and acc, L are still 0
+  const float alpha = Mc == -INFINITY ? 1.0f : exp2f(M - Mc);
+  L *= alpha;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const float w = live[c] ? exp2f(k.ml[c].x - Mc) : 0.0f;
+    L = live[c] ? fmaf(k.ml[c].y, w, L) : L;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = live[c] ? fmaf(k.o[c][e], w, acc[e]) : acc[e];
+  }
+  M = Mc;
+}
+
+// Splits holding tokens of a row of key length klen: each of them holds at
+// least one, so its whole record was written and is finite.
+__device__ __forceinline__ int merge_live(const DecArgs& a, int klen) {
+  return klen <= 0 ? 0 : min(a.num_splits, (klen + a.tokens_per_split - 1) / a.tokens_per_split);
+}
+
+
 }  // namespace hkv

@@ -196,6 +196,7 @@ def decode_attention(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
                      max_klen: int, queries_per_seq: int = 1, sm_scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
+    """Decode attention; see include/hkv.h (one call at a time per workspace)."""
     _need(query, "query", dims=3, device=False)
     _need(cache, "cache", dtype=torch.uint8, dims=4, device=False)
     _need(block_table, "block_table", dtype=torch.int32, dims=2, device=False)

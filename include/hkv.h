@@ -142,6 +142,8 @@ hkv_status hkv_dequantize(const hkv_format* f /*host*/, const uint8_t* cache,
  * hkv_decode_workspace_bytes -- bytes of device workspace hkv_decode_attention
  * needs for these sizes (0 on invalid arguments).  max_klen is a host upper
  * bound of q_to_klen.
+ * The workspace holds the split partial results; its contents need no
+ * initialisation.  Calls that overlap in time must not share a workspace.
  */
 size_t hkv_decode_workspace_bytes(const hkv_format* f /*host*/, int32_t num_queries,
                                   int32_t num_q_heads, int32_t num_kv_heads,
