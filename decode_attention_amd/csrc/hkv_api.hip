@@ -284,6 +284,55 @@ size_t hkv_decode_workspace_bytes(const hkv_format* f, int32_t num_queries, int3
   return p.workspace_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both decode entry points; on success *d and *p hold the
+// device format and the launch plan.  *done is set when there is nothing to
+// launch (no queries).
+hkv_status decode_check(const char* who, const hkv_format* f, const void* query, int32_t q_dtype,
+                        int32_t num_queries, int32_t num_q_heads, int32_t num_kv_heads,
+                        const uint8_t* cache, const int32_t* block_table,
+                        int32_t max_pages_per_req, const int32_t* q_to_req,
+                        const int32_t* q_to_klen, int32_t max_klen, int32_t queries_per_seq,
+                        float sm_scale, const float* out, hkv::DevFmt* d, hkv::DecodePlan* p,
+                        bool* done) {
+  *done = false;
+  hkv_status st = check_format(f);
+  if (st != HKV_OK) return st;
+  if (num_queries < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(HKV_ERR_INVALID_ARG,
+                "%s: need num_q_heads a positive multiple of num_kv_heads (%d, %d), "
+                "num_queries >= 0 (%d)", who, num_q_heads, num_kv_heads, num_queries);
+  if (queries_per_seq < 1 || queries_per_seq > 16 || num_queries % queries_per_seq)
+    return fail(HKV_ERR_INVALID_ARG,
+                "%s: queries_per_seq must be in [1, 16] and divide num_queries (%d, %d)", who,
+                queries_per_seq, num_queries);
+  if (q_dtype != HKV_F32 && q_dtype != HKV_F16)
+    return fail(HKV_ERR_INVALID_ARG, "%s: bad query dtype %d", who, (int)q_dtype);
+  if (max_klen < 0) return fail(HKV_ERR_INVALID_ARG, "%s: max_klen < 0", who);
+  if (!std::isfinite(sm_scale)) return fail(HKV_ERR_INVALID_ARG, "%s: sm_scale not finite", who);
+  if (num_queries == 0) {
+    *done = true;
+    return HKV_OK;
+  }
+  if (!query || !cache || !block_table || !q_to_req || !q_to_klen || !out)
+    return fail(HKV_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (max_pages_per_req <= 0) return fail(HKV_ERR_INVALID_ARG, "%s: max_pages_per_req <= 0", who);
+  if (!aligned(cache, 16)) return fail(HKV_ERR_INVALID_ARG, "cache must be 16-byte aligned");
+  *d = hkv::to_dev(*f);
+  if (!hkv::plan_decode(*d, num_queries, num_q_heads, num_kv_heads, max_klen, queries_per_seq, p))
+    return fail(HKV_ERR_UNSUPPORTED,
+                "%s: unsupported shape (query rows per KV head = %d x %d must be <= 32)", who,
+                num_q_heads / num_kv_heads, queries_per_seq);
+  return HKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 hkv_status hkv_decode_attention(const hkv_format* f, const void* query, int32_t q_dtype,
                                 int32_t num_queries, int32_t num_q_heads, int32_t num_kv_heads,
                                 const uint8_t* cache, const int32_t* block_table,
@@ -291,31 +340,14 @@ hkv_status hkv_decode_attention(const hkv_format* f, const void* query, int32_t 
                                 const int32_t* q_to_klen, int32_t max_klen,
                                 int32_t queries_per_seq, float sm_scale, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  hkv_status st = check_format(f);
-  if (st != HKV_OK) return st;
-  if (num_queries < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
-    return fail(HKV_ERR_INVALID_ARG,
-                "decode: need num_q_heads a positive multiple of num_kv_heads (%d, %d), "
-                "num_queries >= 0 (%d)", num_q_heads, num_kv_heads, num_queries);
-  if (queries_per_seq < 1 || queries_per_seq > 16 || num_queries % queries_per_seq)
-    return fail(HKV_ERR_INVALID_ARG,
-                "decode: queries_per_seq must be in [1, 16] and divide num_queries (%d, %d)",
-                queries_per_seq, num_queries);
-  if (q_dtype != HKV_F32 && q_dtype != HKV_F16)
-    return fail(HKV_ERR_INVALID_ARG, "decode: bad query dtype %d", (int)q_dtype);
-  if (max_klen < 0) return fail(HKV_ERR_INVALID_ARG, "decode: max_klen < 0");
-  if (!std::isfinite(sm_scale)) return fail(HKV_ERR_INVALID_ARG, "decode: sm_scale not finite");
-  if (num_queries == 0) return HKV_OK;
-  if (!query || !cache || !block_table || !q_to_req || !q_to_klen || !out)
-    return fail(HKV_ERR_INVALID_ARG, "decode: NULL pointer");
-  if (max_pages_per_req <= 0) return fail(HKV_ERR_INVALID_ARG, "decode: max_pages_per_req <= 0");
-  if (!aligned(cache, 16)) return fail(HKV_ERR_INVALID_ARG, "cache must be 16-byte aligned");
-  const hkv::DevFmt d = hkv::to_dev(*f);
+  hkv::DevFmt d;
   hkv::DecodePlan p;
-  if (!hkv::plan_decode(d, num_queries, num_q_heads, num_kv_heads, max_klen, queries_per_seq, &p))
-    return fail(HKV_ERR_UNSUPPORTED,
-                "decode: unsupported shape (query rows per KV head = %d x %d must be <= 32)",
-                num_q_heads / num_kv_heads, queries_per_seq);
+  bool done;
+  const hkv_status st =
+      decode_check("decode", f, query, q_dtype, num_queries, num_q_heads, num_kv_heads, cache,
+                   block_table, max_pages_per_req, q_to_req, q_to_klen, max_klen,
+                   queries_per_seq, sm_scale, out, &d, &p, &done);
+  if (st != HKV_OK || done) return st;
   if (workspace_bytes < p.workspace_bytes || (p.workspace_bytes && !workspace))
     return fail(HKV_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
                 p.workspace_bytes, workspace_bytes);
@@ -326,6 +358,35 @@ hkv_status hkv_decode_attention(const hkv_format* f, const void* query, int32_t 
                                           q_to_req, q_to_klen, sm_scale, out, workspace,
                                           (hipStream_t)stream);
   return e == hipSuccess ? HKV_OK : hip_fail(e, "decode launch");
+}
+
+hkv_status hkv_decode_attention_noalloc(const hkv_format* f, const void* query, int32_t q_dtype,
+                                        int32_t num_queries, int32_t num_q_heads,
+                                        int32_t num_kv_heads, const uint8_t* cache,
+                                        const int32_t* block_table, int32_t max_pages_per_req,
+                                        const int32_t* q_to_req, const int32_t* q_to_klen,
+                                        int32_t max_klen, int32_t queries_per_seq,
+                                        float sm_scale, float* out, void* stream) {
+  hkv::DevFmt d;
+  hkv::DecodePlan p;
+  bool done;
+  const hkv_status st =
+      decode_check("decode_noalloc", f, query, q_dtype, num_queries, num_q_heads, num_kv_heads,
+                   cache, block_table, max_pages_per_req, q_to_req, q_to_klen, max_klen,
+                   queries_per_seq, sm_scale, out, &d, &p, &done);
+  if (st != HKV_OK || done) return st;
+  if (p.workspace_bytes > HKV_DECODE_SCRATCH_BYTES)
+    return fail(HKV_ERR_WORKSPACE,
+                "decode_noalloc: these sizes need %zu bytes of scratch, the library's static "
+                "scratch holds %zu; call hkv_decode_attention with a workspace instead",
+                p.workspace_bytes, (size_t)HKV_DECODE_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  hipError_t e = hkv::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "decode_noalloc: scratch address");
+  e = hkv::launch_decode(d, p, query, q_dtype == HKV_F16, num_q_heads, num_kv_heads, cache,
+                         block_table, max_pages_per_req, q_to_req, q_to_klen, sm_scale, out,
+                         scratch, (hipStream_t)stream);
+  return e == hipSuccess ? HKV_OK : hip_fail(e, "decode_noalloc launch");
 }
 
 }  // extern "C"

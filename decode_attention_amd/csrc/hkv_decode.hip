@@ -654,4 +654,31 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   return hipGetLastError();
 }
 
+// Scratch of hkv_decode_attention_noalloc: the split partial records of one
+// call, in place of a caller's workspace.  Every device the library runs on
+// holds its own copy until the process ends.  In host code the name stands
+// for a host-side handle, not a device address: host code uses only the
+// address decode_scratch() obtains from the runtime.
+__device__ __align__(256) uint8_t scratch[HKV_DECODE_SCRATCH_BYTES];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace hkv

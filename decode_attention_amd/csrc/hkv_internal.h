@@ -49,4 +49,8 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
                          const int32_t* q_to_req, const int32_t* q_to_klen, float sm_scale,
                          float* out, void* workspace, hipStream_t s);
 
+// Device address of the static decode scratch (HKV_DECODE_SCRATCH_BYTES) on
+// the current device, looked up once per device.
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace hkv

@@ -21,10 +21,12 @@ HKV_OK, HKV_ERR_INVALID_ARG, HKV_ERR_UNSUPPORTED, HKV_ERR_WORKSPACE, HKV_ERR_HIP
 HKV_F32, HKV_F16 = 0, 1
 HKV_KIND_Q4_0, HKV_KIND_OCTAVE, HKV_KIND_Q8_0 = 0, 1, 2
 HKV_MAX_HEAD = 256
+DECODE_SCRATCH_BYTES = 64 << 20  # HKV_DECODE_SCRATCH_BYTES
 
 # Names of the exported entry points (include/hkv.h).
 EXPORTS = ("hkv_format_init", "hkv_quantize_append", "hkv_dequantize",
-           "hkv_decode_workspace_bytes", "hkv_decode_attention", "hkv_hadamard",
+           "hkv_decode_workspace_bytes", "hkv_decode_attention",
+           "hkv_decode_attention_noalloc", "hkv_hadamard",
            "hkv_last_error", "hkv_version")
 
 
@@ -76,6 +78,10 @@ def lib():
                                                vp, i32, vp, vp, i32, i32, ctypes.c_float, vp, vp,
                                                ctypes.c_size_t, vp]
             L.hkv_decode_attention.restype = ctypes.c_int
+            L.hkv_decode_attention_noalloc.argtypes = [P(HkvFormat), vp, i32, i32, i32, i32,
+                                                       vp, vp, i32, vp, vp, i32, i32,
+                                                       ctypes.c_float, vp, vp]
+            L.hkv_decode_attention_noalloc.restype = ctypes.c_int
             L.hkv_hadamard.argtypes = [vp, i32, vp, i64, i32, i32, vp, i32, vp]
             L.hkv_hadamard.restype = ctypes.c_int
             L.hkv_last_error.restype = ctypes.c_char_p
@@ -238,6 +244,39 @@ def decode_attention(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
         _ptr(block_table), block_table.shape[1], _ptr(q_to_req), _ptr(q_to_klen), int(max_klen),
         int(queries_per_seq), float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return out
+
+
+def decode_attention_noalloc(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
+                             block_table: torch.Tensor, q_to_req: torch.Tensor,
+                             q_to_klen: torch.Tensor, max_klen: int, queries_per_seq: int,
+                             sm_scale: float, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Decode attention into a caller's `out` with the library's static scratch
+    in place of a workspace; allocates nothing (include/hkv.h).  Calls that
+    overlap in time on one device race on the scratch."""
+    _need(query, "query", dims=3, device=False)
+    _need(cache, "cache", dtype=torch.uint8, dims=4, device=False)
+    _need(block_table, "block_table", dtype=torch.int32, dims=2, device=False)
+    _need(q_to_req, "q_to_req", dtype=torch.int32, dims=1, device=False)
+    _need(q_to_klen, "q_to_klen", dtype=torch.int32, dims=1, device=False)
+    _need(out, "out", dtype=torch.float32, dims=3, device=False)
+    Q, Hq, D = query.shape
+    if D != fmt.head_size:
+        raise ValueError(f"decode_attention_noalloc: query head size {D} != format head_size "
+                         f"{fmt.head_size}")
+    if cache.shape[2] != fmt.page_size or cache.shape[3] != fmt.slot_bytes:
+        raise ValueError("decode_attention_noalloc: cache shape does not match the format")
+    if q_to_req.shape[0] != Q or q_to_klen.shape[0] != Q:
+        raise ValueError(f"decode_attention_noalloc: q_to_req and q_to_klen need {Q} entries")
+    if tuple(out.shape) != (Q, Hq, D):
+        raise ValueError(f"decode_attention_noalloc: out must be {(Q, Hq, D)}")
+    for t, n in ((query, "query"), (cache, "cache"), (block_table, "block_table"),
+                 (q_to_req, "q_to_req"), (q_to_klen, "q_to_klen"), (out, "out")):
+        _on_device(t, n)
+    _check(lib().hkv_decode_attention_noalloc(
+        ctypes.byref(fmt), _ptr(query), _dtype_code(query), Q, Hq, cache.shape[1], _ptr(cache),
+        _ptr(block_table), block_table.shape[1], _ptr(q_to_req), _ptr(q_to_klen), int(max_klen),
+        int(queries_per_seq), float(sm_scale), _ptr(out), _stream(stream)))
     return out
 
 

@@ -14,7 +14,8 @@
  * Conventions common to every entry point
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and
  *     allocates every buffer, including the decode workspace; the library
- *     allocates no memory and keeps no state besides its code.
+ *     allocates no memory and keeps no state besides its code and the
+ *     static scratch of hkv_decode_attention_noalloc.
  *   - Every call is asynchronous on `stream` (a hipStream_t, passed as void*;
  *     NULL is the legacy default stream); nothing synchronizes the host.
  *   - Arguments the host can check (format, sizes, null pointers, alignment,
@@ -179,6 +180,36 @@ hkv_status hkv_decode_attention(const hkv_format* f /*host*/, const void* query,
                                 const int32_t* q_to_klen, int32_t max_klen,
                                 int32_t queries_per_seq, float sm_scale, float* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the static per-device scratch of hkv_decode_attention_noalloc. */
+#define HKV_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * hkv_decode_attention_noalloc -- hkv_decode_attention for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * kernels as hkv_decode_attention, without the workspace: the split partial
+ * records go to a scratch array of HKV_DECODE_SCRATCH_BYTES (64 MiB) that the
+ * library holds on each device it runs on, from the first call on that
+ * device until the process ends.  The call itself allocates nothing.
+ *   - The device is the current device; stream must belong to it.
+ *   - Sizes whose hkv_decode_workspace_bytes exceeds
+ *     HKV_DECODE_SCRATCH_BYTES return HKV_ERR_WORKSPACE and enqueue nothing
+ *     (e.g. 64 sequences x 4 query tokens x 32 query heads over 4 KV heads at
+ *     32K tokens needs 65 MiB: use hkv_decode_attention there).
+ *   - All calls on one device share its scratch, and the scratch keeps the
+ *     last call's contents (no call needs it zeroed).  Calls that may overlap
+ *     in time on one device -- on different streams, or from different host
+ *     threads without ordering -- race on it; order them on one stream.
+ */
+hkv_status hkv_decode_attention_noalloc(const hkv_format* f /*host*/, const void* query,
+                                        int32_t q_dtype, int32_t num_queries,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        const uint8_t* cache, const int32_t* block_table,
+                                        int32_t max_pages_per_req, const int32_t* q_to_req,
+                                        const int32_t* q_to_klen, int32_t max_klen,
+                                        int32_t queries_per_seq, float sm_scale, float* out,
+                                        void* stream);
 
 /*
  * hkv_hadamard -- blockwise orthonormal Walsh-Hadamard rotation of rows, the

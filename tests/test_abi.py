@@ -135,6 +135,34 @@ def test_decode_host_errors_and_workspace():
     assert call(Hq=64, Hkv=1) == hkv.HKV_ERR_UNSUPPORTED      # 64 rows per KV head
 
 
+def test_decode_noalloc_host_errors():
+    """The no-allocation decode checks what hkv_decode_attention checks and
+    refuses sizes whose partial records exceed the static scratch, before it
+    touches a device."""
+    L = hkv.lib()
+    f = _fmt("octave_k3v3_compact", 256, 64, 16)
+
+    def call(**kw):
+        return L.hkv_decode_attention_noalloc(
+            ctypes.byref(kw.get("f", f)), kw.get("q", FAKE), 1, kw.get("Q", 256),
+            kw.get("Hq", 32), kw.get("Hkv", 4), kw.get("cache", FAKE), FAKE, 2048, FAKE, FAKE,
+            kw.get("mk", 32768), kw.get("nq", 4), 0.0625, kw.get("out", FAKE), None)
+    need = hkv.decode_workspace_bytes(f, 256, 32, 4, 32768, 4)
+    assert need > hkv.DECODE_SCRATCH_BYTES                  # 65 MiB of partial records
+    assert call() == hkv.HKV_ERR_WORKSPACE
+    assert b"hkv_decode_attention with a workspace" in L.hkv_last_error()
+    assert call(Q=0) == hkv.HKV_OK
+    assert call(nq=3) == hkv.HKV_ERR_INVALID_ARG
+    assert call(q=None) == hkv.HKV_ERR_INVALID_ARG
+    assert call(out=None) == hkv.HKV_ERR_INVALID_ARG
+    assert call(mk=-1) == hkv.HKV_ERR_INVALID_ARG
+    assert call(cache=FAKE + 2) == hkv.HKV_ERR_INVALID_ARG
+    assert call(Hq=256, Hkv=1, Q=4, nq=1) == hkv.HKV_ERR_UNSUPPORTED
+    assert "HKV_DECODE_SCRATCH_BYTES ((size_t)64 << 20)" in open(
+        os.path.join(ROOT, "include", "hkv.h")).read()
+    assert hkv.DECODE_SCRATCH_BYTES == 64 << 20
+
+
 def test_hadamard_host_errors():
     L = hkv.lib()
     h = lambda **kw: L.hkv_hadamard(kw.get("x", FAKE), kw.get("dt", 0), kw.get("y", FAKE + (1 << 24)),

@@ -1,0 +1,88 @@
+"""hkv_decode_attention_noalloc (the decode entry point for callers that
+cannot allocate: it keeps the split partial records in the library's static
+per-device scratch) gives what hkv_decode_attention gives with a caller's
+workspace, on two calls in a row, the second smaller than the first, so that
+the second runs over the first call's leftover scratch contents.  Both are
+also checked against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_amd import hkv
+from decode_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ATOL, RTOL = 2e-3, 1e-3
+
+
+def _setup(ci, sizes):
+    cfg = W.CONFIGS[ci]
+    w = W.make_workload(cfg, **sizes)
+    f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
+    cache = hkv.new_cache(f, w.num_pages, cfg.num_kv_heads, DEV)
+    hkv.quantize_append(f, torch.from_numpy(w.key).to(DEV), torch.from_numpy(w.value).to(DEV),
+                        torch.from_numpy(w.slot_mapping).to(DEV), cache)
+    t = dict(query=torch.from_numpy(w.query).to(DEV),
+             bt=torch.from_numpy(w.block_table).to(DEV),
+             q2r=torch.from_numpy(w.q_to_req).to(DEV),
+             q2k=torch.from_numpy(w.q_to_klen).to(DEV))
+    return cfg, w, f, cache, t
+
+
+def _within(got, ref, what):
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    assert not bad.any(), f"{what}: {bad.sum()} values off, max abs err {err.max():.3e}"
+
+
+@pytest.mark.parametrize("ci,first,second", [
+    (2, dict(batch=3, seq_len=8192), dict(batch=1, seq_len=1537)),
+    (9, dict(batch=2, seq_len=5000), dict(batch=1, seq_len=777)),
+    (4, dict(batch=4, seq_len=4000, min_len=1000), dict(batch=2, seq_len=700, min_len=300)),
+    (5, dict(batch=6, seq_len=3000, min_len=200), dict(batch=2, seq_len=900, min_len=100)),
+])
+def test_noalloc_matches_workspace_entry_point(ci, first, second):
+    for sizes in (first, second):
+        print(f"noalloc decode: config {ci} {sizes}", flush=True)
+        cfg, w, f, cache, t = _setup(ci, sizes)
+        Q, Hq, D = w.query.shape
+        scale = W.default_sm_scale(cfg.head_size)
+        need = hkv.decode_workspace_bytes(f, Q, Hq, cfg.num_kv_heads, w.max_klen, cfg.n_q)
+        assert 0 < need <= hkv.DECODE_SCRATCH_BYTES
+        out_na = torch.full((Q, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+        hkv.decode_attention_noalloc(f, t["query"], cache, t["bt"], t["q2r"], t["q2k"],
+                                     w.max_klen, cfg.n_q, scale, out_na)
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        out_ws = hkv.decode_attention(f, t["query"], cache, t["bt"], t["q2r"], t["q2k"],
+                                      w.max_klen, cfg.n_q, scale, workspace=ws)
+        torch.cuda.synchronize()
+        got = out_na.cpu().numpy().astype(np.float64)
+        _within(got, out_ws.cpu().numpy().astype(np.float64), "noalloc vs workspace")
+        fo = O.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim)
+        ref = O.attention(fo, w.query, cache.cpu().numpy(), w.block_table, w.q_to_req,
+                          w.q_to_klen, scale)
+        _within(got, ref, "noalloc vs oracle")
+
+
+def test_noalloc_refuses_oversize_scratch():
+    """Sizes beyond the static scratch are refused with HKV_ERR_WORKSPACE and
+    leave the output untouched."""
+    cfg = W.CONFIGS[5]
+    f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
+    Q, Hq, D, Hkv = 256, cfg.num_q_heads, cfg.head_size, cfg.num_kv_heads
+    assert hkv.decode_workspace_bytes(f, Q, Hq, Hkv, 32768, 4) > hkv.DECODE_SCRATCH_BYTES
+    query = torch.zeros((Q, Hq, D), dtype=torch.float16, device=DEV)
+    cache = hkv.new_cache(f, 1, Hkv, DEV)
+    bt = torch.zeros((64, 1), dtype=torch.int32, device=DEV)
+    q2r = torch.arange(64, dtype=torch.int32, device=DEV).repeat_interleave(4)
+    q2k = torch.ones(Q, dtype=torch.int32, device=DEV)
+    out = torch.full((Q, Hq, D), 7.0, dtype=torch.float32, device=DEV)
+    with pytest.raises(hkv.HkvError) as e:
+        hkv.decode_attention_noalloc(f, query, cache, bt, q2r, q2k, 32768, 4, 0.0625, out)
+    assert e.value.status == hkv.HKV_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
