@@ -35,6 +35,27 @@ WARM_SECONDS = 0.3
 DIST_BLOCKS = 20    # blocks of 10 decode calls for the median / p10 / p90
 
 
+def arith_label(cfg) -> str:
+    """What the decode kernel this workload runs on computes in: the matrix
+    cores' operand types (the query enters as exact multi-part splits: three
+    int8 planes, or an fp16 leading part and residual), then fp32 softmax and
+    accumulation.  A query window wider than one kernel pass runs as
+    sub-groups of whole queries on the same kernel."""
+    group = cfg.num_q_heads // cfg.num_kv_heads
+    rows = group * cfg.n_q
+    i8 = "i8 MFMA scores (3 query planes) + f16 MFMA P.V, f32 softmax/accumulate"
+    f16 = "f16 MFMA scores (lead + residual query) and P.V, f32 softmax/accumulate"
+    if cfg.cache_dtype == "q4_0" and cfg.head_size == 256 and group <= 8:
+        return f16
+    if cfg.cache_dtype == "q8_0" and cfg.head_size == 256 and group <= 8:
+        return i8
+    if cfg.cache_dtype == "octave_k3v3_compact" and rows > 16 and group <= 32:
+        return f16
+    if cfg.cache_dtype.startswith("octave") and group <= 16:
+        return i8
+    return "f32"
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -453,7 +474,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": arith_label(cfg),
         "data": "synthetic",
         "config": {"workload": cfg.name, "cache_dtype": cfg.cache_dtype, "batch": B,
                    "context": int(w.max_klen), "head_size": D, "q_heads": Hq, "kv_heads": Hkv,

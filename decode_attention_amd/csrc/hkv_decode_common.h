@@ -172,6 +172,18 @@ __device__ __forceinline__ int wave_min_int(int v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Three int8 planes of a query code: qi = 2^16 hi + 2^8 mid + lo with hi in
+// [-127, 127] and mid, lo in [-128, 127], for |qi| <= kQ3MaxI.  Against int8
+// keys the three integer products give the score to about 23 bits of the
+// row's largest query value, whatever that value's magnitude.
+constexpr int kQ3MaxI = 127 * 65536 + 127 * 256 + 127;
+__device__ __forceinline__ void q_split3(int qi, int& hi, int& mid, int& lo) {
+  hi = (qi + 32896) >> 16;       // qi - 2^16 hi in [-32896, 32639]
+  const int rem = qi - hi * 65536;
+  mid = (rem + 128) >> 8;
+  lo = rem - mid * 256;
+}
+
 // Workgroups of a decode launch (see wg_item).
 inline int64_t decode_wgs(int num_groups, int nsub, int num_kv_heads, int num_splits) {
   const int64_t items = (int64_t)(num_groups / nsub) * num_kv_heads * num_splits;

@@ -25,8 +25,13 @@
 //  * Scores on v_mfma_i32_16x16x64_i8, one per 64-dim scale block: A = the
 //    int8 codebook values of the codes (looked up with v_perm_b32; 16-entry
 //    tables take two lookups and a per-byte select on the code's top bit),
-//    B = the rotated query as two int8 planes.  Each block's int32 result is
-//    scaled by the token's fp16 block scale.
+//    B = the rotated query as three int8 planes (q = 2^16 hi + 2^8 mid + lo
+//    per row, ~23 bits of the row's largest value, so the scores keep fp32
+//    accuracy at any query magnitude).  8-row mode: B columns [hi | lo] and
+//    [mid | 0]; the first product, shifted left 8 bits, accumulates the
+//    second, leaving 2^8 hi + mid and 2^8 lo in lanes n and n + 8.  16-row
+//    mode: one product per plane, 2^8 hi + mid joined the same way.  Each
+//    block's int32 result is scaled by the token's fp16 block scale.
 //  * P.V on v_mfma_f32_16x16x32_f16: B = the codebook value as an exact fp16
 //    (the biased byte LUT[c] + 128 under an 0x64 high byte is 1152 + LUT[c]),
 //    so no residual is needed on this side; the token's V scale multiplies p
@@ -46,7 +51,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
-typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // Slot layouts (slot words; vLLM docs, module text and OctaveFormat).
 // kCompact: K is one 3-bit block under one scale (else a 4-bit RoPE block and
@@ -122,8 +126,8 @@ struct FmtK3V3C {           // octave_k3v3_compact, head size 256
 constexpr int kRowsMax = 16;       // query rows per KV head (16-row mode)
 constexpr int kT = 16;             // tokens per tile
 constexpr int kTS = kT + 4;        // token stride (words) of the transposed tile
-constexpr int kQMaxI = 32639;      // largest |q| code of the two-plane int8 split
-constexpr float kQMax = 32639.0f;
+constexpr int kQMaxI = kQ3MaxI;    // largest |q| code of the three-plane int8 split
+constexpr float kQMax = (float)kQ3MaxI;
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max is raised
 constexpr int kQWaves = 8;         // waves per workgroup (two per SIMD)
 constexpr int kMaxSplitTiles = 256;
@@ -140,6 +144,25 @@ constexpr uint32_t kK3[2] = {lut_word(kLut3, 0, 0), lut_word(kLut3, 1, 0)};
 constexpr uint32_t kV4[4] = {lut_word(kLut4, 0, 128), lut_word(kLut4, 1, 128),
                              lut_word(kLut4, 2, 128), lut_word(kLut4, 3, 128)};
 constexpr uint32_t kV3[2] = {lut_word(kLut3, 0, 128), lut_word(kLut3, 1, 128)};
+
+// The 3-bit codebook as fp16 bit patterns, low bytes and high bytes, entries
+// 4 i .. 4 i + 3 in word i (one v_perm_b32 lookup each for four codes).
+constexpr uint32_t half_bits_int(int v) {  // exact for |v| < 2048
+  if (v == 0) return 0u;
+  const uint32_t sgn = v < 0 ? 0x8000u : 0u;
+  const int m = v < 0 ? -v : v;
+  int e = 0;
+  while ((m >> (e + 1)) != 0) ++e;
+  return sgn | ((uint32_t)(e + 15) << 10) | (((uint32_t)m << (10 - e)) & 0x3ffu);
+}
+constexpr uint32_t half_byte_word(int i, int byte) {
+  uint32_t w = 0;
+  for (int k = 0; k < 4; ++k) w |= ((half_bits_int(kLut3[4 * i + k]) >> (8 * byte)) & 255u) << (8 * k);
+  return w;
+}
+constexpr uint32_t kH3Lo[2] = {half_byte_word(0, 0), half_byte_word(1, 0)};
+constexpr uint32_t kH3Hi[2] = {half_byte_word(0, 1), half_byte_word(1, 1)};
+static_assert(half_bits_int(127) == 0x57F0u && half_bits_int(-14) == 0xCB00u, "fp16 bits");
 
 // 0xFF in each byte whose bit 7 is set in y, else 0x00 (v_perm_b32
 // sign-replicating selectors 8-11 read bit 7 of bytes 1, 3 of the low and
@@ -189,9 +212,11 @@ struct __align__(16) OctLds {
   static constexpr int kD = F::kD;
   static constexpr int kSlotW = (F::kSlot + 3) / 4 > 16 * F::kChunks ? (F::kSlot + 3) / 4
                                                                       : 16 * F::kChunks;
-  // B operand bytes, [64-dim block][column][dim]: 8-row mode column r + 8 plane,
-  // 16-row mode 16 plane + r.
-  int8_t qB[kD / 64][2 * RM][64];
+  // B operand bytes, [64-dim block][column][dim].  8-row mode: columns r
+  // (hi), 8 + r (lo), 16 + r (mid) of row r, 24-31 zero; 16-row mode: r (hi),
+  // 16 + r (lo), 32 + r (mid).
+  static constexpr int kQCols = RM == 8 ? 32 : 48;
+  int8_t qB[kD / 64][kQCols][64];
   float qsc[RM];
   float mlw[kQWaves][RM][2];
   int pid[kMaxSplitTiles];
@@ -304,11 +329,13 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     for (int e = 0; e < kE; ++e) {
       int qi = (int)rintf(x[e] * inv);
       qi = min(kQMaxI, max(-kQMaxI, qi));
-      const int hi = (qi + 128) >> 8;
-      const int lo = qi - hi * 256;
+      int hi, mid, lo;
+      q_split3(qi, hi, mid, lo);
       const int d = kWave * e + lane;
-      L.qB[d >> 6][kK16 ? r : r][d & 63] = (int8_t)hi;
+      L.qB[d >> 6][r][d & 63] = (int8_t)hi;
       L.qB[d >> 6][kK16 ? 16 + r : 8 + r][d & 63] = (int8_t)lo;
+      L.qB[d >> 6][kK16 ? 32 + r : 16 + r][d & 63] = (int8_t)mid;
+      if constexpr (!kK16) L.qB[d >> 6][24 + r][d & 63] = 0;
     }
     // 1/64: the codebook scale (LUT_ONE) of the K values.
     if (lane == 0) L.qsc[r] = (qmax / kQMax) * a.q_scale * (1.0f / 64.0f);
@@ -324,14 +351,17 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   __syncthreads();
 
   const float qs = L.qsc[row];
-  const float w_own = n < 8 ? 256.0f * qs : qs;
-  const float w_partner = n < 8 ? qs : 256.0f * qs;
-  // 8-row mode: one B operand per block (columns = rows x planes); 16-row
-  // mode: the hi and lo planes of 16 rows.
-  int4_t qreg[kD / 64], qlo[kK16 ? kD / 64 : 1];
+  // 8-row mode: lane n < 8 ends with 2^8 hi + mid of row n, lane n + 8 with
+  // 2^8 lo (in units of the row's query step).
+  const float w_own = n < 8 ? 256.0f * qs : qs * (1.0f / 256.0f);
+  const float w_partner = n < 8 ? qs * (1.0f / 256.0f) : 256.0f * qs;
+  // B operands of every block: 8-row mode [hi | lo] and [mid | 0] (columns =
+  // rows x planes); 16-row mode the hi, lo and mid planes of 16 rows.
+  int4_t qreg[kD / 64], qmid[kD / 64], qlo[kK16 ? kD / 64 : 1];
 #pragma unroll
   for (int c = 0; c < kD / 64; ++c) {
     qreg[c] = *(const int4_t*)&L.qB[c][n][16 * g];
+    qmid[c] = *(const int4_t*)&L.qB[c][(kK16 ? 32 : 16) + n][16 * g];
     if constexpr (kK16) qlo[c] = *(const int4_t*)&L.qB[c][16 + n][16 * g];
   }
   const bool live_row = row < a.rows;
@@ -412,6 +442,10 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 #pragma unroll
           for (int c = 0; c <= F::kNope; ++c)
             C[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[c], qreg[c], zero4, 0, 0, 0);
+          // (|2^8 hi + mid| sums stay below 2^29: 64 products of at most 2^14)
+#pragma unroll
+          for (int c = 0; c <= F::kNope; ++c)
+            C[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[c], qmid[c], C[c] << 8, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float acc = (float)C[0][i] * kscale(0, i);
@@ -420,7 +454,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
             sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
           }
         } else {
-          // hi and lo planes joined in int32 (exact: |hi| 256 + |lo| < 2^31).
+          // 2^8 hi + mid joined in int32 (exact, below 2^29), then the lo
+          // plane in fp32.
           int4_t H[1 + F::kNope], Lo[1 + F::kNope];
 #pragma unroll
           for (int c = 0; c <= F::kNope; ++c) {
@@ -428,17 +463,21 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
             Lo[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[c], qlo[c], zero4, 0, 0, 0);
           }
 #pragma unroll
+          for (int c = 0; c <= F::kNope; ++c)
+            H[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[c], qmid[c], H[c] << 8, 0, 0, 0);
+#pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float acc = (float)(H[0][i] * 256 + Lo[0][i]) * kscale(0, i);
+            float acc = fmaf((float)H[0][i], 256.0f, (float)Lo[0][i]) * kscale(0, i);
 #pragma unroll
             for (int c = 1; c <= F::kNope; ++c)
-              acc = fmaf((float)(H[c][i] * 256 + Lo[c][i]), kscale(c, i), acc);
+              acc = fmaf(fmaf((float)H[c][i], 256.0f, (float)Lo[c][i]), kscale(c, i), acc);
             sc[i] = acc * qs;
           }
         }
       } else {
-        // Four 64-dim blocks under one scale: the int32 results add up.
-        int4_t C = zero4, Cl = zero4;
+        // Four 64-dim blocks under one scale: the int32 results add up (the
+        // sums of one plane stay below 2^23, so 2^8 hi + mid below 2^31).
+        int4_t C = zero4, Cm = zero4, Cl = zero4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t lw = tr[(4 * c + g) * kTS + n];
@@ -450,15 +489,17 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
             Ac[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
           }
           C = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac, qreg[c], C, 0, 0, 0);
+          Cm = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac, qmid[c], Cm, 0, 0, 0);
           if constexpr (kK16) Cl = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac, qlo[c], Cl, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const int hm = C[i] * 256 + Cm[i];  // 8-row mode lanes n >= 8: 2^8 lo (Cm = 0)
           if constexpr (!kK16) {
-            const float acc = (float)C[i] * h2f((uint16_t)(ksw[i] & 0xffffu));
+            const float acc = (float)hm * h2f((uint16_t)(ksw[i] & 0xffffu));
             sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
           } else {
-            sc[i] = (float)(C[i] * 256 + Cl[i]) * h2f((uint16_t)(ksw[i] & 0xffffu)) * qs;
+            sc[i] = fmaf((float)hm, 256.0f, (float)Cl[i]) * h2f((uint16_t)(ksw[i] & 0xffffu)) * qs;
           }
         }
       }
@@ -708,11 +749,16 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 // The rows of a sequence group sharing a KV head (up to 32) take every tile
 // once, so the codebook lookups of K and V are paid once for all of them.
 // Both products run on the 32 x 32 matrix-core shapes:
-//  * scores on v_mfma_i32_32x32x32_i8: A = the int8 codebook values of 32
-//    tokens x 32 dims (a lane: token l % 32, dims 16 (l / 32) .. + 15 of the
-//    block, which are one low-plane word of the token), B = one plane of the
-//    rotated query (32 dims x 32 rows), two planes into two accumulators.
-//    A lane ends with the scores of its row l % 32 for tokens
+//  * scores on v_mfma_f32_32x32x16_f16: A = the codebook values of 32
+//    tokens x 16 dims as exact fp16 (a lane: token l % 32, 8 of the dims
+//    16 (l / 32) .. + 15 of a 32-dim block, which are one low-plane word of
+//    the token; two products per block), B = the rotated query, each row
+//    scaled by a power of two so that its largest value lies in
+//    [2^14, 2^15), as an fp16 leading part and the fp16 residual; both
+//    planes go into one fp32 accumulator, which keeps about 23 bits of the
+//    row's largest value whatever its magnitude.  (Three int8 planes would
+//    need a third 16-register accumulator, which this kernel has no room
+//    for.)  A lane ends with the scores of its row l % 32 for tokens
 //    8 j + 4 (l / 32) + i, j, i < 4: the very k-slots that lane supplies as
 //    the B operand of P.V, so p never moves between lanes.
 //  * P.V on v_mfma_f32_32x32x16_f16 as O^T = V^T P^T (rows = dims, columns =
@@ -731,7 +777,6 @@ constexpr int kOB = 65;  // row stride (floats) of the cross-wave sum: 64 values
 template <int W>
 struct __align__(16) Oct32Lds {
   static constexpr int kWords = 48;  // code words of a compact slot (the scale word is staged as floats)
-  int8_t qB[2][8][kR32][32];         // [plane][32-dim block][row][dim in block]
   float qsc[kR32];
   float mlw[W][kR32][2];
   int pid[kMaxSplitTiles];
@@ -741,6 +786,7 @@ struct __align__(16) Oct32Lds {
     struct {
       uint32_t tt[W][2][kWords][kTS];  // [tile][slot word][token], one unit per wave
       float sc[W][2][2][kT];           // [tile][K | V][token] scales as fp32
+      _Float16 qB[2][8][kR32][32];     // [lead | residual][32-dim block][row][dim in block]
     } s;
     float ob[W][2][kR32][kOB];         // [wave][l / 32][row][value] for one half of the dims
   } u;
@@ -834,19 +880,18 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
 #pragma unroll
     for (int e = 0; e < kE; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
     qmax = wave_max(qmax);
-    const float inv = qmax > 0.0f ? kQMax / qmax : 0.0f;
+    // x 2^k (exact) puts the row's largest value in [2^14, 2^15).
+    const float rs = qmax > 0.0f ? ldexpf(1.0f, 14 - ilogbf(qmax)) : 1.0f;
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-      int qi = (int)rintf(x[e] * inv);
-      qi = min(kQMaxI, max(-kQMaxI, qi));
-      const int hi = (qi + 128) >> 8;
-      const int lo = qi - hi * 256;
+      const float y = x[e] * rs;
+      const _Float16 hi = (_Float16)y;
       const int d = kWave * e + lane;
-      L.qB[0][d >> 5][r][d & 31] = (int8_t)hi;
-      L.qB[1][d >> 5][r][d & 31] = (int8_t)lo;
+      L.u.s.qB[0][d >> 5][r][d & 31] = hi;
+      L.u.s.qB[1][d >> 5][r][d & 31] = (_Float16)(y - (float)hi);  // exact difference
     }
     // 1/64: the codebook scale (LUT_ONE) of the K values.
-    if (lane == 0) L.qsc[r] = (qmax / kQMax) * a.q_scale * (1.0f / 64.0f);
+    if (lane == 0) L.qsc[r] = a.q_scale * (1.0f / 64.0f) / rs;
   }
   const int n = lane & 31;  // this lane's query row (scores, P.V columns) and token (K operand)
   const int h = lane >> 5;
@@ -900,23 +945,32 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
       }
 
       // ---- scores: 32 tokens x 32 rows ----
-      i32x16 chi = {}, clo = {};
+      f32x16 acc = {};
       {
         const uint32_t* tk = tw + (n >> 4) * (Oct32Lds<W>::kWords * kTS) + (n & 15);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const uint32_t lw = tk[(2 * c + h) * kTS];
           const uint32_t hw = tk[(F::kWKHi + c) * kTS] >> (4 * h);
-          int4_t A;
+          // dims 4 i + jb of the lane's 16 as fp16: product j takes i = 2 j, 2 j + 1
+          uint32_t A[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t s = ((lw >> (2 * i)) & 0x03030303u) | (((hw >> i) << 2) & 0x04040404u);
-            A[i] = (int)__builtin_amdgcn_perm(kK3[1], kK3[0], s);
+            const uint32_t lb = __builtin_amdgcn_perm(kH3Lo[1], kH3Lo[0], s);
+            const uint32_t hb = __builtin_amdgcn_perm(kH3Hi[1], kH3Hi[0], s);
+            A[2 * i] = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
+            A[2 * i + 1] = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
           }
-          const int4_t bh = *(const int4_t*)&L.qB[0][c][n][16 * h];
-          const int4_t bl = *(const int4_t*)&L.qB[1][c][n][16 * h];
-          chi = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, bh, chi, 0, 0, 0);
-          clo = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, bl, clo, 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint4 Aj = {A[4 * j], A[4 * j + 1], A[4 * j + 2], A[4 * j + 3]};
+            const half8_t a8 = __builtin_bit_cast(half8_t, Aj);
+            const half8_t bh = *(const half8_t*)&L.u.s.qB[0][c][n][16 * h + 8 * j];
+            const half8_t bl = *(const half8_t*)&L.u.s.qB[1][c][n][16 * h + 8 * j];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, bl, acc, 0, 0, 0);
+          }
         }
       }
       // score k = 4 j + i: token 8 j + 4 h + i of the unit (tile j >> 1),
@@ -928,7 +982,7 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
         const float kk[4] = {ks.x, ks.y, ks.z, ks.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          s[4 * j + i] = (float)(chi[4 * j + i] * 256 + clo[4 * j + i]) * kk[i];
+          s[4 * j + i] = acc[4 * j + i] * kk[i];
       }
       const int t0 = t_begin + 2 * kT * u_cur;
       if (!(t0 + 2 * kT <= t_lim)) {

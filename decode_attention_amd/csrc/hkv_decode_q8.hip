@@ -15,9 +15,13 @@
 // and one KV head, one unit after another:
 //  * Scores, S^T = K Q^T on v_mfma_i32_16x16x32_i8, one per 32-value block
 //    and tile: A is the block's int8 codes as loaded (lane (n, g): token n,
-//    codes 8 g .. 8 g + 7, one 8-byte load each), B the rotated query as two
-//    int8 planes (16 columns = 8 rows x {hi, lo}, ~15 bits of q); each
-//    block's int32 result is scaled by the token's fp16 block scale.
+//    codes 8 g .. 8 g + 7, one 8-byte load each), B the rotated query as
+//    three int8 planes, q = 2^16 hi + 2^8 mid + lo per row (~23 bits of the
+//    row's largest value, so the scores keep fp32 accuracy at any query
+//    magnitude), in two products: B columns [hi | lo] (8 rows x 2), then
+//    [mid | 0] accumulated onto the first result shifted left 8 bits, which
+//    leaves 2^8 hi + mid and 2^8 lo in lanes n and n + 8; each block's int32
+//    result is scaled by the token's fp16 block scale.
 //  * A lane then holds 4 consecutive tokens of one row per tile: the 8
 //    scores of a unit are the A operand of v_mfma_f32_16x16x32_f16 for P.V
 //    (rows 0-7 fp16(p), rows 8-15 the residual x 2^12).  B is code x scale
@@ -46,8 +50,8 @@ constexpr int kNB = kD / 32;            // Q8_0 blocks per head vector
 constexpr int kRows = 8;                // query rows per KV head
 constexpr int kT = 16;                  // tokens per tile
 constexpr int kSlot = 2 * kD + kD / 8;  // 544: K codes, V codes, 8 + 8 fp16 scales
-constexpr int kQMaxI = 32639;           // largest |q| code of the two-plane int8 split
-constexpr float kQMax = 32639.0f;
+constexpr int kQMaxI = kQ3MaxI;         // largest |q| code of the three-plane int8 split
+constexpr float kQMax = (float)kQ3MaxI;
 constexpr int kVS = kT + 4;             // padded token stride of the transposed V tile
 constexpr float kLazy = 8.0f;           // log2 headroom before the running max is raised
 constexpr int kQWaves = 8;              // waves per workgroup (two per SIMD)
@@ -65,7 +69,9 @@ struct Tile8 {
 };
 
 struct __align__(16) Q8Lds {
-  int8_t qB[kNB][16][32];  // B operand bytes: [block][column][dim]
+  // B operand bytes, [block][column][dim]: columns r (hi), 8 + r (lo),
+  // 16 + r (mid) of row r, 24-31 zero.
+  int8_t qB[kNB][32][32];
   float qsc[kRows];        // per-row score scale
   float mlw[kQWaves][kRows][2];
   int pid[kMaxSplitTiles];  // page of each tile of the split
@@ -183,11 +189,13 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
     for (int e = 0; e < 4; ++e) {
       int qi = (int)rintf(x[e] * inv);
       qi = min(kQMaxI, max(-kQMaxI, qi));
-      const int hi = (qi + 128) >> 8;
-      const int lo = qi - hi * 256;
+      int hi, mid, lo;
+      q_split3(qi, hi, mid, lo);
       const int d = kWave * e + lane;
       L.qB[d >> 5][r][d & 31] = (int8_t)hi;
       L.qB[d >> 5][8 + r][d & 31] = (int8_t)lo;
+      L.qB[d >> 5][16 + r][d & 31] = (int8_t)mid;
+      L.qB[d >> 5][24 + r][d & 31] = 0;
     }
     if (lane == 0) L.qsc[r] = (qmax / kQMax) * a.q_scale;
   }
@@ -201,11 +209,13 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
 
   const float qs = L.qsc[row];
   // The query's B operand of every block, held in registers for the whole stream.
+  // (the mid plane is read from LDS at each use: registers are full)
   long qreg[kNB];
 #pragma unroll
   for (int b = 0; b < kNB; ++b) qreg[b] = *(const long*)&L.qB[b][n][8 * g];
-  const float w_own = n < 8 ? 256.0f * qs : qs;
-  const float w_partner = n < 8 ? qs : 256.0f * qs;
+  const long* const qmid = (const long*)&L.qB[0][16 + n][8 * g];
+  const float w_own = n < 8 ? 256.0f * qs : qs * (1.0f / 256.0f);
+  const float w_partner = n < 8 ? qs * (1.0f / 256.0f) : 256.0f * qs;
   const bool live_row = row < a.rows;  // lanes n and n + 8 carry the same row
   const float alpha_a = live_row ? (n < 8 ? 1.0f : 4096.0f) : 0.0f;
   const float beta_a = live_row ? (n < 8 ? 0.0f : -4096.0f) : 0.0f;
@@ -271,8 +281,10 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
 #pragma unroll
         for (int b = 0; b < kNB; ++b) {
           const uint2 kw = hb ? kb[b] : ka[b];
-          const int4_t C = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, kw),
-                                                                 qreg[b], zero4, 0, 0, 0);
+          const long ak = __builtin_bit_cast(long, kw);
+          // (|2^8 hi + mid| sums stay below 2^28: 32 products of at most 2^14)
+          int4_t C = __builtin_amdgcn_mfma_i32_16x16x32_i8(ak, qreg[b], zero4, 0, 0, 0);
+          C = __builtin_amdgcn_mfma_i32_16x16x32_i8(ak, qmid[b * (32 * 32 / 8)], C << 8, 0, 0, 0);
           // K scales of block b for tokens 4g..4g+3 of this tile
           const uint2 ks = *(const uint2*)&L.u.s.sh[wave][0][b][g][hb][0];
 #pragma unroll
@@ -281,6 +293,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
             const float sk = h2f((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
             acc[i] = fmaf((float)C[i], sk, acc[i]);
           }
+          // (two blocks at a time: interleaving more holds more results live
+          // than the registers allow)
+          if (b & 1) __builtin_amdgcn_sched_barrier(0);
         }
         // lane n < 8 holds the hi plane and lane n + 8 the lo plane of a row
 #pragma unroll

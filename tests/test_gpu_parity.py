@@ -362,9 +362,9 @@ def test_decode_compact_one_pass_edge_lengths(Hq, Hkv):
     q_to_klen = np.array([[L - 3, L - 2, L - 1, L] for L in lens], np.int32).reshape(-1)
     q_to_klen[2] = 0                 # klen 0 -> zero row
     q_to_klen[-4] = -5               # negative -> zero row
-    # small and large query magnitudes in one pass (per-row query planes; the
-    # largest gives logits of a few tens, within the range where the query's
-    # 15-bit planes keep the scores inside the tolerance)
+    # small and large query magnitudes in one pass (each row's query operand
+    # follows its own scale; larger magnitudes are covered in
+    # test_gpu_query_magnitude.py)
     q = (rng.standard_normal((len(q_to_req), Hq, D)) *
          rng.choice([0.01, 1.0, 4.0], size=(len(q_to_req), Hq, 1))).astype(np.float32)
     scale = W.default_sm_scale(D)

@@ -1,0 +1,91 @@
+"""Decode parity at large query magnitudes.
+
+The pages' reference attention takes its scores in fp32 on the float query
+and the dequantized keys (vLLM API docs, "vllm.v1.attention.ops.rocm_octave",
+reference_attention), so the tolerance holds whatever the query's scale.
+Queries x30 and x100 put logits in the hundreds, where the softmax is nearly
+one-hot and a score error of 1e-3 already moves the output; one pass mixes
+x0.01 and x100 rows, so each row's query operand must follow its own scale.
+Every decode kernel is covered: Q4_0 and Q8_0 on the matrix cores, the
+Octave kernel in its 8-row and 16-row modes, the one-pass 32-row kernel, and
+the generic kernel.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_amd import hkv
+from decode_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-3
+DEV = "cuda:0"
+
+KERNELS = [  # dtype, D, rope_dim, Hq, Hkv, queries_per_seq
+    ("q4_0", 256, 0, 16, 2, 1),                   # Q4_0 matrix-core kernel, 8 rows
+    ("q8_0", 256, 0, 16, 2, 1),                   # Q8_0 matrix-core kernel, 8 rows
+    ("octave_k3v4", 128, 64, 32, 8, 1),           # Octave kernel, 8-row mode (4 live rows)
+    ("octave_k3v4", 128, 64, 32, 4, 2),           # Octave kernel, 16-row mode
+    ("octave_k3v3_compact", 256, 64, 32, 4, 1),   # Octave compact, 8 rows
+    ("octave_k3v3_compact", 256, 64, 32, 4, 4),   # one-pass 32-row kernel
+    ("q8_0", 128, 0, 8, 2, 1),                    # generic kernel
+]
+
+
+def _case(dtype, D, R, Hq, Hkv, qps, mult, seed):
+    lens = [1300, 700, 37]
+    P = 16
+    rng = np.random.default_rng(seed)
+    T = sum(lens)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    pages = [(L + P - 1) // P for L in lens]
+    perm = rng.permutation(sum(pages))
+    bt = np.zeros((len(lens), max(pages)), np.int32)
+    sm = np.empty(T, np.int64)
+    off = t0 = 0
+    for b, L in enumerate(lens):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+        pos = np.arange(L)
+        sm[t0:t0 + L] = bt[b, pos // P].astype(np.int64) * P + pos % P
+        t0 += L
+    q_to_req = np.arange(len(lens), dtype=np.int32).repeat(qps)
+    q_to_klen = np.array([[L - qps + 1 + i for i in range(qps)] for L in lens],
+                         np.int32).reshape(-1)
+    q = rng.standard_normal((len(q_to_req), Hq, D))
+    if mult == "mixed":
+        q *= rng.choice([0.01, 100.0], size=(len(q_to_req), Hq, 1))
+    else:
+        q *= mult
+    return k, v, sm, bt, q_to_req, q_to_klen, q.astype(np.float32)
+
+
+@pytest.mark.parametrize("mult", [30.0, 100.0, "mixed"])
+@pytest.mark.parametrize("dtype,D,R,Hq,Hkv,qps", KERNELS)
+def test_decode_large_query_magnitudes(dtype, D, R, Hq, Hkv, qps, mult):
+    print(f"query magnitude {mult}: {dtype} D={D} Hq={Hq} Hkv={Hkv} qps={qps}", flush=True)
+    k, v, sm, bt, q_to_req, q_to_klen, q = _case(dtype, D, R, Hq, Hkv, qps, mult,
+                                                 seed=D + 7 * Hq + qps)
+    P = 16
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
+    cache = hkv.new_cache(f, int(bt.max()) + 1, Hkv, DEV)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    ref_cache = np.zeros(tuple(cache.shape), np.uint8)
+    ref_cache[sm // P, :, sm % P] = slots
+    assert np.array_equal(cache.cpu().numpy(), ref_cache)
+    scale = W.default_sm_scale(D)
+    got = hkv.decode_attention(f, torch.from_numpy(q).to(DEV), cache,
+                               torch.from_numpy(bt).to(DEV), torch.from_numpy(q_to_req).to(DEV),
+                               torch.from_numpy(q_to_klen).to(DEV), int(q_to_klen.max()), qps,
+                               scale).cpu().numpy().astype(np.float64)
+    ref = O.attention(fo, q, ref_cache, bt, q_to_req, q_to_klen, scale)
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    assert not bad.any(), (f"{dtype} x{mult}: {bad.sum()} of {bad.size} outside tolerance; "
+                           f"max abs err {err.max():.3e}")
