@@ -60,6 +60,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--deterministic", action="store_true",
+                   help="decode in the bitwise-reproducible mode (fixed unit order)")
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=3)
     p.add_argument("--copies", type=int, default=0,
@@ -350,11 +352,12 @@ def main():
         c = caches[i % copies]
         hkv.quantize_append(f, new_k, new_v, new_sm, c)
         hkv.decode_attention(f, query, c, block_table, q_to_req, q_to_klen, w.max_klen, cfg.n_q,
-                             scale, out=out, workspace=workspace)
+                             scale, out=out, workspace=workspace, deterministic=args.deterministic)
 
     def decode_call(i):
         hkv.decode_attention(f, query, caches[i % copies], block_table, q_to_req, q_to_klen,
-                             w.max_klen, cfg.n_q, scale, out=out, workspace=workspace)
+                             w.max_klen, cfg.n_q, scale, out=out, workspace=workspace,
+                             deterministic=args.deterministic)
 
     run_step, run_decode = step, decode_call
     if args.graph:
@@ -480,7 +483,8 @@ def main():
                    "context": int(w.max_klen), "head_size": D, "q_heads": Hq, "kv_heads": Hkv,
                    "page_size": cfg.page_size, "queries_per_seq": cfg.n_q,
                    "append_tokens_per_seq": cfg.n_append, "cache_copies_rotated": copies,
-                   "launch": "hip_graph" if args.graph else "eager"},
+                   "launch": "hip_graph" if args.graph else "eager",
+                   "deterministic": bool(args.deterministic)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_call"],

@@ -296,8 +296,8 @@ hkv_status decode_check(const char* who, const hkv_format* f, const void* query,
                         const uint8_t* cache, const int32_t* block_table,
                         int32_t max_pages_per_req, const int32_t* q_to_req,
                         const int32_t* q_to_klen, int32_t max_klen, int32_t queries_per_seq,
-                        float sm_scale, const float* out, hkv::DevFmt* d, hkv::DecodePlan* p,
-                        bool* done) {
+                        float sm_scale, uint32_t flags, const float* out, hkv::DevFmt* d,
+                        hkv::DecodePlan* p, bool* done) {
   *done = false;
   hkv_status st = check_format(f);
   if (st != HKV_OK) return st;
@@ -313,6 +313,8 @@ hkv_status decode_check(const char* who, const hkv_format* f, const void* query,
     return fail(HKV_ERR_INVALID_ARG, "%s: bad query dtype %d", who, (int)q_dtype);
   if (max_klen < 0) return fail(HKV_ERR_INVALID_ARG, "%s: max_klen < 0", who);
   if (!std::isfinite(sm_scale)) return fail(HKV_ERR_INVALID_ARG, "%s: sm_scale not finite", who);
+  if (flags & ~HKV_DECODE_DETERMINISTIC)
+    return fail(HKV_ERR_INVALID_ARG, "%s: unknown flags 0x%x", who, flags);
   if (num_queries == 0) {
     *done = true;
     return HKV_OK;
@@ -338,15 +340,16 @@ hkv_status hkv_decode_attention(const hkv_format* f, const void* query, int32_t 
                                 const uint8_t* cache, const int32_t* block_table,
                                 int32_t max_pages_per_req, const int32_t* q_to_req,
                                 const int32_t* q_to_klen, int32_t max_klen,
-                                int32_t queries_per_seq, float sm_scale, float* out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                int32_t queries_per_seq, float sm_scale, uint32_t flags,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   hkv::DevFmt d;
   hkv::DecodePlan p;
   bool done;
   const hkv_status st =
       decode_check("decode", f, query, q_dtype, num_queries, num_q_heads, num_kv_heads, cache,
                    block_table, max_pages_per_req, q_to_req, q_to_klen, max_klen,
-                   queries_per_seq, sm_scale, out, &d, &p, &done);
+                   queries_per_seq, sm_scale, flags, out, &d, &p, &done);
   if (st != HKV_OK || done) return st;
   if (workspace_bytes < p.workspace_bytes || (p.workspace_bytes && !workspace))
     return fail(HKV_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
@@ -356,6 +359,7 @@ hkv_status hkv_decode_attention(const hkv_format* f, const void* query, int32_t 
   const hipError_t e = hkv::launch_decode(d, p, query, q_dtype == HKV_F16, num_q_heads,
                                           num_kv_heads, cache, block_table, max_pages_per_req,
                                           q_to_req, q_to_klen, sm_scale, out, workspace,
+                                          (flags & HKV_DECODE_DETERMINISTIC) != 0,
                                           (hipStream_t)stream);
   return e == hipSuccess ? HKV_OK : hip_fail(e, "decode launch");
 }
@@ -366,14 +370,15 @@ hkv_status hkv_decode_attention_noalloc(const hkv_format* f, const void* query, 
                                         const int32_t* block_table, int32_t max_pages_per_req,
                                         const int32_t* q_to_req, const int32_t* q_to_klen,
                                         int32_t max_klen, int32_t queries_per_seq,
-                                        float sm_scale, float* out, void* stream) {
+                                        float sm_scale, uint32_t flags, float* out,
+                                        void* stream) {
   hkv::DevFmt d;
   hkv::DecodePlan p;
   bool done;
   const hkv_status st =
       decode_check("decode_noalloc", f, query, q_dtype, num_queries, num_q_heads, num_kv_heads,
                    cache, block_table, max_pages_per_req, q_to_req, q_to_klen, max_klen,
-                   queries_per_seq, sm_scale, out, &d, &p, &done);
+                   queries_per_seq, sm_scale, flags, out, &d, &p, &done);
   if (st != HKV_OK || done) return st;
   if (p.workspace_bytes > HKV_DECODE_SCRATCH_BYTES)
     return fail(HKV_ERR_WORKSPACE,
@@ -385,7 +390,7 @@ hkv_status hkv_decode_attention_noalloc(const hkv_format* f, const void* query, 
   if (e != hipSuccess) return hip_fail(e, "decode_noalloc: scratch address");
   e = hkv::launch_decode(d, p, query, q_dtype == HKV_F16, num_q_heads, num_kv_heads, cache,
                          block_table, max_pages_per_req, q_to_req, q_to_klen, sm_scale, out,
-                         scratch, (hipStream_t)stream);
+                         scratch, (flags & HKV_DECODE_DETERMINISTIC) != 0, (hipStream_t)stream);
   return e == hipSuccess ? HKV_OK : hip_fail(e, "decode_noalloc launch");
 }
 

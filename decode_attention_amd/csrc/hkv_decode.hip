@@ -591,7 +591,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
                          int num_q_heads, int num_kv_heads, const uint8_t* cache,
                          const int32_t* block_table, int max_pages_per_req,
                          const int32_t* q_to_req, const int32_t* q_to_klen, float sm_scale,
-                         float* out, void* workspace, hipStream_t s) {
+                         float* out, void* workspace, bool deterministic, hipStream_t s) {
   if (p.num_groups == 0) return hipSuccess;
   DecArgs a;
   a.query = query;
@@ -615,6 +615,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   a.num_splits = p.num_splits;
   a.ws = (float*)workspace;
   a.pstride = (int)p.partial_floats;
+  a.det = deterministic ? 1 : 0;
   const int R = round_rows(p.rows);
   const dim3 grid((unsigned)p.num_wgs);
   hipError_t e;

@@ -32,6 +32,8 @@ struct DecArgs {
   int num_splits;
   float* ws;
   int pstride;    // floats per partial record: 4 + D (m, l, pad, pad, o[D])
+  int det;        // 1: each wave takes its units in a fixed order (no queue),
+                  // so the summation order, and the result, never vary
 };
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -43,6 +45,16 @@ __device__ __forceinline__ float wave_max(float v) {
 // Lane l <- lane (l ^ 8) within each row of 16 (DPP row_ror:8).
 __device__ __forceinline__ float ror8(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+
+// The 8-row matrix-core kernels hold the two parts of a score row in lanes n
+// and n + 8 of each row of 16 and join them in both lanes, with the parts in
+// opposite roles, so the two joins can differ in the last bit.  Lane n + 8
+// then takes lane n's score: the lanes derive the leading fp16 part and the
+// residual of one p, which must come from bitwise the same score.
+__device__ __forceinline__ float pair_score(float own_join, int n) {
+  const float from_n = ror8(own_join);
+  return n < 8 ? own_join : from_n;
 }
 
 // Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 with the lane-swap
@@ -109,7 +121,7 @@ __device__ __forceinline__ void pin_args(DecArgs& a, int& x0, int& x1, float& y)
   asm("" : "+s"(a.q_f16), "+s"(a.num_q_heads), "+s"(a.num_kv_heads), "+s"(a.group),
       "+s"(a.n_q), "+s"(a.rows), "+s"(a.rows_pad), "+s"(a.num_queries), "+s"(a.num_groups),
       "+s"(a.nsub), "+s"(a.max_pages), "+s"(a.tokens_per_split), "+s"(a.num_splits),
-      "+s"(a.pstride), "+s"(x0), "+s"(x1), "+s"(y));
+      "+s"(a.pstride), "+s"(a.det), "+s"(x0), "+s"(x1), "+s"(y));
   a.query = pin_global(a.query);
   a.cache = pin_global(a.cache);
   a.block_table = pin_global(a.block_table);

@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
             float acc = (float)C[0][i] * kscale(0, i);
 #pragma unroll
             for (int c = 1; c <= F::kNope; ++c) acc = fmaf((float)C[c][i], kscale(c, i), acc);
-            sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+            sc[i] = pair_score(fmaf(acc, w_own, ror8(acc) * w_partner), n);
           }
         } else {
           // 2^8 hi + mid joined in int32 (exact, below 2^29), then the lo
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
           const int hm = C[i] * 256 + Cm[i];  // 8-row mode lanes n >= 8: 2^8 lo (Cm = 0)
           if constexpr (!kK16) {
             const float acc = (float)hm * h2f((uint16_t)(ksw[i] & 0xffffu));
-            sc[i] = fmaf(acc, w_own, ror8(acc) * w_partner);
+            sc[i] = pair_score(fmaf(acc, w_own, ror8(acc) * w_partner), n);
           } else {
             sc[i] = fmaf((float)hm, 256.0f, (float)Cl[i]) * h2f((uint16_t)(ksw[i] & 0xffffu)) * qs;
           }
@@ -657,9 +657,11 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     int buf = 0;
     AOps A;
     while (u_nxt < nu) {
-      int u_nn = 0;
-      if (lane == 0) u_nn = atomicAdd(&L.next_unit, 1);
-      u_nn = __builtin_amdgcn_readfirstlane(u_nn);
+      int u_nn = u_nxt + kQWaves;  // deterministic mode: a fixed order
+      if (!a.det) {
+        if (lane == 0) u_nn = atomicAdd(&L.next_unit, 1);
+        u_nn = __builtin_amdgcn_readfirstlane(u_nn);
+      }
       stage_m(sa, sb, u_cur, buf, A);
       // One basic block: P.V of unit u_cur and the scores of unit u_nxt.
       const int sbuf = buf ^ 1;
@@ -936,9 +938,11 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
         }
       }
       wave_sync_lds();
-      int u_nxt = 0;
-      if (lane == 0) u_nxt = atomicAdd(&L.next_unit, 1);
-      u_nxt = __builtin_amdgcn_readfirstlane(u_nxt);
+      int u_nxt = u_cur + W;  // deterministic mode: a fixed order
+      if (!a.det) {
+        if (lane == 0) u_nxt = atomicAdd(&L.next_unit, 1);
+        u_nxt = __builtin_amdgcn_readfirstlane(u_nxt);
+      }
       if (u_nxt < nu) {
         fetch(ta, 2 * u_nxt);
         fetch(tb, 2 * u_nxt + 1);

@@ -379,10 +379,11 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
       };
       // Lane n < 8 holds the leading part and lane n + 8 the residual of a
       // row: both form q_scale / s (lead + res / 2^11) from their own value
-      // and the partner's.
+      // and the partner's, and lane n + 8 keeps lane n's result.
       auto stage_s_join = [&](const SState& st, float (&sc)[4]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = fmaf(st.acc[i], w_own, ror8(st.acc[i]) * w_partner);
+        for (int i = 0; i < 4; ++i)
+          sc[i] = pair_score(fmaf(st.acc[i], w_own, ror8(st.acc[i]) * w_partner), n);
       };
       auto stage_s = [&](int h, int buf, float (&sc)[4]) {
         SState st;
@@ -503,9 +504,11 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4_mfma_kernel(DevF
       int buf = 0;
       half8_t A;
       while (u_nxt < nu) {
-        int u_nn = 0;
-        if (lane == 0) u_nn = atomicAdd(&L.next_unit, 1);
-        u_nn = __builtin_amdgcn_readfirstlane(u_nn);
+        int u_nn = u_nxt + kQWaves;  // deterministic mode: a fixed order
+        if (!a.det) {
+          if (lane == 0) u_nn = atomicAdd(&L.next_unit, 1);
+          u_nn = __builtin_amdgcn_readfirstlane(u_nn);
+        }
         stage_m(sa, sb, u_cur, A);
         const int sbuf = buf ^ 1;
         store_unit(u_nxt, sbuf);

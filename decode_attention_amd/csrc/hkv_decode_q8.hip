@@ -264,9 +264,11 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
       uint2 ka[kNB], kb[kNB];
 #pragma unroll
       for (int b = 0; b < kNB; ++b) ka[b] = ta.k[b], kb[b] = tb.k[b];
-      int u_nxt = 0;
-      if (lane == 0) u_nxt = atomicAdd(&L.next_unit, 1);
-      u_nxt = __builtin_amdgcn_readfirstlane(u_nxt);
+      int u_nxt = u_cur + kQWaves;  // deterministic mode: a fixed order
+      if (!a.det) {
+        if (lane == 0) u_nxt = atomicAdd(&L.next_unit, 1);
+        u_nxt = __builtin_amdgcn_readfirstlane(u_nxt);
+      }
       if (u_nxt < nu) {
         fetch(ta, 2 * u_nxt);
         fetch(tb, 2 * u_nxt + 1);
@@ -299,7 +301,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
         }
         // lane n < 8 holds the hi plane and lane n + 8 the lo plane of a row
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[4 * hb + i] = fmaf(acc[i], w_own, ror8(acc[i]) * w_partner);
+        for (int i = 0; i < 4; ++i)
+          s[4 * hb + i] = pair_score(fmaf(acc[i], w_own, ror8(acc[i]) * w_partner), n);
       }
 
       // ---- softmax: mask, running max, p, the P.V A operand ----

@@ -47,7 +47,7 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
                          int num_q_heads, int num_kv_heads, const uint8_t* cache,
                          const int32_t* block_table, int max_pages_per_req,
                          const int32_t* q_to_req, const int32_t* q_to_klen, float sm_scale,
-                         float* out, void* workspace, hipStream_t s);
+                         float* out, void* workspace, bool deterministic, hipStream_t s);
 
 // Device address of the static decode scratch (HKV_DECODE_SCRATCH_BYTES) on
 // the current device, looked up once per device.

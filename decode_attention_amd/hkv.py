@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libhkv.so")
 
 HKV_OK, HKV_ERR_INVALID_ARG, HKV_ERR_UNSUPPORTED, HKV_ERR_WORKSPACE, HKV_ERR_HIP = range(5)
 HKV_F32, HKV_F16 = 0, 1
+HKV_DECODE_DETERMINISTIC = 1
 HKV_KIND_Q4_0, HKV_KIND_OCTAVE, HKV_KIND_Q8_0 = 0, 1, 2
 HKV_MAX_HEAD = 256
 DECODE_SCRATCH_BYTES = 64 << 20  # HKV_DECODE_SCRATCH_BYTES
@@ -75,12 +76,12 @@ def lib():
             L.hkv_decode_workspace_bytes.argtypes = [P(HkvFormat), i32, i32, i32, i32, i32]
             L.hkv_decode_workspace_bytes.restype = ctypes.c_size_t
             L.hkv_decode_attention.argtypes = [P(HkvFormat), vp, i32, i32, i32, i32, vp,
-                                               vp, i32, vp, vp, i32, i32, ctypes.c_float, vp, vp,
-                                               ctypes.c_size_t, vp]
+                                               vp, i32, vp, vp, i32, i32, ctypes.c_float,
+                                               ctypes.c_uint32, vp, vp, ctypes.c_size_t, vp]
             L.hkv_decode_attention.restype = ctypes.c_int
             L.hkv_decode_attention_noalloc.argtypes = [P(HkvFormat), vp, i32, i32, i32, i32,
                                                        vp, vp, i32, vp, vp, i32, i32,
-                                                       ctypes.c_float, vp, vp]
+                                                       ctypes.c_float, ctypes.c_uint32, vp, vp]
             L.hkv_decode_attention_noalloc.restype = ctypes.c_int
             L.hkv_hadamard.argtypes = [vp, i32, vp, i64, i32, i32, vp, i32, vp]
             L.hkv_hadamard.restype = ctypes.c_int
@@ -201,8 +202,9 @@ def decode_attention(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
                      block_table: torch.Tensor, q_to_req: torch.Tensor, q_to_klen: torch.Tensor,
                      max_klen: int, queries_per_seq: int = 1, sm_scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> torch.Tensor:
-    """Decode attention; see include/hkv.h (one call at a time per workspace)."""
+                     stream=None, deterministic: bool = False) -> torch.Tensor:
+    """Decode attention; see include/hkv.h (one call at a time per workspace;
+    deterministic=True: bitwise reproducible, a few percent slower)."""
     _need(query, "query", dims=3, device=False)
     _need(cache, "cache", dtype=torch.uint8, dims=4, device=False)
     _need(block_table, "block_table", dtype=torch.int32, dims=2, device=False)
@@ -242,15 +244,16 @@ def decode_attention(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
     _check(lib().hkv_decode_attention(
         ctypes.byref(fmt), _ptr(query), _dtype_code(query), Q, Hq, Hkv, _ptr(cache),
         _ptr(block_table), block_table.shape[1], _ptr(q_to_req), _ptr(q_to_klen), int(max_klen),
-        int(queries_per_seq), float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        int(queries_per_seq), float(sm_scale), HKV_DECODE_DETERMINISTIC if deterministic else 0,
+        _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 
 def decode_attention_noalloc(fmt: HkvFormat, query: torch.Tensor, cache: torch.Tensor,
                              block_table: torch.Tensor, q_to_req: torch.Tensor,
                              q_to_klen: torch.Tensor, max_klen: int, queries_per_seq: int,
-                             sm_scale: float, out: torch.Tensor, stream=None) -> torch.Tensor:
+                             sm_scale: float, out: torch.Tensor, stream=None,
+                             deterministic: bool = False) -> torch.Tensor:
     """Decode attention into a caller's `out` with the library's static scratch
     in place of a workspace; allocates nothing (include/hkv.h).  Calls that
     overlap in time on one device race on the scratch."""
@@ -276,7 +279,8 @@ def decode_attention_noalloc(fmt: HkvFormat, query: torch.Tensor, cache: torch.T
     _check(lib().hkv_decode_attention_noalloc(
         ctypes.byref(fmt), _ptr(query), _dtype_code(query), Q, Hq, cache.shape[1], _ptr(cache),
         _ptr(block_table), block_table.shape[1], _ptr(q_to_req), _ptr(q_to_klen), int(max_klen),
-        int(queries_per_seq), float(sm_scale), _ptr(out), _stream(stream)))
+        int(queries_per_seq), float(sm_scale), HKV_DECODE_DETERMINISTIC if deterministic else 0,
+        _ptr(out), _stream(stream)))
     return out
 
 

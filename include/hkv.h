@@ -150,6 +150,9 @@ size_t hkv_decode_workspace_bytes(const hkv_format* f /*host*/, int32_t num_quer
                                   int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t max_klen, int32_t queries_per_seq);
 
+/* hkv_decode_attention flags. */
+#define HKV_DECODE_DETERMINISTIC 1u
+
 /*
  * hkv_decode_attention -- per-query-token attention over the paged quantized
  * cache ([OCT] reference_attention; query rotated like K and output rotated
@@ -168,6 +171,13 @@ size_t hkv_decode_workspace_bytes(const hkv_format* f /*host*/, int32_t num_quer
  *                 sub-groups of whole queries, each reading the cache).
  *                 num_queries must be a multiple.
  *   sm_scale:     softmax scale applied to q.k.
+ *   flags:        0 or HKV_DECODE_DETERMINISTIC.  By default the waves of a
+ *                 workgroup take the split's 32-token units from a shared
+ *                 queue, which balances their load but lets the summation
+ *                 order, and so the last bits of the result, vary between
+ *                 calls.  HKV_DECODE_DETERMINISTIC gives each wave a fixed
+ *                 set of units: bitwise the same result for the same inputs
+ *                 on every call, at a cost of a few percent.
  *   out:          (num_queries, num_q_heads, D) fp32, unrotated space.
  *   workspace:    >= hkv_decode_workspace_bytes(...) bytes, 16-byte aligned.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
@@ -178,8 +188,9 @@ hkv_status hkv_decode_attention(const hkv_format* f /*host*/, const void* query,
                                 const uint8_t* cache, const int32_t* block_table,
                                 int32_t max_pages_per_req, const int32_t* q_to_req,
                                 const int32_t* q_to_klen, int32_t max_klen,
-                                int32_t queries_per_seq, float sm_scale, float* out,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                int32_t queries_per_seq, float sm_scale, uint32_t flags,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Bytes of the static per-device scratch of hkv_decode_attention_noalloc. */
 #define HKV_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
@@ -208,8 +219,8 @@ hkv_status hkv_decode_attention_noalloc(const hkv_format* f /*host*/, const void
                                         const uint8_t* cache, const int32_t* block_table,
                                         int32_t max_pages_per_req, const int32_t* q_to_req,
                                         const int32_t* q_to_klen, int32_t max_klen,
-                                        int32_t queries_per_seq, float sm_scale, float* out,
-                                        void* stream);
+                                        int32_t queries_per_seq, float sm_scale,
+                                        uint32_t flags, float* out, void* stream);
 
 /*
  * hkv_hadamard -- blockwise orthonormal Walsh-Hadamard rotation of rows, the

@@ -42,11 +42,18 @@ int main() {
           expect(hkv_dequantize(&f, cache, 2, reinterpret_cast<int64_t*>(dummy), 1, 0, dummy,
                                 dummy, nullptr) == HKV_ERR_INVALID_ARG, "dequantize alignment");
           expect(hkv_decode_attention(&f, dummy, HKV_F32, 2, 16, 3, nullptr, nullptr, 1, nullptr,
-                                      nullptr, 64, 1, 0.1f, nullptr, nullptr, 0, nullptr) ==
+                                      nullptr, 64, 1, 0.1f, 0, nullptr, nullptr, 0, nullptr) ==
                      HKV_ERR_INVALID_ARG, "decode head ratio");
           expect(hkv_decode_attention(&f, dummy, HKV_F32, 3, 16, 2, nullptr, nullptr, 1, nullptr,
-                                      nullptr, 64, 2, 0.1f, nullptr, nullptr, 0, nullptr) ==
+                                      nullptr, 64, 2, 0.1f, 0, nullptr, nullptr, 0, nullptr) ==
                      HKV_ERR_INVALID_ARG, "decode queries_per_seq");
+          expect(hkv_decode_attention(&f, dummy, HKV_F32, 2, 16, 2, nullptr, nullptr, 1, nullptr,
+                                      nullptr, 64, 1, 0.1f, 8u, nullptr, nullptr, 0, nullptr) ==
+                     HKV_ERR_INVALID_ARG, "decode flags");
+          expect(hkv_decode_attention_noalloc(&f, dummy, HKV_F32, 2, 16, 3, nullptr, nullptr, 1,
+                                              nullptr, nullptr, 64, 1, 0.1f, 0, nullptr,
+                                              nullptr) == HKV_ERR_INVALID_ARG,
+                 "decode_noalloc head ratio");
           hkv_format g = f;
           g.slot_bytes += 1;
           expect(hkv_quantize_append(&g, dummy, dummy, HKV_F32, 1, 1, nullptr, nullptr, nullptr) ==

@@ -118,8 +118,8 @@ def test_decode_host_errors_and_workspace():
             ctypes.byref(kw.get("f", f)), kw.get("q", FAKE), kw.get("dt", 1), kw.get("Q", 4),
             kw.get("Hq", 16), kw.get("Hkv", 2), kw.get("cache", FAKE), kw.get("bt", FAKE),
             kw.get("mp", 8192), kw.get("qr", FAKE), kw.get("ql", FAKE), kw.get("mk", 131072),
-            kw.get("nq", 1), kw.get("scale", 0.0625), kw.get("out", FAKE), kw.get("ws", FAKE),
-            kw.get("wsb", need), None)
+            kw.get("nq", 1), kw.get("scale", 0.0625), kw.get("flags", 0), kw.get("out", FAKE),
+            kw.get("ws", FAKE), kw.get("wsb", need), None)
     assert call(Q=0) == hkv.HKV_OK
     assert call(Hkv=3) == hkv.HKV_ERR_INVALID_ARG
     assert call(nq=3) == hkv.HKV_ERR_INVALID_ARG
@@ -128,6 +128,7 @@ def test_decode_host_errors_and_workspace():
     assert call(out=None) == hkv.HKV_ERR_INVALID_ARG
     assert call(mk=-1) == hkv.HKV_ERR_INVALID_ARG
     assert call(scale=float("inf")) == hkv.HKV_ERR_INVALID_ARG
+    assert call(flags=2) == hkv.HKV_ERR_INVALID_ARG             # unknown flag bit
     assert call(wsb=need - 1) == hkv.HKV_ERR_WORKSPACE
     assert call(ws=None) == hkv.HKV_ERR_WORKSPACE
     assert call(ws=FAKE + 4) == hkv.HKV_ERR_INVALID_ARG
@@ -146,7 +147,8 @@ def test_decode_noalloc_host_errors():
         return L.hkv_decode_attention_noalloc(
             ctypes.byref(kw.get("f", f)), kw.get("q", FAKE), 1, kw.get("Q", 256),
             kw.get("Hq", 32), kw.get("Hkv", 4), kw.get("cache", FAKE), FAKE, 2048, FAKE, FAKE,
-            kw.get("mk", 32768), kw.get("nq", 4), 0.0625, kw.get("out", FAKE), None)
+            kw.get("mk", 32768), kw.get("nq", 4), 0.0625, kw.get("flags", 1), kw.get("out", FAKE),
+            None)
     need = hkv.decode_workspace_bytes(f, 256, 32, 4, 32768, 4)
     assert need > hkv.DECODE_SCRATCH_BYTES                  # 65 MiB of partial records
     assert call() == hkv.HKV_ERR_WORKSPACE
@@ -156,6 +158,7 @@ def test_decode_noalloc_host_errors():
     assert call(q=None) == hkv.HKV_ERR_INVALID_ARG
     assert call(out=None) == hkv.HKV_ERR_INVALID_ARG
     assert call(mk=-1) == hkv.HKV_ERR_INVALID_ARG
+    assert call(flags=4) == hkv.HKV_ERR_INVALID_ARG
     assert call(cache=FAKE + 2) == hkv.HKV_ERR_INVALID_ARG
     assert call(Hq=256, Hkv=1, Q=4, nq=1) == hkv.HKV_ERR_UNSUPPORTED
     assert "HKV_DECODE_SCRATCH_BYTES ((size_t)64 << 20)" in open(

@@ -35,13 +35,14 @@ def _oracle_cache(fo, w, shape):
     return ref, slots
 
 
-def _decode(f, w, cache, scale, qps=None):
+def _decode(f, w, cache, scale, qps=None, deterministic=False):
     cfg = w.cfg
     return hkv.decode_attention(f, torch.from_numpy(w.query).to(DEV), cache,
                                 torch.from_numpy(w.block_table).to(DEV),
                                 torch.from_numpy(w.q_to_req).to(DEV),
                                 torch.from_numpy(w.q_to_klen).to(DEV), w.max_klen,
-                                cfg.n_q if qps is None else qps, scale)
+                                cfg.n_q if qps is None else qps, scale,
+                                deterministic=deterministic)
 
 
 def _assert_close(got, ref, what):
@@ -383,15 +384,15 @@ def test_decode_is_deterministic_and_page_relabel_invariant():
     f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
     cache = _gpu_cache(f, w)
     scale = W.default_sm_scale(cfg.head_size)
-    a = _decode(f, w, cache, scale).cpu().numpy()
-    b = _decode(f, w, cache, scale).cpu().numpy()
+    a = _decode(f, w, cache, scale, deterministic=True).cpu().numpy()
+    b = _decode(f, w, cache, scale, deterministic=True).cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     # relabel physical pages: identical result
     perm = torch.randperm(cache.shape[0], generator=torch.Generator().manual_seed(0))
     cache2 = torch.empty_like(cache)
     cache2[perm.to(DEV)] = cache
     w2 = W.Workload(**{**w.__dict__, "block_table": perm.numpy()[w.block_table].astype(np.int32)})
-    c = _decode(f, w2, cache2, scale).cpu().numpy()
+    c = _decode(f, w2, cache2, scale, deterministic=True).cpu().numpy()
     assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
 
 
@@ -408,7 +409,12 @@ def _full_size_check(ci, seqs, n_slot_samples=4096):
     """A workload at its full size, decoded in the launch configuration the
     benchmark times; the oracle checks sampled slots bit for bit and every
     output row of the sequences in `seqs` (it quantizes those sequences
-    itself: nothing it uses comes from the GPU)."""
+    itself: nothing it uses comes from the GPU).
+
+    The deterministic mode is the race detector of the waves' shared LDS
+    work: two of its calls must agree bit for bit over the whole output
+    (every wave, every split and the merge run in a fixed order), and agree
+    with the default mode to rounding."""
     cfg = W.CONFIGS[ci]
     w = W.make_workload(cfg)
     f = hkv.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim, cfg.page_size)
@@ -416,6 +422,10 @@ def _full_size_check(ci, seqs, n_slot_samples=4096):
     cache = _gpu_cache(f, w)
     scale = W.default_sm_scale(cfg.head_size)
     got = _decode(f, w, cache, scale).cpu().numpy()
+    det1 = _decode(f, w, cache, scale, deterministic=True).cpu().numpy()
+    det2 = _decode(f, w, cache, scale, deterministic=True).cpu().numpy()
+    assert np.array_equal(det1.view(np.uint32), det2.view(np.uint32)), (
+        f"deterministic mode: {(det1 != det2).sum()} of {det1.size} values differ between calls")
     P = cfg.page_size
     # sampled slots, bit-exact
     rng = np.random.default_rng(7)
@@ -435,7 +445,15 @@ def _full_size_check(ci, seqs, n_slot_samples=4096):
     ref = O.attention(fo, sub.query.astype(np.float32), ref_cache, sub.block_table, sub.q_to_req,
                       sub.q_to_klen, scale)
     qsel = np.concatenate([np.nonzero(w.q_to_req == b)[0] for b in seqs])
-    _assert_close(got[qsel], ref, f"config {ci} full size, sequences {seqs}")
+    e_def = _assert_close(got[qsel], ref, f"config {ci} full size, sequences {seqs}")
+    e_det = _assert_close(det1[qsel], ref, f"config {ci} full size, deterministic, sequences {seqs}")
+    # the two modes differ only in summation order: far inside the oracle bar
+    d = np.abs(det1.astype(np.float64) - got)
+    bad = d > ATOL / 10 + RTOL / 10 * np.abs(got)
+    where = np.unravel_index(int(np.argmax(d)), d.shape)
+    assert not bad.any(), (f"modes differ at {bad.sum()} of {bad.size} values; max {d.max():.3e} at "
+                           f"{where} ({got[where]:.6e} vs {det1[where]:.6e}); oracle errors "
+                           f"default {e_def:.3e}, deterministic {e_det:.3e}")
 
 
 def test_decode_full_size_q4_0_128k():
