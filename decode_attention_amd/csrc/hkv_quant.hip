@@ -63,10 +63,29 @@ __device__ __forceinline__ float block_tree_sum(float (&t)[E], int e0, int nreg)
   return wave_tree_sum(acc);
 }
 
-// Octave quantizer (_quantize_lut) over registers [e0, e0+nreg) of a strided
-// vector: block RMS, nearest Lloyd-Max code, scale with x . x_hat = |x|^2.
-// The codes land in codes[e0 .. e0+nreg); returns the fp16 bits of the scale
-// (the same in every lane).
+// The Octave block quantizer (vLLM docs "vllm.v1.attention.ops.rocm_octave",
+// _quantize_lut) rests on three properties, one helper each:
+//  * the block is normalised by its RMS, sqrt(|x|^2 / n), floored at 1e-12 so
+//    that an all-zero block divides by a positive number;
+//  * each value takes the code of the nearest codebook entry to its
+//    normalised value times the codebook's multiplier (bucket, above);
+//  * the fp16 scale s makes the dequantized block x_hat = s * LUT[code] / 64
+//    keep the block's norm along x: x . x_hat = |x|^2, i.e.
+//    s = 64 * |x|^2 / (x . LUT[code]), and 0 when that dot product is not
+//    positive (an all-zero block).
+// Every sum is one of the block sums in their fixed order.
+__device__ __forceinline__ float oct_block_rms(float ss, int n) {
+  const float r = sqrtf(ss / (float)n);
+  return r < 1e-12f ? 1e-12f : r;
+}
+__device__ __forceinline__ uint32_t oct_norm_preserving_scale(float ss, float dot) {
+  const float q = dot > 0.0f ? ss / (dot > 1e-30f ? dot : 1e-30f) : 0.0f;
+  return f2h(q * (float)kLutOne);
+}
+
+// The quantizer over registers [e0, e0+nreg) of a strided vector.  The codes
+// land in codes[e0 .. e0+nreg); returns the fp16 bits of the scale (the same
+// in every lane).
 template <int E, int BITS>
 __device__ __forceinline__ uint32_t octave_block(const float (&x)[E], int e0, int nreg,
                                                  uint32_t (&codes)[E]) {
@@ -74,23 +93,18 @@ __device__ __forceinline__ uint32_t octave_block(const float (&x)[E], int e0, in
 #pragma unroll
   for (int e = 0; e < E; ++e) t[e] = x[e] * x[e];
   const float ss = block_tree_sum<E>(t, e0, nreg);
-  float rms = sqrtf(ss / (float)(nreg * kWave));
-  rms = rms < 1e-12f ? 1e-12f : rms;
+  const float rms = oct_block_rms(ss, nreg * kWave);
   const float mult = (float)(BITS == 3 ? kLutMult3 : kLutMult4);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     t[e] = 0.0f;
     if (e >= e0 && e < e0 + nreg) {
-      const float y = (x[e] / rms) * mult;
       int lv;
-      codes[e] = (uint32_t)bucket<BITS>(y, &lv);
+      codes[e] = (uint32_t)bucket<BITS>((x[e] / rms) * mult, &lv);
       t[e] = x[e] * (float)lv;
     }
   }
-  const float dot = block_tree_sum<E>(t, e0, nreg);
-  float sc = 0.0f;
-  if (dot > 0.0f) sc = ss / (dot > 1e-30f ? dot : 1e-30f);
-  return f2h(sc * (float)kLutOne);
+  return oct_norm_preserving_scale(ss, block_tree_sum<E>(t, e0, nreg));
 }
 
 // Q4_0 over one 32-value block = one half-register (lanes 0-31 or 32-63).
@@ -1001,8 +1015,7 @@ __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float 
 #pragma unroll
     for (int i = 0; i < 4; ++i) t[q][i] = x[q][i] * x[q][i];
   const float ss = tree16<Q, NQ>(t, q0);
-  float rms = sqrtf(ss / (float)(NQ * kWave));
-  rms = rms < 1e-12f ? 1e-12f : rms;
+  const float rms = oct_block_rms(ss, NQ * kWave);
   const float ry = recip_rn(rms);
   float qv[NQ][4];
   bool tiny = false;
@@ -1034,10 +1047,7 @@ __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float 
       codes[q0 + q][i] = oct_code<BITS>(T, qv[q][i] * m2, &lv);
       t[q0 + q][i] = x[q0 + q][i] * lv;
     }
-  const float dot = tree16<Q, NQ>(t, q0);
-  float sc = 0.0f;
-  if (dot > 0.0f) sc = ss / (dot > 1e-30f ? dot : 1e-30f);
-  return f2h(sc * (float)kLutOne);
+  return oct_norm_preserving_scale(ss, tree16<Q, NQ>(t, q0));
 }
 
 // Slot words of one group's codes (segment-relative group qq, segment of n
