@@ -788,7 +788,10 @@ struct __align__(16) Oct32Lds {
     struct {
       uint32_t tt[W][2][kWords][kTS];  // [tile][slot word][token], one unit per wave
       float sc[W][2][2][kT];           // [tile][K | V][token] scales as fp32
-      _Float16 qB[2][8][kR32][32];     // [lead | residual][32-dim block][row][dim in block]
+      // [lead | residual][32-dim block][row][dim in block]; rows padded to 40
+      // halves (20 words), so the 16-byte reads of 16 rows at a time cover
+      // every bank once
+      _Float16 qB[2][8][kR32][40];
     } s;
     float ob[W][2][kR32][kOB];         // [wave][l / 32][row][value] for one half of the dims
   } u;

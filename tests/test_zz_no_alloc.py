@@ -66,6 +66,15 @@ def test_noalloc_matches_workspace_entry_point(ci, first, second):
         ref = O.attention(fo, w.query, cache.cpu().numpy(), w.block_table, w.q_to_req,
                           w.q_to_klen, scale)
         _within(got, ref, "noalloc vs oracle")
+        # the deterministic mode of both entry points runs the same kernels
+        # in the same order: the outputs agree bit for bit
+        det_na = hkv.decode_attention_noalloc(f, t["query"], cache, t["bt"], t["q2r"], t["q2k"],
+                                              w.max_klen, cfg.n_q, scale, torch.empty_like(out_na),
+                                              deterministic=True)
+        det_ws = hkv.decode_attention(f, t["query"], cache, t["bt"], t["q2r"], t["q2k"],
+                                      w.max_klen, cfg.n_q, scale, workspace=ws, deterministic=True)
+        torch.cuda.synchronize()
+        assert torch.equal(det_na.view(torch.int32), det_ws.view(torch.int32))
 
 
 def test_noalloc_refuses_oversize_scratch():
