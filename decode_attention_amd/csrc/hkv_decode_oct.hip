@@ -365,8 +365,6 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     if constexpr (kK16) qlo[c] = *(const int4_t*)&L.qB[c][16 + n][16 * g];
   }
   const bool live_row = row < a.rows;
-  const float alpha_a = live_row ? (kK16 || n < 8 ? 1.0f : 4096.0f) : 0.0f;
-  const float beta_a = live_row ? (kK16 || n < 8 ? 0.0f : -4096.0f) : 0.0f;
   // Gathers byte (n & 3) of a word of tokens t0..t3 into bytes 0..3.
   const int jb = n & 3;
   const uint32_t gsel_lo = (uint32_t)jb | ((uint32_t)(jb + 4) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
@@ -382,7 +380,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   float4_t o[kAcc];
 #pragma unroll
   for (int b = 0; b < kAcc; ++b) o[b] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  // sps: running sum of the P.V A operand's p s over this lane's tokens (the
+  // values enter biased by 1152; the bias is removed at the end with it)
+  float m_run = -INFINITY, l_run = 0.0f, sps = 0.0f;
 
   if (has_work) {
     // Scores of one tile (before masking) from its registers; the tile goes
@@ -536,6 +536,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
         const float m_new = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
         l_run *= alpha;
+        sps *= alpha;
         float al[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, kK16 ? 4 * g + i : (4 * g + i) & 7, kWave);
@@ -552,19 +553,35 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       const uint4 va = lds_u4(&L.u.tt[wave][buf][0][kWVs][4 * g]);
       const uint4 vb = lds_u4(&L.u.tt[wave][buf][1][kWVs][4 * g]);
       const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+      float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float p = __builtin_amdgcn_exp2f(s[i] - m_ref - 6.0f);  // p / 64
         l_run += p;
-        const float pv = p * h2f((uint16_t)((vw[i] >> kVsh) & 0xffffu));
-        const _Float16 h = (_Float16)pv;
+        pv[i] = p * h2f((uint16_t)((vw[i] >> kVsh) & 0xffffu));
+        sps += pv[i];
+      }
+      // The leading fp16 parts come from one conversion instruction and the
+      // residuals are taken against exactly those values, so that the matrix
+      // cores see p s to 2^-21 (the 1152 bias of the values multiplies any
+      // gap between the two parts).
+      _Float16 h[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half2_t hp = __builtin_amdgcn_cvt_pkrtz(pv[2 * j], pv[2 * j + 1]);
+        h[2 * j] = (_Float16)hp[0];
+        h[2 * j + 1] = (_Float16)hp[1];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const _Float16 r = (_Float16)(fmaf((float)h[i], -4096.0f, pv[i] * 4096.0f));  // exact before the rounding
         if constexpr (!kK16) {
-          A.a[i] = (_Float16)fmaf((float)h, beta_a, pv * alpha_a);
+          A.a[i] = live_row ? (n < 8 ? h[i] : r) : (_Float16)0.0f;
         } else {
           // k-slots 0-3: fp16(p s) of the tile's 4 tokens, 4-7: residual x 2^12.
           half8_t& At = i < 4 ? A.a : A.b;
-          At[i & 3] = (_Float16)(pv * alpha_a);
-          At[4 + (i & 3)] = (_Float16)(fmaf((float)h, -1.0f, pv) * (4096.0f * alpha_a));
+          At[i & 3] = live_row ? h[i] : (_Float16)0.0f;
+          At[4 + (i & 3)] = live_row ? r : (_Float16)0.0f;
         }
       }
     };
@@ -594,9 +611,6 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       }
     };
     auto stage_p = [&](const AOps& A, int buf, int w0, int nw) {
-      const half8_t c1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
-                             (_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
-                             (_Float16)-1152.0f, (_Float16)-1152.0f};
       const uint32_t* va = &L.u.tt[wave][buf][0][0][4 * g];
       const uint32_t* vb = &L.u.tt[wave][buf][1][0][4 * g];
       // Biased codebook bytes of four codes -> fp16 pairs (1024 + byte).
@@ -620,8 +634,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
           const uint32_t ha = lut16((ga >> 4) & 0x07070707u, byte_sign_mask(ga), kV4[0], kV4[1], kV4[2], kV4[3]);
           const uint32_t lb = lut16(gb & 0x07070707u, byte_sign_mask(gb << 4), kV4[0], kV4[1], kV4[2], kV4[3]);
           const uint32_t hb = lut16((gb >> 4) & 0x07070707u, byte_sign_mask(gb), kV4[0], kV4[1], kV4[2], kV4[3]);
-          const half8_t lo = __builtin_bit_cast(half8_t, spread(la, lb)) + c1152;
-          const half8_t hi = __builtin_bit_cast(half8_t, spread(ha, hb)) + c1152;
+          const half8_t lo = __builtin_bit_cast(half8_t, spread(la, lb));
+          const half8_t hi = __builtin_bit_cast(half8_t, spread(ha, hb));
           mma(A, lo, o[2 * W]);
           mma(A, hi, o[2 * W + 1]);
         }
@@ -641,7 +655,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
             const uint32_t sb_ = ((glb >> (2 * vi)) & 0x03030303u) | (((ghb >> sh) << 2) & 0x04040404u);
             const uint32_t la = __builtin_amdgcn_perm(kV3[1], kV3[0], sa_);
             const uint32_t lb = __builtin_amdgcn_perm(kV3[1], kV3[0], sb_);
-            const half8_t vv = __builtin_bit_cast(half8_t, spread(la, lb)) + c1152;
+            const half8_t vv = __builtin_bit_cast(half8_t, spread(la, lb));
             mma(A, vv, o[m]);
           }
         }
@@ -701,13 +715,16 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   // ---- merge the waves ----------------------------------------------------
   float lsum = l_run + __shfl_xor(l_run, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
+  // the row's sum of p s (lanes n and n + 8 of the 8-row mode hold the same)
+  float ssum = sps + __shfl_xor(sps, 16, kWave);
+  ssum += __shfl_xor(ssum, 32, kWave);
   if (g == 0 && n < RM) {
     L.mlw[wave][n][0] = m_run;
     L.mlw[wave][n][1] = lsum * 64.0f;  // p was kept as p / 64
   }
   __syncthreads();
   if (kK16 || g < 2) {
-    float fw[4];
+    float fw[4], bias[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;
@@ -716,12 +733,13 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
       const float mw = L.mlw[wave][r][0];
       fw[i] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+      bias[i] = 1152.0f * __shfl(ssum, r, kWave);
     }
 #pragma unroll
     for (int b = 0; b < kAcc; ++b) {
       const int d = F::kV3 ? 16 * b + n : 32 * (b >> 1) + 8 * (n >> 2) + (n & 3) + 4 * (b & 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = o[b][i] * fw[i];
+      for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = (o[b][i] - bias[i]) * fw[i];
     }
   }
   __syncthreads();
