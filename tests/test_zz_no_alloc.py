@@ -95,3 +95,43 @@ def test_noalloc_refuses_oversize_scratch():
     assert e.value.status == hkv.HKV_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+def test_noalloc_replays_from_a_graph():
+    """The use the entry point is for: a decode captured in a HIP graph (no
+    allocation may happen under capture).  Every replay, with eager work of
+    the program between replays, gives the eager deterministic-mode bits."""
+    cfg, w, f, cache, t = _setup(3, dict(batch=2, seq_len=3000))
+    Q, Hq, D = w.query.shape
+    scale = W.default_sm_scale(cfg.head_size)
+    out = torch.empty((Q, Hq, D), dtype=torch.float32, device=DEV)
+
+    def call():
+        hkv.decode_attention_noalloc(f, t["query"], cache, t["bt"], t["q2r"], t["q2k"],
+                                     w.max_klen, cfg.n_q, scale, out, deterministic=True)
+
+    call()  # first call on the device: the scratch address is looked up here
+    torch.cuda.synchronize()
+    eager = out.clone()
+    ref = O.attention(O.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim), w.query,
+                      cache.cpu().numpy(), w.block_table, w.q_to_req, w.q_to_klen, scale)
+    _within(eager.cpu().numpy().astype(np.float64), ref, "noalloc eager vs oracle")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    other = torch.empty_like(out)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        hkv.decode_attention(f, t["query"], cache, t["bt"], t["q2r"], t["q2k"], w.max_klen,
+                             cfg.n_q, scale, out=other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"replay {rep}"
