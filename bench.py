@@ -15,6 +15,7 @@ CPU oracle on a bounded sample of the same workload.
     python bench.py [--steps K] [--warmup W] [--config 3]
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -94,29 +95,61 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
 
 
-def source_hash() -> str:
+# Sources of the decode kernels a cache format runs on: the format's
+# split-K kernel, the planner, merge and generic kernel, and their headers.
+DECODE_SOURCES = {
+    "q4_0": "hkv_decode_q4.hip",
+    "q8_0": "hkv_decode_q8.hip",
+    "octave": "hkv_decode_oct.hip",
+}
+SHARED_SOURCES = ("hkv_decode.hip", "hkv_decode_common.h", "hkv_device.h", "hkv_internal.h")
+
+
+def source_hash(cache_dtype=None) -> str:
+    """Hash of the kernel sources: all of csrc, or only those the decode of
+    `cache_dtype` runs on."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "decode_attention_amd", "csrc")
-    for n in sorted(os.listdir(d)):
+    names = sorted(os.listdir(d))
+    if cache_dtype is not None:
+        own = DECODE_SOURCES["octave" if cache_dtype.startswith("octave") else cache_dtype]
+        names = sorted((own,) + SHARED_SOURCES)
+    for n in names:
         with open(os.path.join(d, n), "rb") as f:
             h.update(n.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, cache_dtype: str):
     """HBM traffic per decode call from committed rocprofv3 counter runs, if
-    they were taken on the current kernel sources."""
+    they were taken on the current sources of this format's decode kernels."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
+    if t.get("decode_source_hash") != source_hash(cache_dtype):
         return None
     return t
 
 
 CPU_WORKERS = 16   # host threads a GPU job may use on the benchmark machines
+
+
+def gpu_info(torch) -> dict:
+    """The device the run used: name, architecture, compute units, and its
+    peak engine clock (hipDeviceGetAttribute, hipDeviceAttributeClockRate =
+    5 in hip_runtime_api.h of this ROCm)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:
+            info["peak_clock_mhz"] = v.value // 1000
+    except OSError:
+        pass
+    return info
 
 
 def host_cpus() -> int:
@@ -463,9 +496,11 @@ def main():
     bulk_ms = e0.elapsed_time(e1) / copies
 
     packed = W.packed_bytes(w, f.slot_bytes)
+    bulk_gbs = (2 * total_tokens * Hkv * D * w.key.itemsize +
+                total_tokens * Hkv * f.slot_bytes) / (bulk_ms * 1e-3) / 1e9
     value = packed / (ms_per_step * 1e-3) / 1e9
     achieved = packed / (decode_ms * 1e-3) / 1e9
-    traffic = load_traffic(cfg.name)
+    traffic = load_traffic(cfg.name, cfg.cache_dtype)
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -500,9 +535,9 @@ def main():
         "append_tokens_per_s": (round(len(rows) / (append_ms * 1e-3), 1)
                                 if append_ms > 0 else None),
         "bulk_quantize_tokens_per_s": round(total_tokens / (bulk_ms * 1e-3), 1),
-        "bulk_quantize_gbps": round((2 * total_tokens * Hkv * D * w.key.itemsize +
-                                     total_tokens * Hkv * f.slot_bytes) / (bulk_ms * 1e-3) / 1e9,
-                                    3),
+        "bulk_quantize_gbps": round(bulk_gbs, 3),
+        "bulk_quantize_hbm_frac": round(bulk_gbs / HBM_PEAK_GBS, 4),
+        "gpu": gpu_info(torch),
     }
     if not args.no_cpu_baseline and not args.profile:
         threads = args.cpu_threads or min(CPU_WORKERS, host_cpus())
