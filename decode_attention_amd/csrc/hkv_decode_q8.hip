@@ -182,8 +182,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q8_mfma_kernel(DevF
 #pragma unroll
     for (int e = 0; e < 4; ++e) qmax = fmaxf(qmax, fabsf(x[e]));
     qmax = wave_max(qmax);
-    // |q| <= 32639 keeps both planes in int8: hi = (q + 128) >> 8 in
-    // [-127, 127], lo = q - 256 hi in [-128, 127].
+    // |q| <= kQ3MaxI keeps the three planes in int8 (q_split3).
     const float inv = qmax > 0.0f ? kQMax / qmax : 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
