@@ -171,17 +171,23 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, w, threads: int, scale: float, min_seconds: float = 10.0):
+def cpu_baseline(cfg, w, threads: int, scale: float, min_seconds: float = 10.0,
+                 outputs: list = None):
     """The oracle, as it is, on the host cores: quantize the appended rows,
     then the fp64 attention of every query.  Attention is independent per
-    (query, KV head), so the oracle is called on each such sub-problem (the
-    query's G heads of that KV head over that head's cache), one thread per
-    sub-problem."""
+    (query, KV head), and within one such sub-problem per token range: the
+    oracle runs on each page-aligned range (a shifted block-table row and the
+    range's length) and the ranges merge with their log-sum-exp weights.
+    Every (query, KV head) is cut into as many ranges as it takes to give
+    each thread at least one, and the threads take the pieces in turn.
+    If outputs is a list, the merged attention of the last pass, shaped
+    (queries, Hq, D), is appended to it."""
     import oracle as O
     from decode_attention_amd import workloads as W
 
     fo = O.format_init(cfg.cache_dtype, cfg.head_size, cfg.rope_dim)
     S = fo.slot_bytes
+    P = cfg.page_size
     Hkv, G = cfg.num_kv_heads, cfg.num_q_heads // cfg.num_kv_heads
     # Oracle cache of the whole workload (setup, not timed), built in parallel.
     T = w.key.shape[0]
@@ -198,43 +204,67 @@ def cpu_baseline(cfg, w, threads: int, scale: float, min_seconds: float = 10.0):
     # One cache per KV head, (pages, 1, page_size, S).
     head_cache = []
     for h in range(Hkv):
-        c = np.zeros((w.num_pages, 1, cfg.page_size, S), np.uint8)
-        c[w.slot_mapping // cfg.page_size, 0, w.slot_mapping % cfg.page_size] = slots[:, h]
+        c = np.zeros((w.num_pages, 1, P, S), np.uint8)
+        c[w.slot_mapping // P, 0, w.slot_mapping % P] = slots[:, h]
         head_cache.append(c)
     rows = w.append_rows()
     qf = w.query.astype(np.float32)
     kf = w.key[rows].astype(np.float32)
     vf = w.value[rows].astype(np.float32)
     subs = [(i, h) for i in range(len(w.q_to_req)) for h in range(Hkv)]
-    n_threads = max(1, min(threads, len(subs)))
-    results = [None] * len(subs)
+    n_ranges = max(1, -(-threads // len(subs)))
+    pieces = []                                   # (sub index, first page, tokens)
+    for k, (i, h) in enumerate(subs):
+        L = int(w.q_to_klen[i])
+        pages = -(-L // P)
+        cuts = np.unique(np.linspace(0, pages, n_ranges + 1).round().astype(int))
+        for p0, p1 in zip(cuts[:-1], cuts[1:]):
+            pieces.append((k, int(p0), min(L, int(p1) * P) - int(p0) * P))
+    n_threads = max(1, min(threads, len(pieces)))
+    results = [None] * len(pieces)
 
-    def awork(k0):
-        for k in range(k0, len(subs), n_threads):
+    def awork(j0):
+        for j in range(j0, len(pieces), n_threads):
+            k, p0, n = pieces[j]
             i, h = subs[k]
-            results[k] = O.attention(fo, np.ascontiguousarray(qf[i:i + 1, h * G:(h + 1) * G]),
-                                     head_cache[h], w.block_table, w.q_to_req[i:i + 1],
-                                     w.q_to_klen[i:i + 1], scale)
+            r = int(w.q_to_req[i])
+            results[j] = O.attention_lse(
+                fo, np.ascontiguousarray(qf[i:i + 1, h * G:(h + 1) * G]), head_cache[h],
+                np.ascontiguousarray(w.block_table[r:r + 1, p0:]), np.zeros(1, np.int32),
+                np.array([n], np.int32), scale)
+
+    def merge():
+        out = np.zeros((len(subs), G, cfg.head_size))
+        lse = np.full((len(subs), G), -np.inf)
+        for (k, _, _), (_, s) in zip(pieces, results):
+            lse[k] = np.logaddexp(lse[k], s[0])
+        for (k, _, _), (o, s) in zip(pieces, results):
+            out[k] += np.exp(s[0] - lse[k])[:, None] * o[0]
+        return out
     # One pass = the whole step; passes repeat until min_seconds have elapsed.
     reps = 0
     t0 = time.perf_counter()
     while True:
         O.quantize(fo, kf, vf)
-        th = [threading.Thread(target=awork, args=(k,)) for k in range(n_threads)]
+        th = [threading.Thread(target=awork, args=(j,)) for j in range(n_threads)]
         [t.start() for t in th]
         [t.join() for t in th]
+        merged = merge()
         reps += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
     total = time.perf_counter() - t0
     dt = total / reps
+    if outputs is not None:
+        outputs.append(merged.reshape(len(w.q_to_req), Hkv * G, cfg.head_size))
     nbytes = W.packed_bytes(w, S)
     return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": n_threads,
             "kind": "oracle", "host_cpus": host_cpus(), "cpu_model": cpu_model(),
             "sample": (f"the full step of the workload, {reps} passes: quantize of {len(rows)} "
                        f"appended token rows and fp64 attention of {len(w.q_to_req)} queries over "
-                       f"{nbytes} packed-KV bytes, as {len(subs)} independent (query, KV head) "
-                       f"calls of the oracle; {dt:.3f} s per pass, {total:.1f} s wall on "
+                       f"{nbytes} packed-KV bytes, as {len(pieces)} oracle calls over "
+                       f"page-aligned token ranges of the {len(subs)} (query, KV head) pairs, "
+                       f"merged by log-sum-exp; {dt:.3f} s per pass, {total:.1f} s wall on "
                        f"{n_threads} threads ({host_cpus()} host CPUs available)")}
 
 

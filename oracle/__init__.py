@@ -71,6 +71,9 @@ def lib():
             L.orc_dequantize_f64.argtypes = [P(Format), P(ctypes.c_uint8), i64, i32, P(f64), P(f64)]
             L.orc_attention.argtypes = [P(Format), P(f32), i32, i32, P(ctypes.c_uint8), i32, i32,
                                         P(i32), i32, P(i32), P(i32), f64, P(f64)]
+            L.orc_attention_lse.argtypes = [P(Format), P(f32), i32, i32, P(ctypes.c_uint8), i32,
+                                            i32, P(i32), i32, P(i32), P(i32), f64, P(f64),
+                                            P(f64)]
             _lib = L
     return _lib
 
@@ -242,3 +245,25 @@ def attention(fmt: Format, query: np.ndarray, cache: np.ndarray, block_table: np
                         Hkv, page, _p(bt, ctypes.c_int32), bt.shape[1], _p(qr, ctypes.c_int32),
                         _p(ql, ctypes.c_int32), float(sm_scale), _p(out, ctypes.c_double))
     return out
+
+
+def attention_lse(fmt: Format, query: np.ndarray, cache: np.ndarray, block_table: np.ndarray,
+                  q_to_req: np.ndarray, q_to_klen: np.ndarray, sm_scale: float):
+    """attention() and, per (query, head), the natural log of the softmax
+    denominator over the row's scaled scores (-inf for a row with no tokens):
+    attention over disjoint token ranges merges exactly with these weights."""
+    q = np.ascontiguousarray(query, np.float32)
+    c = np.ascontiguousarray(cache, np.uint8)
+    bt = np.ascontiguousarray(block_table, np.int32)
+    qr = np.ascontiguousarray(q_to_req, np.int32)
+    ql = np.ascontiguousarray(q_to_klen, np.int32)
+    Q, Hq, D = q.shape
+    _, Hkv, page, S = c.shape
+    assert S == fmt.slot_bytes and D == fmt.head_size and Hq % Hkv == 0
+    out = np.zeros((Q, Hq, D), np.float64)
+    lse = np.zeros((Q, Hq), np.float64)
+    lib().orc_attention_lse(ctypes.byref(fmt), _p(q, ctypes.c_float), Q, Hq,
+                            _p(c, ctypes.c_uint8), Hkv, page, _p(bt, ctypes.c_int32),
+                            bt.shape[1], _p(qr, ctypes.c_int32), _p(ql, ctypes.c_int32),
+                            float(sm_scale), _p(out, ctypes.c_double), _p(lse, ctypes.c_double))
+    return out, lse

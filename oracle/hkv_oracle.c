@@ -717,11 +717,15 @@ void orc_dequantize_f64(const orc_format* f, const uint8_t* slots, int64_t num_t
  * first klen_i tokens of request q_to_req[i] (klen <= 0 gives a zero row);
  * query head h reads KV head h / (Hq / Hkv); out = softmax(scale * q.K^T) V
  * with K, V the dequantized cache in the unrotated space.  All in fp64. */
-void orc_attention(const orc_format* f, const float* query, int32_t num_q,
-                   int32_t num_q_heads, const uint8_t* cache, int32_t num_kv_heads,
-                   int32_t page_size, const int32_t* block_table,
-                   int32_t max_pages_per_req, const int32_t* q_to_req,
-                   const int32_t* q_to_klen, double sm_scale, double* out) {
+/* The attention of every query row, and, if lse is not NULL, the natural
+ * log of its softmax denominator, m + log(l) over the row's scores
+ * (sm_scale included); rows with no tokens get -inf. */
+static void attention_rows(const orc_format* f, const float* query, int32_t num_q,
+                           int32_t num_q_heads, const uint8_t* cache, int32_t num_kv_heads,
+                           int32_t page_size, const int32_t* block_table,
+                           int32_t max_pages_per_req, const int32_t* q_to_req,
+                           const int32_t* q_to_klen, double sm_scale, double* out,
+                           double* lse) {
   const int32_t d = f->head_size;
   const int32_t group = num_q_heads / num_kv_heads;
   float* sgn = (float*)malloc(sizeof(float) * (size_t)d);
@@ -731,6 +735,8 @@ void orc_attention(const orc_format* f, const float* query, int32_t num_q,
   uint8_t* codes = (uint8_t*)malloc((size_t)d);
   orc_signs(d, sgn);
   memset(out, 0, sizeof(double) * (size_t)num_q * (size_t)num_q_heads * (size_t)d);
+  if (lse)
+    for (int64_t r = 0; r < (int64_t)num_q * num_q_heads; ++r) lse[r] = -INFINITY;
   for (int32_t i = 0; i < num_q; ++i) {
     const int32_t klen = q_to_klen[i];
     if (klen <= 0) continue;
@@ -762,6 +768,7 @@ void orc_attention(const orc_format* f, const float* query, int32_t num_q,
           l += sg[t];
         }
         for (int32_t t = 0; t < klen; ++t) sg[t] /= l;
+        if (lse) lse[(int64_t)i * num_q_heads + kvh * group + g] = m + log(l);
       }
       /* weighted sum of V */
       memset(acc, 0, sizeof(double) * (size_t)d * (size_t)group);
@@ -787,4 +794,22 @@ void orc_attention(const orc_format* f, const float* query, int32_t num_q,
   free(vec);
   free(acc);
   free(codes);
+}
+
+void orc_attention(const orc_format* f, const float* query, int32_t num_q,
+                   int32_t num_q_heads, const uint8_t* cache, int32_t num_kv_heads,
+                   int32_t page_size, const int32_t* block_table,
+                   int32_t max_pages_per_req, const int32_t* q_to_req,
+                   const int32_t* q_to_klen, double sm_scale, double* out) {
+  attention_rows(f, query, num_q, num_q_heads, cache, num_kv_heads, page_size, block_table,
+                 max_pages_per_req, q_to_req, q_to_klen, sm_scale, out, NULL);
+}
+
+void orc_attention_lse(const orc_format* f, const float* query, int32_t num_q,
+                       int32_t num_q_heads, const uint8_t* cache, int32_t num_kv_heads,
+                       int32_t page_size, const int32_t* block_table,
+                       int32_t max_pages_per_req, const int32_t* q_to_req,
+                       const int32_t* q_to_klen, double sm_scale, double* out, double* lse) {
+  attention_rows(f, query, num_q, num_q_heads, cache, num_kv_heads, page_size, block_table,
+                 max_pages_per_req, q_to_req, q_to_klen, sm_scale, out, lse);
 }

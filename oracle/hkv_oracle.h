@@ -130,6 +130,17 @@ void orc_attention(const orc_format* f, const float* query, int32_t num_q,
                    const int32_t* q_to_req, const int32_t* q_to_klen,
                    double sm_scale, double* out);
 
+/* orc_attention plus lse (Q, Hq) fp64: the natural log of each row's softmax
+ * denominator, m + log(sum exp(s - m)) over its scaled scores, -inf for a row
+ * with no tokens.  Attention over disjoint token ranges merges exactly:
+ * out = sum_k exp(lse_k - lse) out_k with lse = log sum_k exp(lse_k). */
+void orc_attention_lse(const orc_format* f, const float* query, int32_t num_q,
+                       int32_t num_q_heads, const uint8_t* cache,
+                       int32_t num_kv_heads, int32_t page_size,
+                       const int32_t* block_table, int32_t max_pages_per_req,
+                       const int32_t* q_to_req, const int32_t* q_to_klen,
+                       double sm_scale, double* out, double* lse);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,12 @@ static int run_format(const char* dtype, int32_t d, int32_t rope) {
   orc_attention(&f, q, nq, HQ, cache, H, PS, bt, 8, q_to_req, q_to_klen, 1.0 / sqrt((double)d), out);
   int bad = 0;
   for (int32_t i = 0; i < nq * HQ * d; ++i) bad |= !isfinite(out[i]);
+  double lse[3 * HQ];
+  orc_attention_lse(&f, q, nq, HQ, cache, H, PS, bt, 8, q_to_req, q_to_klen,
+                    1.0 / sqrt((double)d), out, lse);
+  for (int32_t i = 0; i < nq * HQ * d; ++i) bad |= !isfinite(out[i]);
+  for (int32_t i = 0; i < 2 * HQ; ++i) bad |= !isfinite(lse[i]); /* klen T and 1 */
+  for (int32_t i = 2 * HQ; i < 3 * HQ; ++i) bad |= !(isinf(lse[i]) && lse[i] < 0); /* klen 0 */
   for (int64_t i = 0; i < T * H * d; ++i) bad |= !isfinite(kd[i]) || !isfinite(vd64[i]);
   free(k), free(v), free(slots), free(kd), free(vd), free(kd64), free(vd64), free(cache), free(q),
       free(out);

@@ -133,3 +133,54 @@ def test_rotated_space_evaluation_agrees(dtype, D, R):
         o_rot = p @ vr[:, h // G].astype(np.float64)
         o = O.fwht(o_rot, f.v_block) * s
         np.testing.assert_allclose(out[0, h], o, rtol=0, atol=1e-10)
+
+
+def test_attention_lse_is_log_sum_exp_and_leaves_output_alone():
+    # lse against scipy's logsumexp of the fp64 scores on the oracle's own
+    # dequantized cache; the output equals attention() bit for bit.
+    from scipy.special import logsumexp
+    lens = [45, 16]
+    Hq, Hkv, D = 6, 2, 128
+    f, slots, cache, bt = _setup("q8_0", D, 0, lens, Hq, Hkv, seed=10)
+    kd, _ = O.dequantize_f64(f, slots)
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((4, Hq, D)).astype(np.float32)
+    qr = np.array([0, 0, 1, 1], np.int32)
+    ql = np.array([45, 17, 0, 16], np.int32)
+    scale = 0.11
+    out, lse = O.attention_lse(f, q, cache, bt, qr, ql, scale)
+    assert np.array_equal(out, O.attention(f, q, cache, bt, qr, ql, scale))
+    starts = [0, 45]
+    G = Hq // Hkv
+    for i in range(4):
+        for h in range(Hq):
+            if ql[i] <= 0:
+                assert lse[i, h] == -np.inf and np.all(out[i, h] == 0)
+                continue
+            k = kd[starts[qr[i]]:starts[qr[i]] + ql[i], h // G]
+            s = k @ q[i, h].astype(np.float64) * scale
+            np.testing.assert_allclose(lse[i, h], logsumexp(s), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype,D,R", FORMATS[:3])
+def test_attention_token_ranges_merge_to_whole(dtype, D, R):
+    # Attention over page-aligned token ranges (a shifted block table and the
+    # range's length) merged with the lse weights gives the whole-range row.
+    lens = [150]
+    Hq, Hkv, P = 4, 2, 16
+    f, slots, cache, bt = _setup(dtype, D, R, lens, Hq, Hkv, page=P, seed=12)
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    L, scale = 150, 1.0 / np.sqrt(D)
+    whole = O.attention(f, q, cache, bt, np.zeros(1, np.int32), np.array([L], np.int32), scale)
+    cuts = [0, 3, 4, 8, 10]                  # page boundaries; last range ragged
+    outs, lses = [], []
+    for p0, p1 in zip(cuts[:-1], cuts[1:]):
+        n = min(L, p1 * P) - p0 * P
+        o, s = O.attention_lse(f, q, cache, np.ascontiguousarray(bt[:, p0:]),
+                               np.zeros(1, np.int32), np.array([n], np.int32), scale)
+        outs.append(o)
+        lses.append(s)
+    lse = np.logaddexp.reduce(np.stack(lses), axis=0)
+    merged = sum(np.exp(s - lse)[..., None] * o for o, s in zip(outs, lses))
+    np.testing.assert_allclose(merged, whole, rtol=0, atol=1e-12)
