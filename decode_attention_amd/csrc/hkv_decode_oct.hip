@@ -33,8 +33,13 @@
 //    mode: one product per plane, 2^8 hi + mid joined the same way.  Each
 //    block's int32 result is scaled by the token's fp16 block scale.
 //  * P.V on v_mfma_f32_16x16x32_f16: B = the codebook value as an exact fp16
-//    (the biased byte LUT[c] + 128 under an 0x64 high byte is 1152 + LUT[c]),
-//    so no residual is needed on this side; the token's V scale multiplies p
+//    (4-bit: the biased byte LUT[c] + 128 under an 0x64 high byte reads
+//    1152 + LUT[c], and one packed subtraction leaves LUT[c]; 3-bit: the low
+//    and high bytes of fp16(LUT[c]) looked up from two tables), so no
+//    residual is needed on this side.  The values enter unbiased: a bias
+//    left in them would grow the accumulators by a factor of ~1152 / |LUT|
+//    and cost ~8 bits of the output (relative to the row's largest value)
+//    to the accumulators' rounding.  The token's V scale multiplies p
 //    in the A operand, fp16(p s) plus its residual x 2^12, in one of two row
 //    modes: with 8 query rows the residual takes A rows 8-15 (one MFMA per 32
 //    tokens); with 16 rows it takes the other half of the K dimension: a
@@ -143,7 +148,6 @@ constexpr uint32_t kK4[4] = {lut_word(kLut4, 0, 0), lut_word(kLut4, 1, 0), lut_w
 constexpr uint32_t kK3[2] = {lut_word(kLut3, 0, 0), lut_word(kLut3, 1, 0)};
 constexpr uint32_t kV4[4] = {lut_word(kLut4, 0, 128), lut_word(kLut4, 1, 128),
                              lut_word(kLut4, 2, 128), lut_word(kLut4, 3, 128)};
-constexpr uint32_t kV3[2] = {lut_word(kLut3, 0, 128), lut_word(kLut3, 1, 128)};
 
 // The 3-bit codebook as fp16 bit patterns, low bytes and high bytes, entries
 // 4 i .. 4 i + 3 in word i (one v_perm_b32 lookup each for four codes).
@@ -162,6 +166,23 @@ constexpr uint32_t half_byte_word(int i, int byte) {
 }
 constexpr uint32_t kH3Lo[2] = {half_byte_word(0, 0), half_byte_word(1, 0)};
 constexpr uint32_t kH3Hi[2] = {half_byte_word(0, 1), half_byte_word(1, 1)};
+// High bytes of fp16(LUT x 2^-12): the exponent field 12 lower (every
+// entry stays normal, |LUT| >= 14); the low bytes are those of kH3Lo.
+constexpr uint32_t half_hi_scaled_word(int i) {
+  uint32_t w = 0;
+  for (int k = 0; k < 4; ++k) w |= (((half_bits_int(kLut3[4 * i + k]) - (12u << 10)) >> 8) & 255u) << (8 * k);
+  return w;
+}
+constexpr uint32_t kH3Hs[2] = {half_hi_scaled_word(0), half_hi_scaled_word(1)};
+static_assert(half_bits_int(14) - (12u << 10) == 0x1B00u, "fp16 bits of 14 x 2^-12");
+
+// fp16 values of the 3-bit codes in the four bytes of sel: the halves of
+// codes 0, 1 in .x and of codes 2, 3 in .y.
+__device__ __forceinline__ uint2 lut3_half(uint32_t sel, uint32_t hi0, uint32_t hi1) {
+  const uint32_t lo = __builtin_amdgcn_perm(kH3Lo[1], kH3Lo[0], sel);
+  const uint32_t hi = __builtin_amdgcn_perm(hi1, hi0, sel);
+  return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+}
 static_assert(half_bits_int(127) == 0x57F0u && half_bits_int(-14) == 0xCB00u, "fp16 bits");
 
 // 0xFF in each byte whose bit 7 is set in y, else 0x00 (v_perm_b32
@@ -380,9 +401,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   float4_t o[kAcc];
 #pragma unroll
   for (int b = 0; b < kAcc; ++b) o[b] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  // sps: running sum of the P.V A operand's p s over this lane's tokens (the
-  // values enter biased by 1152; the bias is removed at the end with it)
-  float m_run = -INFINITY, l_run = 0.0f, sps = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
 
   if (has_work) {
     // Scores of one tile (before masking) from its registers; the tile goes
@@ -536,7 +555,6 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
         const float m_new = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
         l_run *= alpha;
-        sps *= alpha;
         float al[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, kK16 ? 4 * g + i : (4 * g + i) & 7, kWave);
@@ -559,12 +577,10 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
         const float p = __builtin_amdgcn_exp2f(s[i] - m_ref - 6.0f);  // p / 64
         l_run += p;
         pv[i] = p * h2f((uint16_t)((vw[i] >> kVsh) & 0xffffu));
-        sps += pv[i];
       }
       // The leading fp16 parts come from one conversion instruction and the
       // residuals are taken against exactly those values, so that the matrix
-      // cores see p s to 2^-21 (the 1152 bias of the values multiplies any
-      // gap between the two parts).
+      // cores see p s to 2^-21.
       _Float16 h[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -613,12 +629,17 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     auto stage_p = [&](const AOps& A, int buf, int w0, int nw) {
       const uint32_t* va = &L.u.tt[wave][buf][0][0][4 * g];
       const uint32_t* vb = &L.u.tt[wave][buf][1][0][4 * g];
-      // Biased codebook bytes of four codes -> fp16 pairs (1024 + byte).
+      // Biased codebook bytes of 2 x four codes -> the exact fp16 values:
+      // 1024 + byte = 1152 + LUT, less 1152.
       auto spread = [&](uint32_t x, uint32_t y) {
-        return (uint4){__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
-                       __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u),
-                       __builtin_amdgcn_perm(0x64646464u, y, 0x04010400u),
-                       __builtin_amdgcn_perm(0x64646464u, y, 0x04030402u)};
+        const uint4 u = {__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
+                         __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u),
+                         __builtin_amdgcn_perm(0x64646464u, y, 0x04010400u),
+                         __builtin_amdgcn_perm(0x64646464u, y, 0x04030402u)};
+        const half8_t c1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
+                               (_Float16)-1152.0f, (_Float16)-1152.0f, (_Float16)-1152.0f,
+                               (_Float16)-1152.0f, (_Float16)-1152.0f};
+        return __builtin_bit_cast(half8_t, u) + c1152;
       };
       // Byte (n & 3) of a word of tokens 4g..4g+3.
       auto gather = [&](const uint4& W) {
@@ -634,8 +655,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
           const uint32_t ha = lut16((ga >> 4) & 0x07070707u, byte_sign_mask(ga), kV4[0], kV4[1], kV4[2], kV4[3]);
           const uint32_t lb = lut16(gb & 0x07070707u, byte_sign_mask(gb << 4), kV4[0], kV4[1], kV4[2], kV4[3]);
           const uint32_t hb = lut16((gb >> 4) & 0x07070707u, byte_sign_mask(gb), kV4[0], kV4[1], kV4[2], kV4[3]);
-          const half8_t lo = __builtin_bit_cast(half8_t, spread(la, lb));
-          const half8_t hi = __builtin_bit_cast(half8_t, spread(ha, hb));
+          const half8_t lo = spread(la, lb);
+          const half8_t hi = spread(ha, hb);
           mma(A, lo, o[2 * W]);
           mma(A, hi, o[2 * W + 1]);
         }
@@ -653,9 +674,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
             const int sh = 4 * h + vi;
             const uint32_t sa_ = ((gla >> (2 * vi)) & 0x03030303u) | (((gha >> sh) << 2) & 0x04040404u);
             const uint32_t sb_ = ((glb >> (2 * vi)) & 0x03030303u) | (((ghb >> sh) << 2) & 0x04040404u);
-            const uint32_t la = __builtin_amdgcn_perm(kV3[1], kV3[0], sa_);
-            const uint32_t lb = __builtin_amdgcn_perm(kV3[1], kV3[0], sb_);
-            const half8_t vv = __builtin_bit_cast(half8_t, spread(la, lb));
+            const uint2 ha = lut3_half(sa_, kH3Hi[0], kH3Hi[1]);
+            const uint2 hb = lut3_half(sb_, kH3Hi[0], kH3Hi[1]);
+            const half8_t vv = __builtin_bit_cast(half8_t, make_uint4(ha.x, ha.y, hb.x, hb.y));
             mma(A, vv, o[m]);
           }
         }
@@ -715,16 +736,13 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   // ---- merge the waves ----------------------------------------------------
   float lsum = l_run + __shfl_xor(l_run, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
-  // the row's sum of p s (lanes n and n + 8 of the 8-row mode hold the same)
-  float ssum = sps + __shfl_xor(sps, 16, kWave);
-  ssum += __shfl_xor(ssum, 32, kWave);
   if (g == 0 && n < RM) {
     L.mlw[wave][n][0] = m_run;
     L.mlw[wave][n][1] = lsum * 64.0f;  // p was kept as p / 64
   }
   __syncthreads();
   if (kK16 || g < 2) {
-    float fw[4], bias[4];
+    float fw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;
@@ -733,13 +751,12 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
       const float mw = L.mlw[wave][r][0];
       fw[i] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-      bias[i] = 1152.0f * __shfl(ssum, r, kWave);
     }
 #pragma unroll
     for (int b = 0; b < kAcc; ++b) {
       const int d = F::kV3 ? 16 * b + n : 32 * (b >> 1) + 8 * (n >> 2) + (n & 3) + 4 * (b & 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = (o[b][i] - bias[i]) * fw[i];
+      for (int i = 0; i < 4; ++i) L.u.ob[wave][4 * g + i][d] = o[b][i] * fw[i];
     }
   }
   __syncthreads();
@@ -784,10 +801,9 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 //  * P.V on v_mfma_f32_32x32x16_f16 as O^T = V^T P^T (rows = dims, columns =
 //    query rows), 8 tokens per step: a lane's k-slots are its 4 tokens'
 //    fp16(p s) and their residuals x 2^12, against the tokens' values and
-//    values x 2^-12.  The values enter biased, as the fp16 1024 + (LUT[c] +
-//    128) (and that x 2^-12, the same byte under an exponent 2^-2), so each
-//    takes one v_perm_b32; the bias is removed at the end with the running
-//    sum of p s per row.
+//    values x 2^-12, exact fp16 assembled from three byte tables (the low
+//    bytes, the high bytes, the high bytes of the value x 2^-12) with two
+//    v_perm_b32 interleaves per pair of codes and part.
 //  * V dims: tile (b, i) of 32 dims has row a = 4 m' + j holding dim
 //    16 (8 b + m') + 4 i + j; a lane gathers byte j of low-plane word 8 b + m'
 //    of its 4 tokens once and takes the codes of all four i from it.
@@ -935,7 +951,7 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
   for (int b = 0; b < 8; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[b][i] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f, sps = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
 
   if (has_work) {
     uint32_t* const tw = &L.u.s.tt[wave][0][0][0];
@@ -1032,7 +1048,6 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
         const float m_new = fmaxf(m_run, mt);
         const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
         l_run *= alpha;
-        sps *= alpha;
 #pragma unroll
         for (int b = 0; b < 8; ++b)
 #pragma unroll
@@ -1052,11 +1067,9 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
           const float p = __builtin_amdgcn_exp2f(fmaf(s[4 * j + i], qs, -m6));  // p / 64
           l_run += p;
           pv[i] = p * vv[i];
-          sps += pv[i];
         }
         // The leading fp16 parts come from one conversion instruction, so the
-        // residuals are taken against exactly the values the product sees
-        // (the bias correction needs their sum to be the sum of p s).
+        // residuals are taken against exactly the values the product sees.
         const half2_t h01 = __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]);
         const half2_t h23 = __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]);
         const _Float16 hp[4] = {(_Float16)h01[0], (_Float16)h01[1], (_Float16)h23[0], (_Float16)h23[1]};
@@ -1082,11 +1095,13 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t sel = ((gl >> (2 * i)) & 0x03030303u) | (((gh >> i) << 2) & 0x04040404u);
-            const uint32_t x = __builtin_amdgcn_perm(kV3[1], kV3[0], sel);
-            const uint4 A = {__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
-                             __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u),
-                             __builtin_amdgcn_perm(0x34343434u, x, 0x04010400u),
-                             __builtin_amdgcn_perm(0x34343434u, x, 0x04030402u)};
+            const uint32_t xl = __builtin_amdgcn_perm(kH3Lo[1], kH3Lo[0], sel);
+            const uint32_t xh = __builtin_amdgcn_perm(kH3Hi[1], kH3Hi[0], sel);
+            const uint32_t xs = __builtin_amdgcn_perm(kH3Hs[1], kH3Hs[0], sel);
+            const uint4 A = {__builtin_amdgcn_perm(xh, xl, 0x05010400u),
+                             __builtin_amdgcn_perm(xh, xl, 0x07030602u),
+                             __builtin_amdgcn_perm(xs, xl, 0x05010400u),
+                             __builtin_amdgcn_perm(xs, xl, 0x07030602u)};
             o[4 * b + i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                 __builtin_bit_cast(half8_t, A), P[j], o[4 * b + i], 0, 0, 0);
           }
@@ -1100,13 +1115,11 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
   // ---- merge the waves ----------------------------------------------------
   // This lane: row n, values of dims 16 (8 b + m') + 4 i + j for tile 4 b + i,
   // register 4 jj + ii, with 4 m' + j = 8 jj + 4 h + ii.
-  float lsum, psum;
+  float lsum;
   {
-    const uint32_t lu = __float_as_uint(l_run), pu = __float_as_uint(sps);
+    const uint32_t lu = __float_as_uint(l_run);
     const auto ls = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
-    const auto pss = __builtin_amdgcn_permlane32_swap(pu, pu, false, false);
     lsum = __uint_as_float(ls[0]) + __uint_as_float(ls[1]);
-    psum = __uint_as_float(pss[0]) + __uint_as_float(pss[1]);
   }
   if (h == 0) {
     L.mlw[wave][n][0] = m_run;
@@ -1120,14 +1133,13 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
     for (int w = 0; w < W; ++w) M = fmaxf(M, L.mlw[w][n][0]);
     fw = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
   }
-  const float bias = 1152.0f * psum;  // the values entered as 1152 + LUT[c]
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     if (b) __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) L.u.ob[wave][h][n][16 * i + k] = (o[4 * b + i][k] - bias) * fw;
+      for (int k = 0; k < 16; ++k) L.u.ob[wave][h][n][16 * i + k] = o[4 * b + i][k] * fw;
     __syncthreads();
     for (int idx = threadIdx.x; idx < a.rows * 128; idx += blockDim.x) {
       const int r = idx >> 7, dd = idx & 127;
