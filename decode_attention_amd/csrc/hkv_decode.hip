@@ -492,15 +492,19 @@ hipError_t launch_generic_e(const DevFmt& f, const DecArgs& a, int R, dim3 grid,
 
 bool q4_mfma_supported(const DevFmt& f, int rows);
 hipError_t launch_decode_q4_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
+bool q4w_mfma_supported(const DevFmt& f, int rows);
+hipError_t launch_decode_q4w(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
 bool q8_mfma_supported(const DevFmt& f, int rows);
 hipError_t launch_decode_q8_mfma(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
 int oct_mfma_rows(const DevFmt& f, int rows);
 hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s);
 
 // Decode kernels: 0 the generic VALU kernel (every format), 1 the Q4_0 MFMA
-// kernel (head size 256, 8 rows), 2 the Octave MFMA kernel (k3v4 at head
-// size 128, k3v3 compact at 256; 8 or 16 rows).
-constexpr int kKernelGeneric = 0, kKernelQ4 = 1, kKernelOctK3v4 = 2, kKernelQ8 = 3;
+// kernel (head size 256, 8 rows), 2 the Octave MFMA kernels (8, 16 or 32
+// rows), 3 the Q8_0 MFMA kernel (head size 256, 8 rows), 4 the Q4_0 window
+// kernel (head size 256, 9 to 32 rows in one pass).
+constexpr int kKernelGeneric = 0, kKernelQ4 = 1, kKernelOctK3v4 = 2, kKernelQ8 = 3,
+              kKernelQ4W = 4;
 
 constexpr int64_t kTargetSplitsWgs = 512;
 constexpr int kMaxRows = 32;          // query rows per KV head in one pass
@@ -519,14 +523,15 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   q.num_groups = num_queries / queries_per_seq;
   q.nsub = 1;
   auto mfma_kernel = [&](int rows) {
-    return q4_mfma_supported(f, rows)   ? kKernelQ4
-           : q8_mfma_supported(f, rows) ? kKernelQ8
+    return q4_mfma_supported(f, rows)    ? kKernelQ4
+           : q4w_mfma_supported(f, rows) ? kKernelQ4W
+           : q8_mfma_supported(f, rows)  ? kKernelQ8
            : oct_mfma_rows(f, rows) > 0 ? kKernelOctK3v4
                                         : kKernelGeneric;
   };
   q.kernel = mfma_kernel(q.rows);
-  // More rows than one kernel pass takes (the matrix-core kernels: 8 or 16
-  // query rows per KV head; the generic kernel: 32): the queries of a
+  // More rows than one kernel pass takes (the matrix-core kernels: 8, 16 or
+  // 32 query rows per KV head; the generic kernel: 32): the queries of a
   // sequence are split into the largest sub-groups that fit, preferring a
   // matrix-core kernel; each sub-group streams the sequence's K/V through its
   // own workgroups.
@@ -550,8 +555,9 @@ bool plan_decode(const DevFmt& f, int num_queries, int num_q_heads, int num_kv_h
   }
   if (q.rows > kMaxRows) return false;
   q.rows_pad = q.kernel == kKernelQ4 || q.kernel == kKernelQ8 ? 8
-               : q.kernel == kKernelOctK3v4 ? oct_mfma_rows(f, q.rows)
-                                            : round_rows(q.rows);
+               : q.kernel == kKernelQ4W                       ? 32
+               : q.kernel == kKernelOctK3v4                   ? oct_mfma_rows(f, q.rows)
+                                                              : round_rows(q.rows);
   // Split size: enough splits that (sequence group, KV head, split) fills the
   // chip with one resident round of workgroups (the MFMA kernel: one
   // 8-wave workgroup per CU; the generic kernel: two 4-wave ones), in whole
@@ -621,6 +627,8 @@ hipError_t launch_decode(const DevFmt& f, const DecodePlan& p, const void* query
   hipError_t e;
   if (p.kernel == kKernelQ4) {
     e = launch_decode_q4_mfma(f, a, grid, s);
+  } else if (p.kernel == kKernelQ4W) {
+    e = launch_decode_q4w(f, a, grid, s);
   } else if (p.kernel == kKernelQ8) {
     e = launch_decode_q8_mfma(f, a, grid, s);
   } else if (p.kernel == kKernelOctK3v4) {

@@ -328,13 +328,15 @@ def test_decode_edge_lengths(dtype, D, R, Hq, Hkv):
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(32, 4), (24, 4), (17, 1)])
-def test_decode_compact_one_pass_edge_lengths(Hq, Hkv):
-    """The one-pass kernel for 17-32 query rows per KV head (Octave k3v3
-    compact): four queries per sequence (causal: klen L-3 .. L), so with
-    queries_per_seq 4 a pass holds 4 G rows (G = 8: all 32 rows live; G = 6:
-    24 rows and 8 padding rows); lengths at the tile, page and split edges;
-    a query with no tokens and one with a negative length give zero rows."""
-    D, R, P = 256, 64, 16
+@pytest.mark.parametrize("dtype,R", [("octave_k3v3_compact", 64), ("q4_0", 0)])
+def test_decode_one_pass_window_edge_lengths(dtype, R, Hq, Hkv):
+    """The one-pass kernels for up to 32 query rows per KV head (Octave k3v3
+    compact from 17 rows, Q4_0 from 9): four queries per sequence (causal:
+    klen L-3 .. L), so with queries_per_seq 4 a pass holds 4 G rows (G = 8:
+    all 32 rows live; G = 6: 24 rows and 8 padding rows; G = 17: one query
+    per pass, 17 rows); lengths at the tile, page and split edges; a query
+    with no tokens and one with a negative length give zero rows."""
+    D, P = 256, 16
     lens = [4, 5, 16, 19, 20, 35, 1027, 2051, 2500, 7]
     rng = np.random.default_rng(Hq * 7 + Hkv)
     T = sum(lens)
@@ -351,8 +353,8 @@ def test_decode_compact_one_pass_edge_lengths(Hq, Hkv):
         pos = np.arange(L)
         sm[t0:t0 + L] = bt[b, pos // P].astype(np.int64) * P + pos % P
         t0 += L
-    f = hkv.format_init("octave_k3v3_compact", D, R, P)
-    fo = O.format_init("octave_k3v3_compact", D, R)
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
     cache = hkv.new_cache(f, sum(pages), Hkv, DEV)
     hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
                         torch.from_numpy(sm).to(DEV), cache)
@@ -374,7 +376,7 @@ def test_decode_compact_one_pass_edge_lengths(Hq, Hkv):
                                torch.from_numpy(q_to_klen).to(DEV), int(q_to_klen.max()), 4,
                                scale).cpu().numpy()
     ref = O.attention(fo, q, ref_cache, bt, q_to_req, q_to_klen, scale)
-    _assert_close(got, ref, f"compact Hq={Hq} Hkv={Hkv}")
+    _assert_close(got, ref, f"{dtype} Hq={Hq} Hkv={Hkv}")
     assert np.all(got[2] == 0) and np.all(got[-4] == 0)
 
 
@@ -474,6 +476,7 @@ def test_decode_full_size_wider_formats(ci, seqs):
 
 @pytest.mark.parametrize("P", [32, 64, 24, 1])
 @pytest.mark.parametrize("dtype,D,R,Hq,Hkv,qps", [("q4_0", 256, 0, 16, 2, 1),
+                                                  ("q4_0", 256, 0, 16, 2, 4),
                                                   ("q8_0", 256, 0, 16, 2, 1),
                                                   ("octave_k3v4", 128, 64, 32, 8, 1),
                                                   ("octave_k3v3", 128, 64, 16, 4, 4),
@@ -521,6 +524,7 @@ def test_decode_page_sizes(P, dtype, D, R, Hq, Hkv, qps):
 
 
 @pytest.mark.parametrize("dtype,D,R,Hq,Hkv,qps,num_pages", [("q4_0", 256, 0, 16, 2, 1, 600_000),
+                                                            ("q4_0", 256, 0, 16, 2, 4, 600_000),
                                                             ("q8_0", 256, 0, 16, 2, 1, 300_000),
                                                             ("octave_k3v3_compact", 256, 64, 32, 4, 4, 350_000),
                                                             ("octave_k3v4", 128, 64, 32, 8, 1, 300_000)])

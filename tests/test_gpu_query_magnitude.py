@@ -6,9 +6,9 @@ reference_attention), so the tolerance holds whatever the query's scale.
 Queries x30 and x100 put logits in the hundreds, where the softmax is nearly
 one-hot and a score error of 1e-3 already moves the output; one pass mixes
 x0.01 and x100 rows, so each row's query operand must follow its own scale.
-Every decode kernel is covered: Q4_0 and Q8_0 on the matrix cores, the
-Octave kernel in its 8-row and 16-row modes, the one-pass 32-row kernel, and
-the generic kernel.
+Every decode kernel is covered: Q4_0 (8 rows, and the window kernel with
+16 and 32) and Q8_0 on the matrix cores, the Octave kernel in its 8-row and
+16-row modes, the one-pass 32-row kernel, and the generic kernel.
 """
 import numpy as np
 import pytest
@@ -25,6 +25,8 @@ DEV = "cuda:0"
 
 KERNELS = [  # dtype, D, rope_dim, Hq, Hkv, queries_per_seq
     ("q4_0", 256, 0, 16, 2, 1),                   # Q4_0 matrix-core kernel, 8 rows
+    ("q4_0", 256, 0, 16, 2, 4),                   # Q4_0 window kernel, 32 rows
+    ("q4_0", 256, 0, 16, 2, 2),                   # Q4_0 window kernel, 16 rows
     ("q8_0", 256, 0, 16, 2, 1),                   # Q8_0 matrix-core kernel, 8 rows
     ("octave_k3v4", 128, 64, 32, 8, 1),           # Octave kernel, 8-row mode (4 live rows)
     ("octave_k3v4", 128, 64, 32, 4, 2),           # Octave kernel, 16-row mode

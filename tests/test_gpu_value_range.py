@@ -25,6 +25,7 @@ DEV = "cuda:0"
 
 KERNELS = [  # dtype, D, rope_dim, Hq, Hkv, queries_per_seq
     ("q4_0", 256, 0, 16, 2, 1),
+    ("q4_0", 256, 0, 16, 2, 4),
     ("q8_0", 256, 0, 16, 2, 1),
     ("octave_k3v4", 128, 64, 32, 8, 1),
     ("octave_k3v4", 128, 64, 32, 4, 2),
