@@ -204,6 +204,13 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4w32_kernel(DevFmt
   __syncthreads();
   // (kept positive so that a masked score, -inf, stays -inf through the fma)
   const float qs = fmaxf(L.qsc[n], 0x1p-126f);
+  // Nibble masks kept in VGPRs so that mask-and-bias fuses into v_and_or_b32
+  // (whose third operand, the fp16 exponent bias, then comes from an SGPR).
+  uint32_t m000f, m00f0, m0f, mf0;
+  asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m000f));
+  asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(m00f0));
+  asm volatile("v_mov_b32 %0, 0x0f0f0f0f" : "=v"(m0f));
+  asm volatile("v_mov_b32 %0, 0xf0f0f0f0" : "=v"(mf0));
 
   f32x16 o[kNB];  // tile 2 bp + half: V blocks 2 bp, 2 bp + 1, low or high nibbles
 #pragma unroll
@@ -267,12 +274,12 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4w32_kernel(DevFmt
           for (int sl = 0; sl < 2; ++sl) {
             // word 2 sl + h of block b: dims 8 (2 sl + h) .. + 7 as exact fp16
             const uint32_t x = tk[(4 * b + 2 * sl + h) * kTS], x8 = x >> 8;
-            const half2_t h0 = __builtin_bit_cast(half2_t, (x & 0x000F000Fu) | 0x64006400u) + c1032;
+            const half2_t h0 = __builtin_bit_cast(half2_t, (x & m000f) | 0x64006400u) + c1032;
             const half2_t h1 = __builtin_elementwise_fma(
-                __builtin_bit_cast(half2_t, (x & 0x00F000F0u) | 0x64006400u), c16, c72);
-            const half2_t h2 = __builtin_bit_cast(half2_t, (x8 & 0x000F000Fu) | 0x64006400u) + c1032;
+                __builtin_bit_cast(half2_t, (x & m00f0) | 0x64006400u), c16, c72);
+            const half2_t h2 = __builtin_bit_cast(half2_t, (x8 & m000f) | 0x64006400u) + c1032;
             const half2_t h3 = __builtin_elementwise_fma(
-                __builtin_bit_cast(half2_t, (x8 & 0x00F000F0u) | 0x64006400u), c16, c72);
+                __builtin_bit_cast(half2_t, (x8 & m00f0) | 0x64006400u), c16, c72);
             const half8_t A = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
             const half8_t bh = *(const half8_t*)&L.u.s.qB[0][b][n][16 * sl + 8 * h];
             const half8_t bl = *(const half8_t*)&L.u.s.qB[1][b][n][16 * sl + 8 * h];
@@ -358,8 +365,8 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_q4w32_kernel(DevFmt
           const uint4 Wd = lds_u4(vw + (j >> 1) * (kCodeWords * kTS) + 8 * (j & 1));
           const uint32_t x01 = __builtin_amdgcn_perm(Wd.y, Wd.x, vsel);
           const uint32_t x23 = __builtin_amdgcn_perm(Wd.w, Wd.z, vsel);
-          const uint2 lw = {(x01 & 0x0F0F0F0Fu) | 0x64006400u, (x23 & 0x0F0F0F0Fu) | 0x64006400u};
-          const uint2 hw = {(x01 & 0xF0F0F0F0u) | 0x64006400u, (x23 & 0xF0F0F0F0u) | 0x64006400u};
+          const uint2 lw = {(x01 & m0f) | 0x64006400u, (x23 & m0f) | 0x64006400u};
+          const uint2 hw = {(x01 & mf0) | 0x64006400u, (x23 & mf0) | 0x64006400u};
           const half4_t cl = __builtin_bit_cast(half4_t, lw) + c1032;  // c - 8, low nibbles
           const half4_t ch = __builtin_elementwise_fma(__builtin_bit_cast(half4_t, hw), c16, c72);
           const half4_t dv = *(const half4_t*)(vs + (j >> 1) * (2 * kNB * kT) + 8 * (j & 1));
