@@ -98,9 +98,9 @@ def copy_calibration():
 # Sources of the decode kernels a cache format runs on: the format's
 # split-K kernel, the planner, merge and generic kernel, and their headers.
 DECODE_SOURCES = {
-    "q4_0": "hkv_decode_q4.hip",
-    "q8_0": "hkv_decode_q8.hip",
-    "octave": "hkv_decode_oct.hip",
+    "q4_0": ("hkv_decode_q4.hip", "hkv_decode_q4w.hip"),
+    "q8_0": ("hkv_decode_q8.hip",),
+    "octave": ("hkv_decode_oct.hip",),
 }
 SHARED_SOURCES = ("hkv_decode.hip", "hkv_decode_common.h", "hkv_device.h", "hkv_internal.h")
 
@@ -113,7 +113,7 @@ def source_hash(cache_dtype=None) -> str:
     names = sorted(os.listdir(d))
     if cache_dtype is not None:
         own = DECODE_SOURCES["octave" if cache_dtype.startswith("octave") else cache_dtype]
-        names = sorted((own,) + SHARED_SOURCES)
+        names = sorted(own + SHARED_SOURCES)
     for n in names:
         with open(os.path.join(d, n), "rb") as f:
             h.update(n.encode() + f.read())
