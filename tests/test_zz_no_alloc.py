@@ -44,6 +44,7 @@ def _within(got, ref, what):
     (9, dict(batch=2, seq_len=5000), dict(batch=1, seq_len=777)),
     (4, dict(batch=4, seq_len=4000, min_len=1000), dict(batch=2, seq_len=700, min_len=300)),
     (5, dict(batch=6, seq_len=3000, min_len=200), dict(batch=2, seq_len=900, min_len=100)),
+    (6, dict(batch=3, seq_len=3000, min_len=800), dict(batch=2, seq_len=700, min_len=200)),
 ])
 def test_noalloc_matches_workspace_entry_point(ci, first, second):
     for sizes in (first, second):
