@@ -309,6 +309,40 @@ def test_fwht_reduces_q4_error_on_outlier_data():
     assert with_rot < 0.7 * without
 
 
+def test_fwht_outlier_error_figures():
+    """The quality figure of the kind the pages report ([M5] row 5: int4
+    relative L2 error 23.3% -> 8.85% and int8 1.68% -> 0.49% with the
+    rotation, on their outlier data), on the config-1 workload (N(0,1) with
+    four channels x20, D = 256, 512 head vectors).  The figures are printed;
+    what is asserted is their structure: the rotation at least halves the
+    error, and with it the outlier data quantize no worse than plain N(0,1)
+    data (the rotation spreads the outliers' energy over the block)."""
+    from decode_attention_amd import workloads as W
+
+    def rel(a, b):
+        return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+    w = W.make_workload(W.CONFIGS[1])
+    x = w.key.astype(np.float32).reshape(-1, 256)
+    g = np.random.default_rng(11).standard_normal(x.shape).astype(np.float32)
+    figs = {}
+    for dt, block, deq in (("q4_0", O.q4_0_block, _q4_dequant),
+                           ("q8_0", O.q8_0_block,
+                            lambda c, d16: c.astype(np.float64) *
+                            float(np.uint16(d16).view(np.float16)))):
+        f = O.format_init(dt, 256)
+        kh, _ = O.dequantize(f, O.quantize(f, x[:, None], x[:, None]))
+        gh, _ = O.dequantize(f, O.quantize(f, g[:, None], g[:, None]))
+        plain = np.concatenate([[deq(*block(r[32 * b:32 * b + 32])) for b in range(8)]
+                                for r in x]).reshape(x.shape)
+        figs[dt] = (rel(kh[:, 0], x), rel(plain, x), rel(gh[:, 0], g))
+        print(f"{dt}: rel-L2 with FWHT {figs[dt][0]:.4f}, without {figs[dt][1]:.4f}, "
+              f"N(0,1) data with FWHT {figs[dt][2]:.4f}")
+    for dt, (wr, wo, gauss) in figs.items():
+        assert wr < 0.5 * wo, dt
+        assert wr <= 1.1 * gauss, dt
+
+
 # ----------------------------------------------------------------- Q8_0 ---
 def _q8_dequant(c, d16):
     return c.astype(np.float64) * float(np.uint16(d16).view(np.float16))
