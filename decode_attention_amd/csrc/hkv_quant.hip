@@ -644,12 +644,13 @@ HKV_FMAC4_SRC_DEF(0x1B, "quad_perm:[3,2,1,0]")
 #undef HKV_FMAC4_DEF
 #undef HKV_FMAC4_SRC_DEF
 
-// fwht_rows16 in the lane order of qrow_elem.
-template <int Q>
+// fwht_rows16 in the lane order of qrow_elem (from stride 2 when the
+// caller has already done the stride-1 stage, kFrom2).
+template <int Q, bool kFrom2 = false>
 __device__ __forceinline__ void fwht_rows16_q(float (&x)[Q][4], int e, float norm) {
   // h = 1, 2: registers
 #pragma unroll
-  for (int h = 1; h <= 2; h <<= 1)
+  for (int h = kFrom2 ? 2 : 1; h <= 2; h <<= 1)
 #pragma unroll
     for (int q = 0; q < Q; ++q)
 #pragma unroll
@@ -781,6 +782,33 @@ __device__ __forceinline__ void widen16(const uint32_t (&r)[Q][F16 ? 2 : 4], flo
   }
 }
 
+// widen16, and for f16 inputs the stride-1 butterfly stage with it: each
+// sum or difference of two halves is one mixed-precision fma (x 1.0), whose
+// single rounding of the exact fp32 sum is the plain stage's (the widening
+// itself is exact).
+template <int Q, bool F16>
+__device__ __forceinline__ void widen16_stage1(const uint32_t (&r)[Q][F16 ? 2 : 4],
+                                               float (&x)[Q][4]) {
+  // (the 1.0 is opaque, so that the fma is not simplified to an add of two
+  // widened values)
+  float one = 1.0f;
+  if (F16) asm volatile("v_mov_b32 %0, 1.0" : "=v"(one));
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    if (F16) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float a = h2f((uint16_t)r[q][p]), b = h2f((uint16_t)(r[q][p] >> 16));
+        x[q][2 * p] = __builtin_fmaf(a, one, b);
+        x[q][2 * p + 1] = __builtin_fmaf(a, one, -b);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[q][i] = __uint_as_float(r[q][i]);
+    }
+  }
+}
+
 constexpr int kRows16MinRows = 4096;  // below this the one-row-per-wave kernel is faster
 
 // rows as for quantize_append_kernel; key/value 8-byte (f16) or 16-byte (f32)
@@ -803,8 +831,8 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
   int64_t sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
   for (;;) {
     float k[Q][4], v[Q][4];
-    widen16<Q, F16>(rk, k);
-    widen16<Q, F16>(rv, v);
+    widen16_stage1<Q, F16>(rk, k);
+    widen16_stage1<Q, F16>(rv, v);
     const int cur = row;
     const int64_t cur_sm = sm;
     base += stride;
@@ -813,8 +841,8 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
       fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * e, rk, rv);
       sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
     }
-    fwht_rows16_q<Q>(k, e, f.k_norm);
-    fwht_rows16_q<Q>(v, e, f.v_norm);
+    fwht_rows16_q<Q, F16>(k, e, f.k_norm);
+    fwht_rows16_q<Q, F16>(v, e, f.v_norm);
     uint32_t wk[Q], wv[Q], sk[Q], sv[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {

@@ -140,6 +140,8 @@ def test_quantize_many_rows(dtype, D, R, in_dtype, misaligned):
     v[9, 2] = 0
     k[11, 1, :32] = -np.abs(k[11, 1, :32]).max()     # max-abs ties inside one block
     k[11, 1, 3] = -k[11, 1, 3]
+    k[13, 0] = (rng.standard_normal(D) * 3e-6).astype(in_dtype)  # fp16 subnormals
+    v[13, 2] = (rng.standard_normal(D) * 3e-6).astype(in_dtype)
     f = hkv.format_init(dtype, D, R, P)
     fo = O.format_init(dtype, D, R)
     pages = (T + P - 1) // P + 2
