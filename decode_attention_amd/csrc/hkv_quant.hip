@@ -942,12 +942,13 @@ __device__ __forceinline__ uint32_t oct_code(const OctTables& T, float z, float*
 }
 
 // fwht_rows16 for a transform block of 64 or 64Q values (the group stages
-// run only below the block).
-template <int Q>
+// run only below the block); from stride 2 when the caller has done the
+// stride-1 stage (kFrom2).
+template <int Q, bool kFrom2 = false>
 __device__ __forceinline__ void fwht_rows16b(float (&x)[Q][4], int block, float norm) {
   const int l = lane_id() & 15;
 #pragma unroll
-  for (int h = 1; h <= 2; h <<= 1)
+  for (int h = kFrom2 ? 2 : 1; h <= 2; h <<= 1)
 #pragma unroll
     for (int q = 0; q < Q; ++q)
 #pragma unroll
@@ -1128,6 +1129,12 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
       const int d = 64 * q + 4 * l + i;
       smk[q][i] = ((f.sign_bits[d >> 5] >> (d & 31)) & 1u) << 31;
     }
+  // the same for fp16 inputs: the sign bits of the two halves of each word
+  uint32_t smh[Q][2];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) smh[q][p] = (smk[q][2 * p] >> 16) | smk[q][2 * p + 1];
   const int kw = f.k_wide / kWave;  // groups of 4-bit K codes
   const int nks = f.num_k_scales;
   const int nsw = (f.slot_bytes - f.off_scales) / 4;
@@ -1137,8 +1144,29 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
   int64_t sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
   for (;;) {
     float k[Q][4], v[Q][4];
-    widen16<Q, F16>(rk, k);
-    widen16<Q, F16>(rv, v);
+    if (F16) {
+      // signs flipped on the halves, then the stride-1 stage with the widening
+      uint32_t sk[Q][R], sv[Q][R];
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int p = 0; p < R; ++p) {
+          sk[q][p] = rk[q][p] ^ smh[q][p & 1];
+          sv[q][p] = rv[q][p] ^ smh[q][p & 1];
+        }
+      widen16_stage1<Q, F16>(sk, k);
+      widen16_stage1<Q, F16>(sv, v);
+    } else {
+      widen16<Q, F16>(rk, k);
+      widen16<Q, F16>(rv, v);
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          k[q][i] = __uint_as_float(__float_as_uint(k[q][i]) ^ smk[q][i]);
+          v[q][i] = __uint_as_float(__float_as_uint(v[q][i]) ^ smk[q][i]);
+        }
+    }
     const int cur = row;
     const int64_t cur_sm = sm;
     base += stride;
@@ -1147,15 +1175,8 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
       fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * (lane & 15), rk, rv);
       sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
     }
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        k[q][i] = __uint_as_float(__float_as_uint(k[q][i]) ^ smk[q][i]);
-        v[q][i] = __uint_as_float(__float_as_uint(v[q][i]) ^ smk[q][i]);
-      }
-    fwht_rows16b<Q>(k, f.k_block, f.k_norm);
-    fwht_rows16b<Q>(v, f.v_block, f.v_norm);
+    fwht_rows16b<Q, F16>(k, f.k_block, f.k_norm);
+    fwht_rows16b<Q, F16>(v, f.v_block, f.v_norm);
     uint32_t ck[Q][4], cv[Q][4], ks[Q];
     if (f.compact) {
       ks[0] = oct_block16<Q, Q, 3>(T, k, 0, ck);
