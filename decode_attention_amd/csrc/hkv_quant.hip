@@ -509,6 +509,63 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_half_kernel(
 // equal those of the kernel above.  A 32-value block is one q of one 8-lane
 // half-row.
 
+// Row cursor of the many-row kernels: a lane group's row r = t H + h (token
+// t, KV head h of H), advanced by the grid stride with two adds and a carry
+// instead of a division by H per step.
+struct RowCursor {
+  int row, tok, head;
+  int dtok, dhead;  // the stride as dtok H + dhead
+  __device__ __forceinline__ void init(int r, int stride, int H) {
+    row = r;
+    tok = r / H;
+    head = r - tok * H;
+    dtok = stride / H;
+    dhead = stride - dtok * H;
+  }
+  __device__ __forceinline__ void advance(int stride, int H) {
+    row += stride;
+    tok += dtok;
+    head += dhead;
+    const bool carry = head >= H;
+    head = carry ? head - H : head;
+    tok += carry ? 1 : 0;
+  }
+};
+
+// How the many-row kernels address a slot (uniform over the launch): with a
+// power-of-two page size, H page_size below 2^24 and H page_size slot_bytes
+// below 2^32, the page and offset of a slot id below 2^32 are a shift and a
+// mask, and the slot's byte offset ((page H + h) page_size + offset)
+// slot_bytes is page (H page_size slot_bytes) + (h page_size + offset)
+// slot_bytes: one 32 x 32 -> 64-bit multiply-add, the second product on the
+// 24-bit multipliers.
+struct SlotAddr {
+  bool fast;
+  int shift;
+  uint32_t page_bytes;
+  __device__ __forceinline__ void init(const DevFmt& f, int H) {
+    const uint32_t ps = (uint32_t)f.page_size;
+    const uint64_t pb = (uint64_t)H * ps * (uint32_t)f.slot_bytes;
+    fast = (ps & (ps - 1)) == 0 && (uint64_t)H * ps < (1u << 24) && pb <= 0xFFFFFFFFull;
+    shift = __builtin_ctz(ps);
+    page_bytes = (uint32_t)pb;
+  }
+  // Byte offset of slot id `slot` (>= 0) of KV head h.
+  __device__ __forceinline__ uint64_t offset(const DevFmt& f, int64_t slot, int h, int H) const {
+    if (fast && (slot >> 32) == 0) {
+      const uint32_t s32 = (uint32_t)slot;
+      uint32_t in_page = (uint32_t)__umul24(
+          (uint32_t)__umul24((uint32_t)h, (uint32_t)f.page_size) + (s32 & ((uint32_t)f.page_size - 1u)),
+          (uint32_t)f.slot_bytes);
+      asm("" : "+v"(in_page));  // a 32-bit value: not re-associated into 64-bit products
+      return (uint64_t)(s32 >> shift) * (uint64_t)page_bytes + (uint64_t)in_page;
+    }
+    const int64_t page = slot / f.page_size;
+    const int off = (int)(slot % f.page_size);
+    return (uint64_t)(((page * H + h) * (int64_t)f.page_size + off) * (int64_t)f.slot_bytes);
+  }
+};
+
 // Lane order of the Q4_0 / Q8_0 many-row kernel.  Element bits 2-5 of a
 // 64-wide group, e = (e2, e3, e4, e5), sit in lane e2 ^ 2 e3 ^ 7 e4 ^ 8 e5
 // of the 16-lane row, so the partner of every cross-lane butterfly stage is
@@ -825,22 +882,31 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
   const int stride = (int)gridDim.x * kQuantWaves * 4;
   int base = ((int)blockIdx.x * kQuantWaves + wave) * 4;
   if (base >= rows) return;
+  const int H = num_kv_heads;
+  const int ntok = rows / H;
+  SlotAddr sa;
+  sa.init(f, H);
+  RowCursor c;
+  c.init(base + (lane >> 4), stride, H);
+  // The next four rows load during this group, unconditionally (clamped to
+  // the last row; a row past the end reads slot id -1).
+  auto slot_of = [&](const RowCursor& rc) -> int64_t {
+    const int64_t s = slot_mapping[min(rc.tok, ntok - 1)];
+    return rc.tok < ntok ? s : -1;
+  };
   uint32_t rk[Q][R], rv[Q][R];
-  int row = base + (lane >> 4);
-  fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * e, rk, rv);
-  int64_t sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
+  fetch_rows16<Q, F16>(key, value, min(c.row, rows - 1), 4 * e, rk, rv);
+  int64_t sm = slot_of(c);
   for (;;) {
     float k[Q][4], v[Q][4];
     widen16_stage1<Q, F16>(rk, k);
     widen16_stage1<Q, F16>(rv, v);
-    const int cur = row;
+    const int cur_head = c.head;
     const int64_t cur_sm = sm;
     base += stride;
-    row += stride;
-    if (base < rows) {  // the next four rows load during this group
-      fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * e, rk, rv);
-      sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
-    }
+    c.advance(stride, H);
+    fetch_rows16<Q, F16>(key, value, min(c.row, rows - 1), 4 * e, rk, rv);
+    sm = slot_of(c);
     fwht_rows16_q<Q, F16>(k, e, f.k_norm);
     fwht_rows16_q<Q, F16>(v, e, f.v_norm);
     uint32_t wk[Q], wv[Q], sk[Q], sv[Q];
@@ -861,18 +927,7 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
 #pragma unroll
     for (int q = 0; q < Q; ++q) sw = (l == Q + q) ? sv[q] : sw;
     if (cur_sm >= 0) {
-      int64_t page;
-      int off;
-      if ((cur_sm >> 32) == 0) {
-        const uint32_t s32 = (uint32_t)cur_sm;
-        page = s32 / (uint32_t)f.page_size;
-        off = (int)(s32 % (uint32_t)f.page_size);
-      } else {
-        page = cur_sm / f.page_size;
-        off = (int)(cur_sm % f.page_size);
-      }
-      uint32_t* dst =
-          (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, cur % num_kv_heads);
+      uint32_t* dst = (uint32_t*)(cache + sa.offset(f, cur_sm, cur_head, H));
       if (KIND == HKV_KIND_Q8_0) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -1138,10 +1193,21 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
   const int kw = f.k_wide / kWave;  // groups of 4-bit K codes
   const int nks = f.num_k_scales;
   const int nsw = (f.slot_bytes - f.off_scales) / 4;
+  const int H = num_kv_heads;
+  const int ntok = rows / H;
+  SlotAddr sa;
+  sa.init(f, H);
+  RowCursor c;
+  c.init(base + (lane >> 4), stride, H);
+  // The next four rows load during this group, unconditionally (clamped to
+  // the last row; a row past the end reads slot id -1).
+  auto slot_of = [&](const RowCursor& rc) -> int64_t {
+    const int64_t s = slot_mapping[min(rc.tok, ntok - 1)];
+    return rc.tok < ntok ? s : -1;
+  };
   uint32_t rk[Q][R], rv[Q][R];
-  int row = base + (lane >> 4);
-  fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * (lane & 15), rk, rv);
-  int64_t sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
+  fetch_rows16<Q, F16>(key, value, min(c.row, rows - 1), 4 * (lane & 15), rk, rv);
+  int64_t sm = slot_of(c);
   for (;;) {
     float k[Q][4], v[Q][4];
     if (F16) {
@@ -1167,14 +1233,12 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
           v[q][i] = __uint_as_float(__float_as_uint(v[q][i]) ^ smk[q][i]);
         }
     }
-    const int cur = row;
+    const int cur_head = c.head;
     const int64_t cur_sm = sm;
     base += stride;
-    row += stride;
-    if (base < rows) {  // the next four rows load during this group
-      fetch_rows16<Q, F16>(key, value, min(row, rows - 1), 4 * (lane & 15), rk, rv);
-      sm = row < rows ? slot_mapping[row / num_kv_heads] : -1;
-    }
+    c.advance(stride, H);
+    fetch_rows16<Q, F16>(key, value, min(c.row, rows - 1), 4 * (lane & 15), rk, rv);
+    sm = slot_of(c);
     fwht_rows16b<Q, F16>(k, f.k_block, f.k_norm);
     fwht_rows16b<Q, F16>(v, f.v_block, f.v_norm);
     uint32_t ck[Q][4], cv[Q][4], ks[Q];
@@ -1197,18 +1261,7 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
       sw |= (l == (i >> 1)) ? (sc << (16 * (i & 1))) : 0u;
     }
     if (cur_sm >= 0) {
-      int64_t page;
-      int off;
-      if ((cur_sm >> 32) == 0) {
-        const uint32_t s32 = (uint32_t)cur_sm;
-        page = s32 / (uint32_t)f.page_size;
-        off = (int)(s32 % (uint32_t)f.page_size);
-      } else {
-        page = cur_sm / f.page_size;
-        off = (int)(cur_sm % f.page_size);
-      }
-      uint32_t* dst =
-          (uint32_t*)slot_ptr(f, cache, page, off, num_kv_heads, cur % num_kv_heads);
+      uint32_t* dst = (uint32_t*)(cache + sa.offset(f, cur_sm, cur_head, H));
       const int wk3 = f.off_k_nope / 4, nk3 = kWave * (Q - kw), wv0 = f.off_v / 4;
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
