@@ -11,6 +11,8 @@
 // (reference_quantize, _quantize_lut, _pack, reference_dequantize) and Strata
 // pull request #21 (Q4_0 block with one fp16 scale per 32 values; the max-abs
 // tie-break of the merge note).
+#include <cmath>
+
 #include "hkv_internal.h"
 
 namespace hkv {
@@ -702,8 +704,14 @@ HKV_FMAC4_SRC_DEF(0x1B, "quad_perm:[3,2,1,0]")
 #undef HKV_FMAC4_SRC_DEF
 
 // fwht_rows16 in the lane order of qrow_elem (from stride 2 when the
-// caller has already done the stride-1 stage, kFrom2).
-template <int Q, bool kFrom2 = false>
+// caller has already done the stride-1 stage, kFrom2).  kFuseNorm (Q >= 2,
+// fp16 inputs, a power-of-two norm): the last register stage takes the
+// normalising multiply with it, (a + b) s = fma(a, s, b s) and
+// (a - b) s = fma(a, s, -(b s)): b s is exact, and so is the product of a
+// rounded sum by a power of two while it stays normal, which every nonzero
+// value of an fp16 row does (each is a multiple of 2^-24 before the
+// multiply), so the bits are those of the stage followed by the multiply.
+template <int Q, bool kFrom2 = false, bool kFuseNorm = false>
 __device__ __forceinline__ void fwht_rows16_q(float (&x)[Q][4], int e, float norm) {
   // h = 1, 2: registers
 #pragma unroll
@@ -723,8 +731,10 @@ __device__ __forceinline__ void fwht_rows16_q(float (&x)[Q][4], int e, float nor
   fwht_stage_fused<0x141>(x, (e & 4) ? -1.0f : 1.0f);
   fwht_stage_fused<0x128>(x, (e & 8) ? -1.0f : 1.0f);
   // h = 64, 128: register groups (both values carry the lane's sign)
+  constexpr bool kFuse = kFuseNorm && Q >= 2;
+  constexpr int kLast = kFuse ? Q / 2 : Q;  // the stage fused with the multiply
 #pragma unroll
-  for (int hq = 1; hq < Q; hq <<= 1)
+  for (int hq = 1; hq < kLast; hq <<= 1)
 #pragma unroll
     for (int q = 0; q < Q; ++q)
       if ((q & hq) == 0)
@@ -735,36 +745,63 @@ __device__ __forceinline__ void fwht_rows16_q(float (&x)[Q][4], int e, float nor
           x[q + hq][i] = a - b;
         }
   const float sn = (__builtin_popcount(e) & 1) ? -norm : norm;
+  if constexpr (kFuse) {
 #pragma unroll
-  for (int q = 0; q < Q; ++q)
+    for (int q = 0; q < Q; ++q)
+      if ((q & kLast) == 0)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * sn;
+        for (int i = 0; i < 4; ++i) {
+          const float a = x[q][i], bs = x[q + kLast][i] * sn;
+          x[q][i] = __builtin_fmaf(a, sn, bs);
+          x[q + kLast][i] = __builtin_fmaf(a, sn, -bs);
+        }
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[q][i] = x[q][i] * sn;
+  }
 }
 
 // One 64-wide group: codes packed into the words of this lane pair and the
-// fp16 scales of its two blocks, in the lane order of qrow_elem.  On return
-// `word` (lanes with e2 = 0) is slot word 8q + e/2 of the segment and `scale`
-// (lanes 0-7 of the row) is the scale word of the group (block 2q | block
-// 2q+1 << 16).
-__device__ __forceinline__ void q4_group16(const float (&x)[4], uint32_t* word,
+// fp16 scales of its two blocks, in the lane order of qrow_elem.  The group
+// comes in negated, y = -x (the normalising multiply of fwht_rows16_q takes
+// the negated factor, which costs nothing), so that the max-abs key
+// (|x| bits, x >= +0) is the bits of y rotated left by one, and the scale
+// d = m / -8 of the chosen element m is the key rotated right by one (the
+// bits of -m) times 1/8; x (1/d) is y (-1/d).  Keys start at 1, the key of
+// +0, so that a block of zeros of either sign takes m = +0 as the tie-break
+// gives it.  On return `word` (lanes with e2 = 0) is slot word 8q + e/2 of
+// the segment and `scale` (lanes 0-7 of the row) is the scale word of the
+// group (block 2q | block 2q+1 << 16).
+__device__ __forceinline__ void q4_group16(const float (&y)[4], uint32_t* word,
                                            uint32_t* scale) {
   uint32_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t b = __float_as_uint(x[i]);
-    key[i] = (b << 1) | ((~b) >> 31);  // (|x| bits, x >= 0): see q4_block
+    const uint32_t b = __float_as_uint(y[i]);
+    key[i] = __builtin_amdgcn_alignbit(b, b, 31);  // rotate left by one: see q4_block
   }
-  uint32_t kmax = max(max(key[0], key[1]), max(key[2], key[3]));
+  uint32_t kmax = max(max(key[0], key[1]), key[2]);
+  kmax = max(max(kmax, key[3]), 1u);
   kmax = max(kmax, dpp<0xB1>(kmax));   // quad [1,0,3,2]
   kmax = max(kmax, dpp<0x4E>(kmax));   // quad [2,3,0,1]
   kmax = max(kmax, dpp<0x141>(kmax));  // half-row mirror: the 8 lanes of the block
-  const float m = (kmax >> 1) == 0 ? 0.0f : __uint_as_float((kmax >> 1) | ((~kmax) << 31));
-  const float d = m / -8.0f;
-  const float id = (d != 0.0f) ? recip_rn(d) : 0.0f;
+  const float d = __uint_as_float(__builtin_amdgcn_alignbit(kmax, kmax, 1)) * 0.125f;
+  // 1/d: recip_rn's fast form when every lane of the wave has |d| in
+  // [2^-100, 2^100] (|m| in [2^-97, 2^103]: keys 0x1E000000 .. 0xE6000001),
+  // else recip_rn itself, 0 for d = 0.
+  float id;
+  if (__builtin_amdgcn_ballot_w64(kmax - 0x1E000000u > 0xE6000001u - 0x1E000000u) == 0) {
+    const float r = __builtin_amdgcn_rcpf(d);
+    id = __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+  } else {
+    id = (d != 0.0f) ? recip_rn(d) : 0.0f;
+  }
   uint32_t c[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float u = x[i] * id + 8.5f;
+    const float u = y[i] * -id + 8.5f;
     const int ci = (int)u;
     c[i] = (uint32_t)(ci > 15 ? 15 : ci);
   }
@@ -775,13 +812,15 @@ __device__ __forceinline__ void q4_group16(const float (&x)[4], uint32_t* word,
   *scale = h | (dpp<0x128>(h) << 16);  // row_ror:8 -> the other block's scale
 }
 
-// Q8_0 over one 64-wide group in the lane order of qrow_elem: `word` is slot
-// word 16q + e (this lane's four int8 codes), `scale` (lanes 0-7) the scale
-// word of the group, as for Q4_0.
-__device__ __forceinline__ void q8_group16(const float (&x)[4], uint32_t* word,
+// Q8_0 over one 64-wide group in the lane order of qrow_elem, negated as for
+// Q4_0 (y = -x: the magnitudes are those of x, and round(x id) is
+// round(y (-id)), rounding being symmetric): `word` is slot word 16q + e
+// (this lane's four int8 codes), `scale` (lanes 0-7) the scale word of the
+// group, as for Q4_0.
+__device__ __forceinline__ void q8_group16(const float (&y)[4], uint32_t* word,
                                            uint32_t* scale) {
-  uint32_t a = max(max(__float_as_uint(x[0]) & 0x7FFFFFFFu, __float_as_uint(x[1]) & 0x7FFFFFFFu),
-                   max(__float_as_uint(x[2]) & 0x7FFFFFFFu, __float_as_uint(x[3]) & 0x7FFFFFFFu));
+  uint32_t a = max(max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu),
+                   max(__float_as_uint(y[2]) & 0x7FFFFFFFu, __float_as_uint(y[3]) & 0x7FFFFFFFu));
   a = max(a, dpp<0xB1>(a));   // quad [1,0,3,2]
   a = max(a, dpp<0x4E>(a));   // quad [2,3,0,1]
   a = max(a, dpp<0x141>(a));  // half-row mirror: the 8 lanes of the block
@@ -789,7 +828,7 @@ __device__ __forceinline__ void q8_group16(const float (&x)[4], uint32_t* word,
   const float id = (d != 0.0f) ? recip_rn(d) : 0.0f;
   uint32_t w = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w |= ((uint32_t)(int)roundf(x[i] * id) & 0xFFu) << (8 * i);
+  for (int i = 0; i < 4; ++i) w |= ((uint32_t)(int)roundf(y[i] * -id) & 0xFFu) << (8 * i);
   *word = w;
   const uint32_t h = f2h(d);
   *scale = h | (dpp<0x128>(h) << 16);
@@ -870,7 +909,7 @@ constexpr int kRows16MinRows = 4096;  // below this the one-row-per-wave kernel 
 
 // rows as for quantize_append_kernel; key/value 8-byte (f16) or 16-byte (f32)
 // aligned.
-template <int Q, bool F16, int KIND>
+template <int Q, bool F16, int KIND, bool kFuseNorm>
 __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
     DevFmt f, const void* key, const void* value, int rows, int num_kv_heads,
     const int64_t* slot_mapping, uint8_t* cache) {
@@ -907,8 +946,9 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
     c.advance(stride, H);
     fetch_rows16<Q, F16>(key, value, min(c.row, rows - 1), 4 * e, rk, rv);
     sm = slot_of(c);
-    fwht_rows16_q<Q, F16>(k, e, f.k_norm);
-    fwht_rows16_q<Q, F16>(v, e, f.v_norm);
+    // negated outputs (see q4_group16)
+    fwht_rows16_q<Q, F16, kFuseNorm>(k, e, -f.k_norm);
+    fwht_rows16_q<Q, F16, kFuseNorm>(v, e, -f.v_norm);
     uint32_t wk[Q], wv[Q], sk[Q], sv[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
@@ -1345,11 +1385,17 @@ hipError_t launch_quantize_append(const DevFmt& f, const void* key, const void* 
       ((uintptr_t)value % align) == 0) {
     const int64_t g16 = (rows + 4 * kQuantWaves - 1) / (4 * kQuantWaves);
     const dim3 grid16((unsigned)(g16 < kQuantMaxGroups ? g16 : kQuantMaxGroups));
+    // fp16 rows with power-of-two norms take the last stage fused with the
+    // normalising multiply (see fwht_rows16_q)
+    int ek, ev;
+    const bool fuse = in_f16 && std::frexp(f.k_norm, &ek) == 0.5f && std::frexp(f.v_norm, &ev) == 0.5f;
 #define HKV_Q16K(Q_, K_)                                                                     \
-  (in_f16 ? (quantize_rows16_kernel<Q_, true, K_><<<grid16, block, 0, s>>>(                  \
-                f, key, value, r, num_kv_heads, slot_mapping, cache))                        \
-          : (quantize_rows16_kernel<Q_, false, K_><<<grid16, block, 0, s>>>(                 \
-                f, key, value, r, num_kv_heads, slot_mapping, cache)))
+  (!in_f16 ? (quantize_rows16_kernel<Q_, false, K_, false><<<grid16, block, 0, s>>>(         \
+                 f, key, value, r, num_kv_heads, slot_mapping, cache))                       \
+   : fuse  ? (quantize_rows16_kernel<Q_, true, K_, true><<<grid16, block, 0, s>>>(           \
+                 f, key, value, r, num_kv_heads, slot_mapping, cache))                       \
+           : (quantize_rows16_kernel<Q_, true, K_, false><<<grid16, block, 0, s>>>(          \
+                 f, key, value, r, num_kv_heads, slot_mapping, cache)))
 #define HKV_Q16(Q_) (q8 ? HKV_Q16K(Q_, HKV_KIND_Q8_0) : HKV_Q16K(Q_, HKV_KIND_Q4_0))
     switch (f.D / kWave) {
       case 1: HKV_Q16(1); break;
