@@ -1004,7 +1004,7 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
 // byte and LUT[code] in its high byte.  2y = RN(q * 2 mult) exactly, since
 // doubling commutes with rounding.
 
-struct OctTables {
+struct OctTables {  // entry n + 256: LUT[code] (int8) | code << 8
   uint16_t t3[512];
   uint16_t t4[512];
 };
@@ -1017,23 +1017,29 @@ __device__ void oct_tables_fill(OctTables& T) {
 #pragma unroll
       for (int k = 0; k < 7; ++k) c += (kLut3[k] + kLut3[k + 1] <= n) ? 1 : 0;
       lv = kLut3[c];
-      T.t3[e] = (uint16_t)(c | ((lv & 0xFF) << 8));
+      T.t3[e] = (uint16_t)((lv & 0xFF) | (c << 8));
     } else {
 #pragma unroll
       for (int k = 0; k < 15; ++k) c += (kLut4[k] + kLut4[k + 1] <= n) ? 1 : 0;
       lv = kLut4[c];
-      T.t4[e - 512] = (uint16_t)(c | ((lv & 0xFF) << 8));
+      T.t4[e - 512] = (uint16_t)((lv & 0xFF) | (c << 8));
     }
   }
 }
 
+// The table entry of z = 2y (LUT[code] in its low byte, the code in byte 1)
+// and LUT[code] as a float.
 template <int BITS>
 __device__ __forceinline__ uint32_t oct_code(const OctTables& T, float z, float* lv) {
-  int n = (int)ceilf(z) - 1;
-  n = min(max(n, -256), 255);
-  const uint32_t e = (BITS == 3 ? T.t3 : T.t4)[n + 256];
-  *lv = (float)(int)(int8_t)(uint8_t)(e >> 8);
-  return e & 0xFFu;
+  // n = ceil(z) - 1 = ~floor(-z), clamped to [-256, 255] as f = floor(-z) in
+  // [-256, 255]; the entry is n + 256 = 255 - f.
+  int f;
+  asm("v_cvt_flr_i32_f32_e64 %0, -%1" : "=v"(f) : "v"(z));
+  f = min(max(f, -256), 255);
+  const uint16_t* t = BITS == 3 ? T.t3 : T.t4;
+  const uint32_t e = *(const uint16_t*)((const char*)t + 510 + f * -2);
+  *lv = (float)(int)(int8_t)(uint8_t)e;
+  return e;
 }
 
 // fwht_rows16 for a transform block of 64 or 64Q values (the group stages
@@ -1128,9 +1134,21 @@ __device__ __forceinline__ float tree16(const float (&t)[Q][4], int q0) {
   return a + b;
 }
 
-// [OCT] _quantize_lut over groups [q0, q0 + NQ) of a row; codes into
-// codes[q0 ..]; returns the fp16 bits of the scale (the same in the row).
-template <int Q, int NQ, int BITS>
+// [OCT] _quantize_lut over groups [q0, q0 + NQ) of a row; codes (as table
+// entries, the code in byte 1) into codes[q0 ..]; returns the fp16 bits of
+// the scale (the same in the row).
+// kHalfIn (fp16 rows): before the normalising multiply every nonzero value is
+// a multiple of 2^-24 below 2^20 (a block of at most 256 fp16 values), so
+// after it (by 1/sqrt(block) >= 1/16) every nonzero |x| lies in
+// [2^-28, 2^20]: rms (clamped to >= 1e-12) lies in [2^-40, 2^20], a nonzero
+// quotient x / rms is above 2^-48, and dot = sum of |x| |LUT[c]| (the
+// codebooks are symmetric, so a code has the sign of its value; |LUT| >= 6)
+// is zero or in [2^-26, 2^35], with ss / dot in [2^-44, 2^18].  So the
+// reciprocal's fast form needs no range test, Markstein's quotient never
+// takes its tiny-quotient fallback, and ss / dot is the same quotient
+// (RN(1/dot), the product, its exact remainder, one correction) in place of
+// the division.
+template <int Q, int NQ, int BITS, bool kHalfIn>
 __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float (&x)[Q][4], int q0,
                                                 uint32_t (&codes)[Q][4]) {
   float t[Q][4];
@@ -1140,7 +1158,13 @@ __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float 
     for (int i = 0; i < 4; ++i) t[q][i] = x[q][i] * x[q][i];
   const float ss = tree16<Q, NQ>(t, q0);
   const float rms = oct_block_rms(ss, NQ * kWave);
-  const float ry = recip_rn(rms);
+  float ry;
+  if constexpr (kHalfIn) {
+    const float r = __builtin_amdgcn_rcpf(rms);
+    ry = __builtin_fmaf(__builtin_fmaf(-rms, r, 1.0f), r, r);
+  } else {
+    ry = recip_rn(rms);
+  }
   float qv[NQ][4];
   bool tiny = false;
 #pragma unroll
@@ -1151,9 +1175,9 @@ __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float 
       const float q0v = xv * ry;
       const float r = fmaf(-rms, q0v, xv);
       qv[q][i] = fmaf(r, ry, q0v);
-      tiny |= xv != 0.0f && fabsf(qv[q][i]) < 0x1p-100f;
+      if constexpr (!kHalfIn) tiny |= xv != 0.0f && fabsf(qv[q][i]) < 0x1p-100f;
     }
-  if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+  if (!kHalfIn && __builtin_amdgcn_ballot_w64(tiny) != 0) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
@@ -1171,26 +1195,39 @@ __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float 
       codes[q0 + q][i] = oct_code<BITS>(T, qv[q][i] * m2, &lv);
       t[q0 + q][i] = x[q0 + q][i] * lv;
     }
-  return oct_norm_preserving_scale(ss, tree16<Q, NQ>(t, q0));
+  const float dot = tree16<Q, NQ>(t, q0);
+  if constexpr (kHalfIn) {
+    // oct_norm_preserving_scale with the quotient as above (dot > 0 here
+    // unless the row is zero, when ss = dot = 0 and the scale is 0)
+    const float dd = dot > 1e-30f ? dot : 1e-30f;
+    const float r = __builtin_amdgcn_rcpf(dd);
+    const float y = __builtin_fmaf(__builtin_fmaf(-dd, r, 1.0f), r, r);
+    const float g0 = ss * y;
+    const float g = __builtin_fmaf(__builtin_fmaf(-dd, g0, ss), y, g0);
+    return f2h((dot > 0.0f ? g : 0.0f) * (float)kLutOne);
+  } else {
+    return oct_norm_preserving_scale(ss, dot);
+  }
 }
 
 // Slot words of one group's codes (segment-relative group qq, segment of n
-// codes starting at word w0), stored by the lanes that hold them.
+// codes starting at word w0), stored by the lanes that hold them.  The codes
+// come as table entries (code in byte 1), gathered into one byte each.
+__device__ __forceinline__ uint32_t code_bytes16(const uint32_t (&c)[4]) {
+  return __builtin_amdgcn_perm(c[1], c[0], 0x0C0C0501u) | __builtin_amdgcn_perm(c[3], c[2], 0x05010C0Cu);
+}
 __device__ __forceinline__ void store4_16(uint32_t* dst, int w0, int qq, const uint32_t (&c)[4]) {
   const int l = lane_id() & 15;
-  const uint32_t bytes = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  const uint32_t bytes = code_bytes16(c);
   const uint32_t w = bytes | (dpp<0xB1>(bytes) << 4);  // odd lane: the high nibbles
   if ((l & 1) == 0) dst[w0 + 8 * qq + (l >> 1)] = w;
 }
 __device__ __forceinline__ void store3_16(uint32_t* dst, int w0, int n, int qq,
                                           const uint32_t (&c)[4]) {
   const int l = lane_id() & 15;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    lo |= (c[j] & 3u) << (8 * j);
-    hi |= ((c[j] >> 2) & 1u) << (8 * j);
-  }
+  const uint32_t bytes = code_bytes16(c);
+  uint32_t lo = bytes & 0x03030303u;
+  uint32_t hi = (bytes >> 2) & 0x01010101u;
   lo = or_quad(lo << (2 * (l & 3)));                    // low plane: 4 lanes a word
   hi <<= (l & 7);
   hi = or_quad(hi);
@@ -1283,16 +1320,17 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_oct_rows16_kerne
     fwht_rows16b<Q, F16>(v, f.v_block, f.v_norm);
     uint32_t ck[Q][4], cv[Q][4], ks[Q];
     if (f.compact) {
-      ks[0] = oct_block16<Q, Q, 3>(T, k, 0, ck);
+      ks[0] = oct_block16<Q, Q, 3, F16>(T, k, 0, ck);
 #pragma unroll
       for (int q = 1; q < Q; ++q) ks[q] = 0;
     } else {
 #pragma unroll
       for (int q = 0; q < Q; ++q)
-        ks[q] = (q < kw) ? oct_block16<Q, 1, 4>(T, k, q, ck) : oct_block16<Q, 1, 3>(T, k, q, ck);
+        ks[q] = (q < kw) ? oct_block16<Q, 1, 4, F16>(T, k, q, ck) : oct_block16<Q, 1, 3, F16>(T, k, q, ck);
     }
     const bool v4 = f.v_bits == 4;
-    const uint32_t vs = v4 ? oct_block16<Q, Q, 4>(T, v, 0, cv) : oct_block16<Q, Q, 3>(T, v, 0, cv);
+    const uint32_t vs =
+        v4 ? oct_block16<Q, Q, 4, F16>(T, v, 0, cv) : oct_block16<Q, Q, 3, F16>(T, v, 0, cv);
     // scale word w holds scales 2w and 2w + 1: K scales, the V scale, zeros
     uint32_t sw = 0;
 #pragma unroll
