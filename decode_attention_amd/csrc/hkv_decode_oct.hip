@@ -166,15 +166,6 @@ constexpr uint32_t half_byte_word(int i, int byte) {
 }
 constexpr uint32_t kH3Lo[2] = {half_byte_word(0, 0), half_byte_word(1, 0)};
 constexpr uint32_t kH3Hi[2] = {half_byte_word(0, 1), half_byte_word(1, 1)};
-// High bytes of fp16(LUT x 2^-12): the exponent field 12 lower (every
-// entry stays normal, |LUT| >= 14); the low bytes are those of kH3Lo.
-constexpr uint32_t half_hi_scaled_word(int i) {
-  uint32_t w = 0;
-  for (int k = 0; k < 4; ++k) w |= (((half_bits_int(kLut3[4 * i + k]) - (12u << 10)) >> 8) & 255u) << (8 * k);
-  return w;
-}
-constexpr uint32_t kH3Hs[2] = {half_hi_scaled_word(0), half_hi_scaled_word(1)};
-static_assert(half_bits_int(14) - (12u << 10) == 0x1B00u, "fp16 bits of 14 x 2^-12");
 
 // fp16 values of the 3-bit codes in the four bytes of sel: the halves of
 // codes 0, 1 in .x and of codes 2, 3 in .y.
@@ -801,9 +792,10 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
 //  * P.V on v_mfma_f32_32x32x16_f16 as O^T = V^T P^T (rows = dims, columns =
 //    query rows), 8 tokens per step: a lane's k-slots are its 4 tokens'
 //    fp16(p s) and their residuals x 2^12, against the tokens' values and
-//    values x 2^-12, exact fp16 assembled from three byte tables (the low
-//    bytes, the high bytes, the high bytes of the value x 2^-12) with two
-//    v_perm_b32 interleaves per pair of codes and part.
+//    values x 2^-12: the values exact fp16 assembled from two byte tables
+//    (the low and the high bytes) with two v_perm_b32 interleaves per four
+//    codes, the copies one packed multiply by 2^-12 per two values (exact:
+//    every |LUT| >= 14 stays a normal fp16).
 //  * V dims: tile (b, i) of 32 dims has row a = 4 m' + j holding dim
 //    16 (8 b + m') + 4 i + j; a lane gathers byte j of low-plane word 8 b + m'
 //    of its 4 tokens once and takes the codes of all four i from it.
@@ -1097,11 +1089,12 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_oct32_kernel(DevFmt f, De
             const uint32_t sel = ((gl >> (2 * i)) & 0x03030303u) | (((gh >> i) << 2) & 0x04040404u);
             const uint32_t xl = __builtin_amdgcn_perm(kH3Lo[1], kH3Lo[0], sel);
             const uint32_t xh = __builtin_amdgcn_perm(kH3Hi[1], kH3Hi[0], sel);
-            const uint32_t xs = __builtin_amdgcn_perm(kH3Hs[1], kH3Hs[0], sel);
-            const uint4 A = {__builtin_amdgcn_perm(xh, xl, 0x05010400u),
-                             __builtin_amdgcn_perm(xh, xl, 0x07030602u),
-                             __builtin_amdgcn_perm(xs, xl, 0x05010400u),
-                             __builtin_amdgcn_perm(xs, xl, 0x07030602u)};
+            const uint32_t a0 = __builtin_amdgcn_perm(xh, xl, 0x05010400u);
+            const uint32_t a1 = __builtin_amdgcn_perm(xh, xl, 0x07030602u);
+            // the copies x 2^-12: exact (every |LUT| >= 14 stays a normal fp16)
+            const half2_t s12 = {(__fp16)(1.0f / 4096.0f), (__fp16)(1.0f / 4096.0f)};
+            const uint4 A = {a0, a1, __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a0) * s12),
+                             __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a1) * s12)};
             o[4 * b + i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                 __builtin_bit_cast(half8_t, A), P[j], o[4 * b + i], 0, 0, 0);
           }
