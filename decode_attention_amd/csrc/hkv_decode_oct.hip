@@ -135,6 +135,7 @@ constexpr int kQMaxI = kQ3MaxI;    // largest |q| code of the three-plane int8 s
 constexpr float kQMax = (float)kQ3MaxI;
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max is raised
 constexpr int kQWaves = 8;         // waves per workgroup (two per SIMD)
+constexpr int kQWaves12 = 12;      // three per SIMD (8-row mode at head size 128)
 constexpr int kMaxSplitTiles = 256;
 
 // Codebook bytes for v_perm_b32 lookups: entries 4i..4i+3 in word i.
@@ -219,7 +220,7 @@ struct Tile {
   uint32_t sw;
 };
 
-template <class F, int RM>
+template <class F, int RM, int NW>
 struct __align__(16) OctLds {
   static constexpr int kD = F::kD;
   static constexpr int kSlotW = (F::kSlot + 3) / 4 > 16 * F::kChunks ? (F::kSlot + 3) / 4
@@ -230,29 +231,32 @@ struct __align__(16) OctLds {
   static constexpr int kQCols = RM == 8 ? 32 : 48;
   int8_t qB[kD / 64][kQCols][64];
   float qsc[RM];
-  float mlw[kQWaves][RM][2];
+  float mlw[NW][RM][2];
   int pid[kMaxSplitTiles];
   int next_unit;
   int pad_[3];
   union {
-    uint32_t tt[kQWaves][2][2][kSlotW][kTS];  // [buf][tile][slot word][token]
-    float ob[kQWaves][RM][kD];
+    uint32_t tt[NW][2][2][kSlotW][kTS];  // [buf][tile][slot word][token]
+    float ob[NW][RM][kD];
   } u;
 };
 
-template <class F, int RM>
-__global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f, DecArgs a) {
+// NW waves per workgroup: 8 (two per SIMD), or 12 (three per SIMD) where the
+// tiles of 12 waves fit the LDS (head size 128) and the kernel fits the 168
+// VGPRs that three waves leave.
+template <class F, int RM, int NW>
+__global__ __launch_bounds__(NW * kWave, 1) void decode_oct_kernel(DevFmt f, DecArgs a) {
   constexpr int kD = F::kD;
   constexpr int kSlot = F::kSlot;
   constexpr int kE = kD / kWave;  // query values per lane
   constexpr int kAcc = F::kAcc;
   constexpr bool kK16 = RM == 16;       // residual of p in the K dimension
-  constexpr int kQR = RM / kQWaves;     // query rows per wave
-  __shared__ OctLds<F, RM> L;
+  constexpr int kQR = (RM + NW - 1) / NW;  // query rows per wave (rows wave + NW k < RM)
+  __shared__ OctLds<F, RM, NW> L;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
-  static_assert(kMaxSplitTiles <= kQWaves * kWave, "one page id per thread");
+  static_assert(kMaxSplitTiles <= NW * kWave, "one page id per thread");
   int page_size = f.page_size, k_block = f.k_block;
   float k_norm = f.k_norm;
   pin_args(a, page_size, k_block, k_norm);
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   //     indices), so no wait before the barrier covers a later round trip.
   uint32_t qw[kQR][kE];
 #pragma unroll
-  for (int k = 0; k < kQR; ++k) query_row_raw<kE>(a, q0, kvh, wave + kQWaves * k, lane, qw[k]);
+  for (int k = 0; k < kQR; ++k) query_row_raw<kE>(a, q0, kvh, wave + NW * k, lane, qw[k]);
   uint32_t sw[kE];
   lane_sign_words<kE>(f, f.use_signs, lane, sw);
   const int kl = group_klen_lane(a, q0, lane);
@@ -324,10 +328,11 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
   }
   __builtin_amdgcn_sched_barrier(0);
   L.pid[tpid] = pidv;
-  if (threadIdx.x == 0) L.next_unit = 2 * kQWaves;
+  if (threadIdx.x == 0) L.next_unit = 2 * NW;
 #pragma unroll
   for (int k = 0; k < kQR; ++k) {
-    const int r = wave + kQWaves * k;
+    const int r = wave + NW * k;
+    if (RM % NW != 0 && r >= RM) break;  // (wave-uniform) waves past the rows
     float x[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) x[e] = flip_sign(query_value(a, qw[k][e], r < a.rows), sw[e], lane);
@@ -675,7 +680,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     };
 
     float sa[4], sb[4];
-    int u_cur = wave, u_nxt = wave + kQWaves;
+    int u_cur = wave, u_nxt = wave + NW;
     stage_s(ta, 0, 0, sa);
     fetch(ta, 2 * u_nxt);
     stage_s(tb, 1, 0, sb);
@@ -683,7 +688,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     int buf = 0;
     AOps A;
     while (u_nxt < nu) {
-      int u_nn = u_nxt + kQWaves;  // deterministic mode: a fixed order
+      int u_nn = u_nxt + NW;  // deterministic mode: a fixed order
       if (!a.det) {
         if (lane == 0) u_nn = atomicAdd(&L.next_unit, 1);
         u_nn = __builtin_amdgcn_readfirstlane(u_nn);
@@ -739,7 +744,7 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
       const int r = 4 * g + i;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, L.mlw[w][r][0]);
       const float mw = L.mlw[wave][r][0];
       fw[i] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
     }
@@ -755,14 +760,14 @@ __global__ __launch_bounds__(kQWaves * kWave, 1) void decode_oct_kernel(DevFmt f
     const int r = idx / kD, d = idx % kD;
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kQWaves; ++w) acc += L.u.ob[w][r][d];
+    for (int w = 0; w < NW; ++w) acc += L.u.ob[w][r][d];
     part[r * a.pstride + kPartialHead + d] = acc;
   }
   if (threadIdx.x < a.rows) {
     const int r = threadIdx.x;
     float M = -INFINITY, L_ = 0.0f;
-    for (int w = 0; w < kQWaves; ++w) M = fmaxf(M, L.mlw[w][r][0]);
-    for (int w = 0; w < kQWaves; ++w) {
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, L.mlw[w][r][0]);
+    for (int w = 0; w < NW; ++w) {
       const float mw = L.mlw[w][r][0];
       if (mw != -INFINITY) L_ += L.mlw[w][r][1] * exp2f(mw - M);
     }
@@ -1194,16 +1199,17 @@ int oct_mfma_rows(const DevFmt& f, int rows) {
 hipError_t launch_decode_oct(const DevFmt& f, const DecArgs& a, dim3 grid, hipStream_t s) {
   if ((a.tokens_per_split + kT - 1) / kT > kMaxSplitTiles) return hipErrorInvalidValue;
   const dim3 block(kQWaves * kWave);
+  const dim3 block12(kQWaves12 * kWave);
   if (a.rows_pad == 8) {
-    if (f.compact) decode_oct_kernel<FmtK3V3C, 8><<<grid, block, 0, s>>>(f, a);
-    else if (f.v_bits == 3) decode_oct_kernel<FmtK3V3, 8><<<grid, block, 0, s>>>(f, a);
-    else if (f.D == FmtK3V4W::kD) decode_oct_kernel<FmtK3V4W, 8><<<grid, block, 0, s>>>(f, a);
-    else decode_oct_kernel<FmtK3V4, 8><<<grid, block, 0, s>>>(f, a);
+    if (f.compact) decode_oct_kernel<FmtK3V3C, 8, kQWaves><<<grid, block, 0, s>>>(f, a);
+    else if (f.v_bits == 3) decode_oct_kernel<FmtK3V3, 8, kQWaves12><<<grid, block12, 0, s>>>(f, a);
+    else if (f.D == FmtK3V4W::kD) decode_oct_kernel<FmtK3V4W, 8, kQWaves><<<grid, block, 0, s>>>(f, a);
+    else decode_oct_kernel<FmtK3V4, 8, kQWaves12><<<grid, block12, 0, s>>>(f, a);
   } else if (a.rows_pad == 16) {
-    if (f.compact) decode_oct_kernel<FmtK3V3C, 16><<<grid, block, 0, s>>>(f, a);
-    else if (f.v_bits == 3) decode_oct_kernel<FmtK3V3, 16><<<grid, block, 0, s>>>(f, a);
-    else if (f.D == FmtK3V4W::kD) decode_oct_kernel<FmtK3V4W, 16><<<grid, block, 0, s>>>(f, a);
-    else decode_oct_kernel<FmtK3V4, 16><<<grid, block, 0, s>>>(f, a);
+    if (f.compact) decode_oct_kernel<FmtK3V3C, 16, kQWaves><<<grid, block, 0, s>>>(f, a);
+    else if (f.v_bits == 3) decode_oct_kernel<FmtK3V3, 16, kQWaves><<<grid, block, 0, s>>>(f, a);
+    else if (f.D == FmtK3V4W::kD) decode_oct_kernel<FmtK3V4W, 16, kQWaves><<<grid, block, 0, s>>>(f, a);
+    else decode_oct_kernel<FmtK3V4, 16, kQWaves><<<grid, block, 0, s>>>(f, a);
   } else if (a.rows_pad == kR32 && f.compact) {
     decode_oct32_kernel<kQWaves><<<grid, block, 0, s>>>(f, a);
   } else {
