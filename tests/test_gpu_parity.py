@@ -170,6 +170,37 @@ def test_quantize_many_rows(dtype, D, R, in_dtype, misaligned):
     assert np.all(flat[untouched] == 0xA5)
 
 
+@pytest.mark.parametrize("dtype,D,R", [("q4_0", 256, 0), ("q8_0", 128, 0), ("octave_k3v4", 128, 64),
+                                       ("octave_k3v3_compact", 256, 64)])
+@pytest.mark.parametrize("P", [12, 48, 1000])
+def test_quantize_many_rows_page_sizes(dtype, D, R, P):
+    """The many-rows kernels with page sizes that are not powers of two (the
+    slot's page and offset then come from divisions, not a shift and a
+    mask), five KV heads, a ragged last wave and skipped slots: the
+    oracle's bytes, nothing else written."""
+    rng = np.random.default_rng(5 * D + P + len(dtype))
+    T, H = 1003, 5                                     # 5015 rows
+    k = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(np.float16)
+    v = (rng.standard_normal((T, H, D)) * rng.uniform(0.01, 30, (T, H, 1))).astype(np.float16)
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
+    pages = (T + P - 1) // P + 2
+    sm = rng.permutation(pages * P)[:T].astype(np.int64)
+    sm[[1, T // 2, T - 1]] = -1
+    cache = hkv.new_cache(f, pages, H, DEV)
+    cache.fill_(0xA5)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    got = cache.cpu().numpy()
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    keep = sm >= 0
+    assert np.array_equal(got[sm[keep] // P, :, sm[keep] % P], slots[keep])
+    untouched = np.ones(pages * P, bool)
+    untouched[sm[keep]] = False
+    flat = got.transpose(0, 2, 1, 3).reshape(pages * P, H, -1)
+    assert np.all(flat[untouched] == 0xA5)
+
+
 @pytest.mark.parametrize("dtype,D", [("q4_0", 256), ("q4_0", 128), ("q4_0", 64), ("q8_0", 256)])
 @pytest.mark.parametrize("in_dtype", [np.float32, np.float16])
 @pytest.mark.parametrize("T", [3, 512, 513, 1000])
