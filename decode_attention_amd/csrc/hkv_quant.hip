@@ -1126,12 +1126,24 @@ __device__ __forceinline__ float tree16(const float (&t)[Q][4], int q0) {
       for (int q = 1; q < NQ; ++q) u[i] = u[i] + t[q0 + q][i];
     }
   }
+  // Element stride 32 (lanes 8) on all four registers; lanes l and l ^ 8
+  // then hold the same sums (the add commutes bitwise), so the upper
+  // half-row takes registers 1 and 3 in place of 0 and 2, and the strides
+  // 16, 8, 4 (lanes 4, 2, 1) run on two registers instead of four.
+  // Stride 2 pairs registers 0 and 2 (lanes 0-7) and 1 and 3 (lanes 8-15);
+  // stride 1 adds the two half-rows.  The same pairs in the same order.
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1)
+  for (int i = 0; i < 4; ++i) u[i] = u[i] + shfl_xor(u[i], 8);
+  const bool upper = (lane_id() & 8) != 0;
+  float v01 = upper ? u[1] : u[0];
+  float v23 = upper ? u[3] : u[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] = u[i] + shfl_xor(u[i], m);
-  const float a = u[0] + u[2], b = u[1] + u[3];
-  return a + b;
+  for (int m = 4; m >= 1; m >>= 1) {
+    v01 = v01 + shfl_xor(v01, m);
+    v23 = v23 + shfl_xor(v23, m);
+  }
+  const float a = v01 + v23;
+  return a + shfl_xor(a, 8);
 }
 
 // [OCT] _quantize_lut over groups [q0, q0 + NQ) of a row; codes (as table
