@@ -772,10 +772,9 @@ __device__ __forceinline__ void fwht_rows16_q(float (&x)[Q][4], int e, float nor
 // bits of -m) times 1/8; x (1/d) is y (-1/d).  Keys start at 1, the key of
 // +0, so that a block of zeros of either sign takes m = +0 as the tie-break
 // gives it.  On return `word` (lanes with e2 = 0) is slot word 8q + e/2 of
-// the segment and `scale` (lanes 0-7 of the row) is the scale word of the
-// group (block 2q | block 2q+1 << 16).
-__device__ __forceinline__ void q4_group16(const float (&y)[4], uint32_t* word,
-                                           uint32_t* scale) {
+// the segment and `d` the scale of this lane's block (block 2q in lanes 0-7,
+// 2q + 1 in lanes 8-15).
+__device__ __forceinline__ void q4_group16(const float (&y)[4], uint32_t* word, float* d_out) {
   uint32_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -808,17 +807,15 @@ __device__ __forceinline__ void q4_group16(const float (&y)[4], uint32_t* word,
   // bytes of this lane's four codes; the odd lane's go to the high nibbles
   const uint32_t bytes = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
   *word = bytes | (dpp<0xB1>(bytes) << 4);
-  const uint32_t h = f2h(d);
-  *scale = h | (dpp<0x128>(h) << 16);  // row_ror:8 -> the other block's scale
+  *d_out = d;
 }
 
 // Q8_0 over one 64-wide group in the lane order of qrow_elem, negated as for
 // Q4_0 (y = -x: the magnitudes are those of x, and round(x id) is
 // round(y (-id)), rounding being symmetric): `word` is slot word 16q + e
-// (this lane's four int8 codes), `scale` (lanes 0-7) the scale word of the
-// group, as for Q4_0.
-__device__ __forceinline__ void q8_group16(const float (&y)[4], uint32_t* word,
-                                           uint32_t* scale) {
+// (this lane's four int8 codes), `d` the scale of this lane's block, as for
+// Q4_0.
+__device__ __forceinline__ void q8_group16(const float (&y)[4], uint32_t* word, float* d_out) {
   uint32_t a = max(max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu),
                    max(__float_as_uint(y[2]) & 0x7FFFFFFFu, __float_as_uint(y[3]) & 0x7FFFFFFFu));
   a = max(a, dpp<0xB1>(a));   // quad [1,0,3,2]
@@ -830,8 +827,7 @@ __device__ __forceinline__ void q8_group16(const float (&y)[4], uint32_t* word,
 #pragma unroll
   for (int i = 0; i < 4; ++i) w |= ((uint32_t)(int)roundf(y[i] * -id) & 0xFFu) << (8 * i);
   *word = w;
-  const uint32_t h = f2h(d);
-  *scale = h | (dpp<0x128>(h) << 16);
+  *d_out = d;
 }
 
 // Elements 64q + e4 .. + 3 (q < Q) of the row's K and V, for this lane's
@@ -949,23 +945,29 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
     // negated outputs (see q4_group16)
     fwht_rows16_q<Q, F16, kFuseNorm>(k, e, -f.k_norm);
     fwht_rows16_q<Q, F16, kFuseNorm>(v, e, -f.v_norm);
-    uint32_t wk[Q], wv[Q], sk[Q], sv[Q];
+    uint32_t wk[Q], wv[Q];
+    float dk[Q], dv[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       if (KIND == HKV_KIND_Q8_0) {
-        q8_group16(k[q], &wk[q], &sk[q]);
-        q8_group16(v[q], &wv[q], &sv[q]);
+        q8_group16(k[q], &wk[q], &dk[q]);
+        q8_group16(v[q], &wv[q], &dv[q]);
       } else {
-        q4_group16(k[q], &wk[q], &sk[q]);
-        q4_group16(v[q], &wv[q], &sv[q]);
+        q4_group16(k[q], &wk[q], &dk[q]);
+        q4_group16(v[q], &wv[q], &dv[q]);
       }
     }
-    // scale words: lanes 0..Q-1 the K words, Q..2Q-1 the V words
-    uint32_t sw = sk[0];
+    // scale words: lanes 0..Q-1 the K words, Q..2Q-1 the V words.  Lanes l
+    // and l + 8 pick the scales of the same group (their blocks 2q and
+    // 2q + 1), which one conversion and one row_ror:8 join into the word.
+    const int ls = l & 7;
+    float dsel = dk[0];
 #pragma unroll
-    for (int q = 1; q < Q; ++q) sw = (l == q) ? sk[q] : sw;
+    for (int q = 1; q < Q; ++q) dsel = (ls == q) ? dk[q] : dsel;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) sw = (l == Q + q) ? sv[q] : sw;
+    for (int q = 0; q < Q; ++q) dsel = (ls == Q + q) ? dv[q] : dsel;
+    const uint32_t hsel = f2h(dsel);
+    const uint32_t sw = hsel | (dpp<0x128>(hsel) << 16);
     if (cur_sm >= 0) {
       uint32_t* dst = (uint32_t*)(cache + sa.offset(f, cur_sm, cur_head, H));
       if (KIND == HKV_KIND_Q8_0) {
