@@ -1002,8 +1002,8 @@ __global__ __launch_bounds__(kQuantWaves * kWave) void quantize_rows16_kernel(
 // Codes.  The code is #{k : mid_k < y} with mid_k = (LUT[k] + LUT[k+1]) / 2,
 // i.e. #{k : T_k < 2y} for the integers T_k = LUT[k] + LUT[k+1], which is
 // #{k : T_k <= n} for the integer n = ceil(2y) - 1.  A table indexed by n
-// (clamped to [-256, 255], which holds every T_k) gives the code in its low
-// byte and LUT[code] in its high byte.  2y = RN(q * 2 mult) exactly, since
+// (clamped to [-256, 255], which holds every T_k) gives LUT[code] in its low
+// byte and the code in its high byte.  2y = RN(q * 2 mult) exactly, since
 // doubling commutes with rounding.
 
 struct OctTables {  // entry n + 256: LUT[code] (int8) | code << 8
