@@ -170,6 +170,51 @@ def test_quantize_many_rows(dtype, D, R, in_dtype, misaligned):
     assert np.all(flat[untouched] == 0xA5)
 
 
+@pytest.mark.parametrize("dtype,D,R", [("q4_0", 256, 0), ("q4_0", 128, 0), ("q8_0", 256, 0),
+                                       ("octave_k3v4", 128, 64), ("octave_k3v3", 128, 64),
+                                       ("octave_k3v3_compact", 256, 64), ("octave_k3v4", 192, 64)])
+def test_quantize_many_rows_fp16_extremes(dtype, D, R):
+    """fp16 rows at the ends of the fp16 range through the many-rows kernels,
+    whose fp16 paths rest on the range of a transformed fp16 row (every
+    nonzero value between 2^-28 and 2^20): rows of +-65504, rows of the
+    smallest subnormals, rows mixing both, rows with a single nonzero value
+    and zero rows, beside plain N(0, 1) rows.  Bytes equal the oracle's."""
+    rng = np.random.default_rng(31 * D + R + len(dtype))
+    T, H, P = 1400, 3, 16                              # 4200 rows
+    k = rng.standard_normal((T, H, D)).astype(np.float16)
+    v = rng.standard_normal((T, H, D)).astype(np.float16)
+    tiny = np.float16(2.0 ** -24)
+    big = np.float16(65504.0)
+    sgn = lambda *shape: np.where(rng.random(shape) < 0.5, -1, 1).astype(np.float16)
+    for t in range(0, T, 7):
+        kind = (t // 7) % 6
+        for a in (k, v):
+            h = rng.integers(H)
+            if kind == 0:
+                a[t, h] = big * sgn(D)
+            elif kind == 1:
+                a[t, h] = tiny * sgn(D)
+            elif kind == 2:
+                a[t, h] = np.where(rng.random(D) < 0.5, big, tiny) * sgn(D)
+            elif kind == 3:
+                a[t, h] = 0
+                a[t, h, rng.integers(D)] = big if rng.random() < 0.5 else tiny
+            elif kind == 4:
+                a[t, h] = 0
+            else:
+                a[t, h] = (rng.standard_normal(D) * 1e3).astype(np.float16)
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
+    pages = (T + P - 1) // P + 1
+    sm = rng.permutation(pages * P)[:T].astype(np.int64)
+    cache = hkv.new_cache(f, pages, H, DEV)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    got = cache.cpu().numpy()
+    slots = O.quantize(fo, k.astype(np.float32), v.astype(np.float32))
+    assert np.array_equal(got[sm // P, :, sm % P], slots)
+
+
 @pytest.mark.parametrize("dtype,D,R", [("q4_0", 256, 0), ("q8_0", 128, 0), ("octave_k3v4", 128, 64),
                                        ("octave_k3v3_compact", 256, 64)])
 @pytest.mark.parametrize("P", [12, 48, 1000])
