@@ -77,6 +77,21 @@ __device__ __forceinline__ float div127_rn(float x) {
   return x / 127.0f;
 }
 
+// sqrt(x) rounded to nearest, as sqrtf gives it, for x = +0 and every finite
+// x >= 2^-96 (checked on the hardware over all such floats): v_sqrt_f32,
+// which is within one ulp, then its neighbours s -+ 1 ulp are taken when the
+// exact residual x - s' s says so.  Below 2^-96 those residuals are no longer
+// exact; sqrtf scales the argument there, which is what this leaves out.
+__device__ __forceinline__ float sqrt_rn_large(float x) {
+  const float s = __builtin_amdgcn_sqrtf(x);
+  const float sd = __uint_as_float(__float_as_uint(s) - 1u);
+  const float su = __uint_as_float(__float_as_uint(s) + 1u);
+  const float rd = __builtin_fmaf(-sd, s, x);
+  const float ru = __builtin_fmaf(-su, s, x);
+  const float r = rd <= 0.0f ? sd : s;
+  return ru > 0.0f ? su : r;
+}
+
 // ---------------------------------------------------------------------------
 // Wave shuffles.
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

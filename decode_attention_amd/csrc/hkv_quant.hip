@@ -1154,14 +1154,15 @@ __device__ __forceinline__ float tree16(const float (&t)[Q][4], int q0) {
 // kHalfIn (fp16 rows): before the normalising multiply every nonzero value is
 // a multiple of 2^-24 below 2^20 (a block of at most 256 fp16 values), so
 // after it (by 1/sqrt(block) >= 1/16) every nonzero |x| lies in
-// [2^-28, 2^20]: rms (clamped to >= 1e-12) lies in [2^-40, 2^20], a nonzero
-// quotient x / rms is above 2^-48, and dot = sum of |x| |LUT[c]| (the
-// codebooks are symmetric, so a code has the sign of its value; |LUT| >= 6)
-// is zero or in [2^-26, 2^35], with ss / dot in [2^-44, 2^18].  So the
-// reciprocal's fast form needs no range test, Markstein's quotient never
-// takes its tiny-quotient fallback, and ss / dot is the same quotient
-// (RN(1/dot), the product, its exact remainder, one correction) in place of
-// the division.
+// [2^-28, 2^20]: ss / n is zero or at least 2^-64, rms (clamped to
+// >= 1e-12) lies in [2^-40, 2^20], a nonzero quotient x / rms is above
+// 2^-48, and dot = sum of |x| |LUT[c]| (the codebooks are symmetric, so a
+// code has the sign of its value; |LUT| >= 6) is zero or in [2^-26, 2^35],
+// with ss / dot in [2^-44, 2^18].  So the square root needs no argument
+// scaling (sqrt_rn_large), the reciprocal's fast form no range test,
+// Markstein's quotient never takes its tiny-quotient fallback, and ss / dot
+// is the same quotient (RN(1/dot), the product, its exact remainder, one
+// correction) in place of the division.
 template <int Q, int NQ, int BITS, bool kHalfIn>
 __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float (&x)[Q][4], int q0,
                                                 uint32_t (&codes)[Q][4]) {
@@ -1171,7 +1172,15 @@ __device__ __forceinline__ uint32_t oct_block16(const OctTables& T, const float 
 #pragma unroll
     for (int i = 0; i < 4; ++i) t[q][i] = x[q][i] * x[q][i];
   const float ss = tree16<Q, NQ>(t, q0);
-  const float rms = oct_block_rms(ss, NQ * kWave);
+  float rms;
+  if constexpr (kHalfIn) {
+    // ss / n is zero or at least 2^-64 here: the square root needs no
+    // argument scaling (oct_block_rms otherwise)
+    const float r = sqrt_rn_large(ss / (float)(NQ * kWave));
+    rms = r < 1e-12f ? 1e-12f : r;
+  } else {
+    rms = oct_block_rms(ss, NQ * kWave);
+  }
   float ry;
   if constexpr (kHalfIn) {
     const float r = __builtin_amdgcn_rcpf(rms);

@@ -10,7 +10,8 @@
 //
 // It also holds a check of the library's reciprocal and x / 127 (recip_rn
 // and div127_rn in hkv_device.h) against the IEEE quotients over every
-// float, which the quantizers' bit-exactness rests on.
+// float, and of its square root for large arguments (sqrt_rn_large) against
+// sqrtf, which the quantizers' bit-exactness rests on.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,6 +63,22 @@ __global__ __launch_bounds__(kThreads) void recip_check_kernel(uint32_t base, ui
   }
 }
 
+// sqrt_rn_large(x) against sqrtf(x), bit for bit, for x = +0 and the 2^31
+// bit patterns base .. base + 2^31 - 1 that are finite and at least 2^-96:
+// out[0] counts the mismatches, out[1..8] hold the first ones found.
+__global__ __launch_bounds__(kThreads) void sqrt_check_kernel(uint32_t base, uint32_t* out) {
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < 0x80000000u; i += stride) {
+    const uint32_t u = base + i;
+    if (!(u == 0u || (u >= 0x0F800000u && u <= 0x7F7FFFFFu))) continue;
+    const float x = __uint_as_float(u);
+    if (__float_as_uint(hkv::sqrt_rn_large(x)) != __float_as_uint(sqrtf(x))) {
+      const uint32_t k = atomicAdd(&out[0], 1u);
+      if (k < 8) out[1 + k] = u;
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +101,14 @@ int hkv_probe_recip_check(uint32_t* out, void* stream) {
   if (!out) return 1;
   for (uint32_t half = 0; half < 2; ++half)
     recip_check_kernel<<<4096, kThreads, 0, (hipStream_t)stream>>>(half << 31, out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Runs the square-root check over the non-negative float bit patterns (the
+// first half); out is 9 device words, zeroed by the caller.
+int hkv_probe_sqrt_check(uint32_t* out, void* stream) {
+  if (!out) return 1;
+  sqrt_check_kernel<<<4096, kThreads, 0, (hipStream_t)stream>>>(0u, out);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 }
