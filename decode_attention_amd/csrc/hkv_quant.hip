@@ -1152,7 +1152,7 @@ __device__ __forceinline__ float tree16(const float (&t)[Q][4], int q0) {
 // entries, the code in byte 1) into codes[q0 ..]; returns the fp16 bits of
 // the scale (the same in the row).
 // kHalfIn (fp16 rows): before the normalising multiply every nonzero value is
-// a multiple of 2^-24 below 2^20 (a block of at most 256 fp16 values), so
+// a multiple of 2^-24 below 2^24 (a block of at most 256 fp16 values), so
 // after it (by 1/sqrt(block) >= 1/16) every nonzero |x| lies in
 // [2^-28, 2^20]: ss / n is zero or at least 2^-64, rms (clamped to
 // >= 1e-12) lies in [2^-40, 2^20], a nonzero quotient x / rms is above
