@@ -170,6 +170,43 @@ def test_quantize_many_rows(dtype, D, R, in_dtype, misaligned):
     assert np.all(flat[untouched] == 0xA5)
 
 
+@pytest.mark.parametrize("dtype,D,R,scales", [
+    ("q4_0", 256, 0, (1e35, 1e-30, 1e20, 1e-20)), ("q4_0", 128, 0, (1e35, 1e-30, 1e20, 1e-20)),
+    ("q8_0", 256, 0, (1e35, 1e-30, 1e20, 1e-20)),
+    ("octave_k3v4", 128, 64, (1e15, 1e-15, 1e8, 1e-8)),
+    ("octave_k3v3_compact", 256, 64, (1e15, 1e-15, 1e8, 1e-8))])
+def test_quantize_many_rows_fp32_magnitudes(dtype, D, R, scales):
+    """fp32 rows far outside the fp16 range through the many-rows kernels:
+    whole rows, and single 32-value blocks, scaled up or down by the given
+    factors beside plain rows.  Blocks whose scale falls outside the range
+    where the reciprocal's fast form is exact send their wave to the per-lane
+    reciprocal (Q4_0, Q8_0); the Octave kernels keep every range test on fp32
+    rows.  Bytes equal the oracle's."""
+    rng = np.random.default_rng(17 * D + R + len(dtype))
+    T, H, P = 1400, 3, 16                              # 4200 rows
+    k = rng.standard_normal((T, H, D)).astype(np.float32)
+    v = rng.standard_normal((T, H, D)).astype(np.float32)
+    for t in range(0, T, 5):
+        f_ = scales[(t // 5) % len(scales)]
+        for a in (k, v):
+            h = rng.integers(H)
+            if (t // 5) % 2:
+                a[t, h] *= np.float32(f_)
+            else:
+                b0 = 32 * rng.integers(D // 32)
+                a[t, h, b0:b0 + 32] *= np.float32(f_)
+    f = hkv.format_init(dtype, D, R, P)
+    fo = O.format_init(dtype, D, R)
+    pages = (T + P - 1) // P + 1
+    sm = rng.permutation(pages * P)[:T].astype(np.int64)
+    cache = hkv.new_cache(f, pages, H, DEV)
+    hkv.quantize_append(f, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV),
+                        torch.from_numpy(sm).to(DEV), cache)
+    got = cache.cpu().numpy()
+    slots = O.quantize(fo, k, v)
+    assert np.array_equal(got[sm // P, :, sm % P], slots)
+
+
 @pytest.mark.parametrize("dtype,D,R", [("q4_0", 256, 0), ("q4_0", 128, 0), ("q8_0", 256, 0),
                                        ("octave_k3v4", 128, 64), ("octave_k3v3", 128, 64),
                                        ("octave_k3v3_compact", 256, 64), ("octave_k3v4", 192, 64)])
